@@ -1,0 +1,265 @@
+"""Benchmark of the per-layer KV-cache fusion step on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: key-norm anchors of
+the critical layer's chunks, then the fused layer call (re-rotation, critical-layer scoring and
+top-N selection, scatter of fresh K/V, sparse causal attention). The workload is the
+Mistral-7B-shaped layer (32 Q / 8 KV heads, head_dim 128, 5 chunks x 512 tokens + 32-token query,
+15% of the context recomputed), seeded synthetic data.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu]
+
+Prints one JSON line. `value` = selected context rows per second of the whole step. Inputs are
+resident in HBM; 8 input replicas (~360 MB, more than the 256 MB last-level cache) rotate so that
+successive steps do not hit cached inputs.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+WORKLOAD = 1            # Mistral-7B-shaped layer
+ATTN_SOURCES = ["selective_recompute_attention_amd/csrc/attn.hip"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only plain device copies of known size (for scaling memory counters)")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs for events on the library's stream."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.h.hipEventRecord(e, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        assert self.h.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+def copy_probe():
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}))
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from committed counter runs, only if the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    ent = t.get(kernel_key)
+    if not ent or ent.get("source_digest") != source_digest(ATTN_SOURCES):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, N, budget_s):
+    """The fp64 oracle (as it stands) on the same workload: whole steps until the budget is used."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    cfg = w.cfg
+    lay = w.layer(0)
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        O.extract_anchors(w.k_crit, w.chunks[0], cfg.anchors_k, cfg.dtype)
+        O.fused_layer(k_store=lay["k_store"], v_store=lay["v_store"], chunks=w.chunks[0], L=cfg.total_len,
+                      q_new=lay["q_new"][0], k_new=lay["k_new"][0], v_new=lay["v_new"][0], dtype=cfg.dtype,
+                      base=cfg.rope_base, n_kv_heads=cfg.n_kv_heads, q_crit=w.q_crit[0], k_crit_store=w.k_crit,
+                      n_select=N)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 20:
+            break
+    return {"value": N * steps / el, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} full step(s) of the Mistral-7B-shaped workload (anchors + fused layer, "
+                      f"all {N + cfg.query_len} rows), {el:.1f} s, fp64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the fusion step is measured on one GPU's share at its real shape)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+    import oracle as O
+    import selective_recompute_attention_amd as sra
+    from workloads import make_workload
+
+    w = make_workload(WORKLOAD)
+    cfg = w.cfg
+    lay = w.layer(0)
+    Hq, Hkv, D, Lq, Lctx, L = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.query_len, cfg.ctx_len, cfg.total_len
+    N = sra.select_count(15, 100, Lctx)
+    R = N + Lq
+    shape = sra.make_shape(Hq, Hkv, D, "bf16", cfg.rope_base)
+    n_chunks = w.chunks.shape[1]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    base_in = {k: dev(v) for k, v in lay.items()}
+    base_in["q_crit"], base_in["k_crit"] = dev(w.q_crit), dev(w.k_crit)
+    reps = []
+    for i in range(args.replicas):
+        ins = {k: v.clone() for k, v in base_in.items()}
+        outs = {
+            "k_fused": torch.empty((1, L, Hkv, D), dtype=torch.bfloat16, device="cuda"),
+            "v_fused": torch.empty((1, L, Hkv, D), dtype=torch.bfloat16, device="cuda"),
+            "out": torch.empty((1, R, Hq, D), dtype=torch.bfloat16, device="cuda"),
+            "lse": torch.empty((1, R, Hq), dtype=torch.float32, device="cuda"),
+            "row_pos": torch.empty((1, R), dtype=torch.int32, device="cuda"),
+            "scores": torch.empty((1, Lctx), dtype=torch.float32, device="cuda"),
+            "anchors": torch.empty((n_chunks, cfg.anchors_k), dtype=torch.int32, device="cuda"),
+        }
+        reps.append((ins, outs))
+    ws = torch.empty(sra.workspace_size(shape, 1, n_chunks, L, R, Lq), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    hip = Hip()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i, events=None, anchor_ev=None):
+        ins, outs = reps[i % len(reps)]
+        if anchor_ev is not None:
+            hip.record(anchor_ev[0], sp)
+        sra.extract_anchors(shape, ins["k_crit"], w.chunks[0], cfg.anchors_k, outs["anchors"])
+        if anchor_ev is not None:
+            hip.record(anchor_ev[1], sp)
+        sra.fused_layer(shape, chunks=w.chunks, k_store=ins["k_store"], v_store=ins["v_store"],
+                        q_fresh=ins["q_new"], k_fresh=ins["k_new"], v_fresh=ins["v_new"],
+                        row_pos=outs["row_pos"], k_fused=outs["k_fused"], v_fused=outs["v_fused"],
+                        out=outs["out"], lse=outs["lse"], ws=ws, q_crit=ins["q_crit"],
+                        k_crit_store=ins["k_crit"], n_select=N, scores=outs["scores"], stage_events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    # Per-stage durations from HIP events recorded by the library on this stream (separate pass).
+    n_ev = args.steps
+    ev = [(ctypes.c_void_p * 8)(*[hip.event() for _ in range(8)]) for _ in range(n_ev)]
+    aev = [(hip.event(), hip.event()) for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(i, ev[i], aev[i])
+    torch.cuda.synchronize()
+    names = ["rerotate", "score_select", "scatter", "attention"]
+    stage_ms = {n: float(np.mean([hip.elapsed_ms(ctypes.c_void_p(ev[i][2 * s]), ctypes.c_void_p(ev[i][2 * s + 1]))
+                                  for i in range(n_ev)])) for s, n in enumerate(names)}
+    stage_ms["anchors"] = float(np.mean([hip.elapsed_ms(a, b) for a, b in aev]))
+
+    # algorithmic work (realised row positions)
+    rp = reps[0][1]["row_pos"].cpu().numpy()[0].astype(np.int64)
+    attn_flops = 4.0 * Hq * D * float(np.sum(rp + 1))
+    kv_row_bytes = Hkv * D * 2
+    s1_bytes = 4 * kv_row_bytes * Lctx                  # read K,V of every context row, write both
+    s2_bytes = kv_row_bytes * Lctx                      # critical layer's K once
+    s2_flops = 2.0 * Lq * Hq * D * Lctx
+    s3_bytes = 4 * kv_row_bytes * R
+    anchors_bytes = kv_row_bytes * Lctx
+    t_attn = stage_ms["attention"] * 1e-3
+    achieved = attn_flops / t_attn / 1e12
+    rs_t = (stage_ms["rerotate"] + stage_ms["score_select"]) * 1e-3
+    key = "attention_mistral7b_layer"
+    result = {
+        "metric": "fused-layer selected rows/s (whole step); attention MFMA TFLOP/s; re-rotate+score HBM GB/s",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 chunk caches with 2% x4 key-norm outliers; no weights or datasets)",
+        "config": {"workload": "mistral7b_layer: 32 Q / 8 KV heads, d 128, 5 x 512-token chunks + 32-token query, "
+                               "15% recompute (N=384, R=416)", "global_batch": 1, "seq_len": L,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic_for(key),
+                     "kernel": "sparse causal attention stage (k_attn_mfma + split merge)",
+                     "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": stage_ms["attention"]},
+        "stages_ms": stage_ms,
+        "rerotate_score_hbm_gbs": (s1_bytes + s2_bytes) / rs_t / 1e9,
+        "rerotate_hbm_gbs": s1_bytes / (stage_ms["rerotate"] * 1e-3) / 1e9,
+        "scatter_hbm_gbs": s3_bytes / (stage_ms["scatter"] * 1e-3) / 1e9,
+        "anchors_hbm_gbs": anchors_bytes / (stage_ms["anchors"] * 1e-3) / 1e9,
+        "score_flops_tflops": s2_flops / (stage_ms["score_select"] * 1e-3) / 1e12,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, N, args.cpu_seconds)
+    # the parity of this exact output against the oracle is covered by the GPU tests
+    assert (np.diff(rp[:N]) > 0).all() and rp[N] == Lctx
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

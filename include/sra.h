@@ -1,0 +1,272 @@
+/*
+ * sra.h -- C ABI of the per-layer KV-cache fusion step (selective recompute attention)
+ *          for AMD Instinct MI355X (gfx950).
+ *
+ * The step reuses independently precomputed chunk KV caches in a new, non-prefix order
+ * and restores cross-chunk attention by recomputing a few selected tokens:
+ *   S1  re-rotation: move each chunk's cached keys to their new absolute positions
+ *       ("full KV reuse ... adjusting the position encoding", CacheBlend problem definition
+ *       page, §2.4 Full KV Reuse);
+ *   S2  query-centric selection: key-norm anchors per chunk, then the attention of the
+ *       query's Q against one critical middle layer's K picks the top-N context tokens
+ *       (QCFuse technical summary (zh), §2.A anchor probing and critical-layer attention
+ *       profiling; (ja) §2 system workflow);
+ *   S3  scatter of the selected tokens' fresh K/V into the fused cache (KVCache reuse 01,
+ *       §1.3.4 CacheBlend per-layer selective recompute: "extend K_i and V_i");
+ *   S4  location-aware sparse causal attention of the recomputed rows against every key
+ *       at or before their absolute position (QCFuse summary (zh), §2.A location-aware
+ *       sparse attention kernel over a discrete token index table with a strict causal
+ *       constraint; KVCache reuse 01 §1.3.4 "selected tokens x all tokens").
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller (allocated e.g. by torch).
+ *     Host arrays are marked "host". The library never allocates on these paths: scratch
+ *     memory is the caller's workspace, sized by sra_workspace_size().
+ *   - Every call only enqueues work on `stream` and returns; results are ready when the
+ *     stream reaches that point. Calls on one stream run in order.
+ *   - Storage type: shape->dtype selects bfloat16 (SRA_DTYPE_BF16) or float32
+ *     (SRA_DTYPE_F32) for every K/V/Q/output tensor; arithmetic is float32 on the device
+ *     (matrix-core products take bf16 operands and accumulate in float32).
+ *   - Rotary embedding: pairs (x_i, x_{i+d/2}) rotate by pos * theta_i,
+ *     theta_i = rope_base^(-2i/d); angles are formed in float64.
+ *   - Tensor layouts are row-major and token-major: [tokens][heads][head_dim].
+ *   - Return value: SRA_OK (0) or an error status. Errors detectable on the host are
+ *     reported before anything is enqueued; the message is then in sra_last_error()
+ *     (thread-local). No C++ exception crosses this interface. Device-data preconditions
+ *     (row positions sorted, unique and in range) are the caller's contract;
+ *     sra_check_rows() verifies them synchronously.
+ */
+#ifndef SRA_H
+#define SRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------------ status codes */
+#define SRA_OK           0
+#define SRA_E_NULL       1  /* a required pointer is NULL                                   */
+#define SRA_E_SHAPE      2  /* bad sizes: Hq % Hkv, head_dim not 64/128, N > L_ctx, ...     */
+#define SRA_E_CHUNKS     3  /* chunk table does not tile the context or reads outside store */
+#define SRA_E_ALIAS      4  /* an input buffer overlaps an output buffer                    */
+#define SRA_E_WORKSPACE  5  /* workspace NULL or smaller than sra_workspace_size()          */
+#define SRA_E_DTYPE      6  /* unknown dtype                                                */
+#define SRA_E_ROWS       7  /* row positions unsorted, duplicated or out of range           */
+#define SRA_E_HIP        8  /* a HIP runtime call failed                                    */
+#define SRA_E_LIMIT      9  /* a size exceeds a documented implementation limit             */
+
+#define SRA_DTYPE_BF16   0
+#define SRA_DTYPE_F32    1
+
+/* Implementation limits (checked, reported as SRA_E_LIMIT). */
+#define SRA_MAX_ANCHOR_K        64      /* anchors per chunk                              */
+#define SRA_MAX_ANCHOR_TOKENS   8192    /* tokens of one chunk scanned for anchors        */
+
+/* Head geometry shared by every call. Hq must be a multiple of Hkv; query head h reads
+ * KV head h / (Hq/Hkv) (contiguous groups, grouped-query attention). head_dim is 64 or 128. */
+typedef struct {
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;        /* SRA_DTYPE_BF16 or SRA_DTYPE_F32 */
+    double  rope_base;    /* e.g. 10000.0 */
+} sra_shape;
+
+/* One chunk of a request (host struct). The chunk's cached tokens sit at rows
+ * [src_row, src_row + n_tokens) of a chunk store; they were rotated at positions
+ * orig_pos + t when the chunk was precomputed (orig_pos = 0 for a chunk computed on its
+ * own). In the request they occupy fused rows [dst_row, dst_row + n_tokens). The chunks of
+ * a request are listed in request order and must tile the context: dst_row of chunk c is
+ * the sum of the lengths of chunks 0..c-1. L_ctx = total length; it must be equal for every
+ * request of a call. The query occupies fused rows [L_ctx, L). */
+typedef struct {
+    int32_t src_row;
+    int32_t n_tokens;
+    int32_t dst_row;
+    int32_t orig_pos;
+} sra_chunk;
+
+/* Arguments of sra_fused_layer (host struct; every pointer is a device pointer unless
+ * marked host). */
+typedef struct {
+    sra_shape shape;
+    int32_t n_req;                 /* requests in the batch                                  */
+    int32_t n_chunks;              /* chunks per request                                     */
+    const sra_chunk* chunks;       /* host [n_req][n_chunks]                                 */
+    int32_t query_len;             /* Lq: query rows, always recomputed, at [L_ctx, L)       */
+    int32_t total_len;             /* L = L_ctx + Lq                                         */
+    /* S1: this layer's chunk store, shared read-only by all requests */
+    const void* k_store;           /* [store_rows][Hkv][d]                                   */
+    const void* v_store;           /* [store_rows][Hkv][d]                                   */
+    int64_t store_rows;
+    /* S2 (optional): when q_crit is NULL, row_pos is an input and no scoring runs */
+    const void* q_crit;            /* [n_req][Lq][Hq][d], before rotary embedding            */
+    const void* k_crit_store;      /* [crit_store_rows][Hkv][d], critical layer's cached K   */
+    int64_t crit_store_rows;
+    int32_t n_select;              /* N per request (ignored when chunk_quota is given)      */
+    const int32_t* chunk_quota;    /* host [n_req][n_chunks] per-chunk N_c, or NULL          */
+    float* scores;                 /* out [n_req][L_ctx] (may be NULL)                       */
+    /* fresh projections of every position (position-indexed, before rotary embedding) */
+    const void* q_fresh;           /* [n_req][L][Hq][d]                                      */
+    const void* k_fresh;           /* [n_req][L][Hkv][d]                                     */
+    const void* v_fresh;           /* [n_req][L][Hkv][d]                                     */
+    int32_t* row_pos;              /* [n_req][n_rows]: out when scoring runs, else in        */
+    int32_t n_rows;                /* R = N + Lq                                             */
+    /* outputs */
+    void* k_fused;                 /* [n_req][L][Hkv][d]                                     */
+    void* v_fused;                 /* [n_req][L][Hkv][d]                                     */
+    void* out;                     /* [n_req][R][Hq][d]                                      */
+    float* lse;                    /* [n_req][R][Hq] natural-log sum of exp, or NULL         */
+    /* optional profiling: host array of 8 events, or NULL. When set, stage s (0 re-rotation,
+     * 1 scoring and selection, 2 scatter, 3 attention) is bracketed by hipEventRecord of
+     * stage_events[2s] and stage_events[2s+1] on `stream` (stage 1 is empty without q_crit). */
+    hipEvent_t* stage_events;
+} sra_layer_args;
+
+/* ------------------------------------------------------------------------ host helpers */
+
+/* N = ceil(num * ctx_len / den) in exact integer arithmetic (the recompute count is rounded
+ * up: Cache-Craft CSDN article §2.1 N = ceil(alpha*CCI*(1-beta')*|C|); KVCache reuse 01
+ * §2.3.3 N = ceil(CFO(C_i)*|C_i|)). num >= 0, den > 0, 0 <= ctx_len. Writes *n_out.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE (negative num, den <= 0, result > ctx_len or overflow). */
+int sra_select_count(int64_t num, int64_t den, int32_t ctx_len, int32_t* n_out);
+
+/* Bytes of device workspace needed by sra_score_select, sra_sparse_causal_attn and
+ * sra_fused_layer for these sizes (the maximum over the three; 256-byte aligned).
+ * n_chunks: chunks per request; L: fused length; R: recomputed rows; Lq: query rows.
+ * Returns 0 for invalid sizes. */
+size_t sra_workspace_size(const sra_shape* shape, int32_t n_req, int32_t n_chunks,
+                          int32_t L, int32_t R, int32_t Lq);
+
+/* Message of a status code (static storage). */
+const char* sra_error_string(int status);
+
+/* Detail of the last error on this thread (empty after success). */
+const char* sra_last_error(void);
+
+/* ------------------------------------------------------------------------ S1 */
+
+/* Re-rotate and gather the cached chunks of every request into its fused cache
+ * (CacheBlend problem definition page, §2.4 Full KV Reuse: reuse chunks computed on their
+ * own after adjusting their position encoding).
+ *   k_fused[q][n_c + t] = round(R(delta_c) k_store[src_c + t]),  delta_c = dst_row - orig_pos
+ *   v_fused[q][n_c + t] = v_store[src_c + t]
+ * k_store, v_store: [store_rows][Hkv][d], read-only, may be shared by all requests.
+ * chunks: host [n_req][n_chunks]. k_fused, v_fused: [n_req][L][Hkv][d]; rows [0, L_ctx) of
+ * every request are written, rows >= L_ctx are left untouched. A chunk with delta 0 is
+ * copied bit for bit. The store must not overlap the fused buffers (out of place).
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_CHUNKS, SRA_E_ALIAS, SRA_E_HIP. */
+int sra_fuse_rerotate(const sra_shape* shape, int32_t n_req,
+                      const void* k_store, const void* v_store, int64_t store_rows,
+                      const sra_chunk* chunks, int32_t n_chunks,
+                      void* k_fused, void* v_fused, int32_t L, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ S2 */
+
+/* Key-norm anchors (QCFuse summary (zh) §2.A anchor-based lightweight query probing: keep
+ * the few tokens of each precomputed chunk with the largest key norm). For chunk c the
+ * norm of token t is the L2 norm of k_store[src_c + t] over all Hkv*d values; anchors are
+ * the first k tokens in the order (larger norm first, lower t on a tie).
+ * chunks: host [n_chunks], any rows of the store (overlap allowed). anchor_rows: out
+ * [n_chunks][k] int32 token offsets t within each chunk. norms: optional out [store_rows]
+ * float32, written at the rows the chunks cover (others untouched).
+ * Errors: SRA_E_NULL, SRA_E_SHAPE (k < 1 or k > n_tokens), SRA_E_LIMIT (k > 64 or
+ * n_tokens > 8192), SRA_E_CHUNKS, SRA_E_DTYPE, SRA_E_HIP. */
+int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t store_rows,
+                        const sra_chunk* chunks, int32_t n_chunks, int32_t k,
+                        int32_t* anchor_rows, float* norms, hipStream_t stream);
+
+/* Query-centric scores and top-N selection from one critical layer (QCFuse summary (zh)
+ * §2.A critical-layer attention profiling: the attention distribution of the query's Q
+ * over that layer's cached K gives the top-N context token indices).
+ *   k'_j    = R(delta_c) k_crit_store[src_c + t] for j = n_c + t (keys in the fused layout)
+ *   q_{i,h} = R(L_ctx + i) q_crit[i][h]
+ *   s_j     = sum over h < Hq, i < Lq of softmax_j(q_{i,h} . k'_{j, h/g} / sqrt(d)), j < L_ctx
+ * then N = n_select context tokens by descending s_j (lower index wins a tie), or with
+ * chunk_quota the top N_c of each chunk's own tokens, written in ascending position order,
+ * followed by the Lq query positions:
+ *   row_pos[q] = [sel_0 < sel_1 < ... < sel_{N-1}, L_ctx, L_ctx+1, ..., L_ctx+Lq-1]
+ * q_crit: [n_req][Lq][Hq][d] before rotary embedding. k_crit_store: [store_rows][Hkv][d].
+ * chunks: host [n_req][n_chunks]. chunk_quota: host [n_req][n_chunks] or NULL; with quotas
+ * every request must select the same total. scores: out [n_req][L_ctx] float32 or NULL.
+ * row_pos: out [n_req][N + Lq]. ws: workspace of at least
+ * sra_workspace_size(shape, n_req, n_chunks, L_ctx + Lq, N + Lq, Lq) bytes.
+ * Reductions run in a fixed order, so repeated calls select identically.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_CHUNKS, SRA_E_WORKSPACE, SRA_E_HIP. */
+int sra_score_select(const sra_shape* shape, int32_t n_req, const void* q_crit, int32_t Lq,
+                     const void* k_crit_store, int64_t store_rows,
+                     const sra_chunk* chunks, int32_t n_chunks,
+                     int32_t n_select, const int32_t* chunk_quota,
+                     float* scores, int32_t* row_pos, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Top-N selection over given scores (the selection half of sra_score_select; the ranking
+ * is a stable sort by descending score, Cache-Craft CSDN article §2.2.2 token selection).
+ * scores: [n_req][ctx_len] float32, not NaN. Writes row_pos [n_req][N + Lq] exactly as
+ * sra_score_select does. With chunk_quota (host [n_req][n_chunks]) the chunks (host
+ * [n_req][n_chunks]) define the per-chunk ranges; without quotas chunks may be NULL.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_CHUNKS, SRA_E_HIP. */
+int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t n_select,
+                    const int32_t* chunk_quota, const sra_chunk* chunks, int32_t n_chunks,
+                    int32_t Lq, int32_t* row_pos, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ S3 */
+
+/* Scatter fresh K/V of the recomputed rows into the fused cache (KVCache reuse 01 §1.3.4:
+ * the selected tokens' freshly computed K/V extend the reused K/V of the other tokens).
+ *   k_fused[q][row_pos[r]] = round(R(row_pos[r]) k_new[q][r]);  v_fused[q][row_pos[r]] = v_new[q][r]
+ * k_new, v_new: [n_req][R][Hkv][d] compact rows aligned with row_pos, K before rotary
+ * embedding. row_pos: [n_req][R] sorted, unique, < L. k_fused, v_fused: [n_req][L][Hkv][d]
+ * updated in place (no other row changes).
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_ALIAS, SRA_E_HIP. */
+int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, const void* v_new,
+                   const int32_t* row_pos, int32_t R, void* k_fused, void* v_fused, int32_t L,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------ S4 */
+
+/* Location-aware sparse causal attention (QCFuse summary (zh) §2.A: discrete recomputed
+ * tokens attend under a strict causal constraint; KVCache reuse 01 §1.3.4: attention of
+ * the selected tokens against all tokens). For row r at absolute position p = row_pos[r]
+ * and query head h:
+ *   q = R(p) q_new[r][h];  out[r][h] = sum_{j <= p} softmax_j(q . k_fused[j][h/g] / sqrt(d)) v_fused[j][h/g]
+ *   lse[r][h] = log sum_{j <= p} exp(q . k_fused[j][h/g] / sqrt(d))
+ * q_new: [n_req][R][Hq][d] compact, before rotary embedding. row_pos: [n_req][R] sorted,
+ * unique, < L. k_fused, v_fused: [n_req][L][Hkv][d]. out: [n_req][R][Hq][d] (storage
+ * dtype). lse: [n_req][R][Hq] float32 or NULL. ws: at least
+ * sra_workspace_size(shape, n_req, 1, L, R, 1) bytes.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_ALIAS, SRA_E_WORKSPACE, SRA_E_HIP. */
+int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_new,
+                           const int32_t* row_pos, int32_t R,
+                           const void* k_fused, const void* v_fused, int32_t L,
+                           void* out, float* lse, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------ fused entry */
+
+/* One layer of the fusion step on one stream (KVCache reuse 01 §1.3.4 per-layer flow;
+ * QCFuse summary (ja) §2 workflow): S1 re-rotation, then S2 scoring and selection when
+ * args->q_crit is set (otherwise args->row_pos is taken as given), then S3 scatter of the
+ * fresh K/V rows gathered from the position-indexed fresh buffers at row_pos, then S4
+ * attention of those rows. Fills k_fused/v_fused (the cache handed on to decoding), out,
+ * lse, row_pos and scores. ws: at least
+ * sra_workspace_size(&args->shape, n_req, n_chunks, total_len, n_rows, query_len) bytes.
+ * Errors: as the stage calls. */
+int sra_fused_layer(const sra_layer_args* args, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ checks */
+
+/* Synchronous check that every row_pos[q] is strictly increasing with values in [0, L).
+ * Returns SRA_OK or SRA_E_ROWS (first offending flat index in *first_bad when non-NULL).
+ * Allocates a few bytes of device memory; not for capture or hot loops. */
+int sra_check_rows(const int32_t* row_pos, int32_t n_req, int32_t R, int32_t L,
+                   int32_t* first_bad, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SRA_H */

@@ -1,0 +1,691 @@
+// Host side of the C ABI declared in include/sra.h: argument validation, workspace planning,
+// kernel-argument chunk tables and launch sequencing on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+#include <vector>
+
+#include "../../include/sra.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SRA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SRA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t elem_size(const sra_shape* s) { return s->dtype == SRA_DTYPE_BF16 ? 2 : 4; }
+
+int check_shape(const sra_shape* s) {
+  if (!s) return fail(SRA_E_NULL, "shape is NULL");
+  if (s->dtype != SRA_DTYPE_BF16 && s->dtype != SRA_DTYPE_F32)
+    return fail(SRA_E_DTYPE, "dtype %d is neither SRA_DTYPE_BF16 nor SRA_DTYPE_F32", s->dtype);
+  if (s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->n_q_heads % s->n_kv_heads != 0)
+    return fail(SRA_E_SHAPE, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(SRA_E_SHAPE, "head_dim %d is not 64 or 128", s->head_dim);
+  if (!(s->rope_base > 1.0) || !std::isfinite(s->rope_base))
+    return fail(SRA_E_SHAPE, "rope_base must be finite and > 1");
+  return SRA_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(SRA_E_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(SRA_E_SHAPE, "%s is not 16-byte aligned", name);
+  return SRA_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Validate a [n_req][n_chunks] table: chunks tile [0, L_ctx) in request order, store rows in
+// range, equal L_ctx for every request. Returns L_ctx through *lctx.
+int check_chunks(const sra_chunk* ch, int n_req, int n_chunks, int64_t store_rows, int* lctx) {
+  if (!ch) return fail(SRA_E_NULL, "chunks is NULL");
+  if (n_chunks <= 0) return fail(SRA_E_SHAPE, "n_chunks must be positive");
+  int first = -1;
+  for (int q = 0; q < n_req; ++q) {
+    int64_t n = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const sra_chunk& k = ch[(int64_t)q * n_chunks + c];
+      if (k.n_tokens < 0) return fail(SRA_E_CHUNKS, "request %d chunk %d: negative n_tokens", q, c);
+      if (k.dst_row != n)
+        return fail(SRA_E_CHUNKS, "request %d chunk %d: dst_row %d, expected %lld (chunks must tile the context in order)",
+                    q, c, k.dst_row, (long long)n);
+      if (k.src_row < 0 || (int64_t)k.src_row + k.n_tokens > store_rows)
+        return fail(SRA_E_CHUNKS, "request %d chunk %d: store rows [%d, %lld) outside [0, %lld)", q, c,
+                    k.src_row, (long long)k.src_row + k.n_tokens, (long long)store_rows);
+      n += k.n_tokens;
+      if (n > std::numeric_limits<int32_t>::max() / 2)
+        return fail(SRA_E_SHAPE, "context too long");
+    }
+    if (first < 0) first = (int)n;
+    else if (n != first)
+      return fail(SRA_E_SHAPE, "request %d has context length %lld, request 0 has %d", q, (long long)n, first);
+  }
+  *lctx = first;
+  return SRA_OK;
+}
+
+// ------------------------------------------------------------------------------ workspace plan
+struct AttnSplit {
+  int n_splits, key_split;
+};
+
+AttnSplit attn_split(int n_req, int Hkv, int R, int g, int L) {
+  const int64_t tiles = (int64_t)n_req * Hkv * ceil_div((int64_t)R * g, 128);
+  AttnSplit s{1, std::max(L, 1)};
+  if (tiles == 0 || tiles >= 512 || L <= 256) return s;
+  const int64_t want = ceil_div(1024, tiles);
+  const int64_t n = std::min<int64_t>(want, ceil_div(L, 256));
+  const int ks = (int)(ceil_div(ceil_div(L, n), 64) * 64);
+  s.key_split = ks;
+  s.n_splits = (int)ceil_div(L, ks);
+  return s;
+}
+
+struct Plan {
+  // offsets in bytes from the workspace base
+  size_t cs = 0;          // rotary table [n_req][R][d/2] float2
+  size_t region = 0;      // start of the union of the score and attention regions
+  // score (bf16)
+  int Mpad = 0;
+  int64_t max_blocks = 0;
+  size_t qrot = 0, ml_part = 0, ml_final = 0, colsum = 0, scores_tmp = 0;
+  int64_t qrot_plane = 0;  // elements per hi/lo plane
+  // score (f32)
+  size_t prob = 0, parts = 0;
+  // attention
+  AttnSplit split{1, 1};
+  size_t part_o = 0, part_ml = 0;
+  size_t score_end = 0, attn_end = 0, total = 0;
+};
+
+Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq) {
+  Plan p;
+  const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads, g = Hq / Hkv;
+  const int Lctx = std::max(L - Lq, 0);
+  size_t off = 0;
+  p.cs = off;
+  off = align256(off + (size_t)n_req * R * (D / 2) * sizeof(float2));
+  p.region = off;
+  // score region
+  size_t so = off;
+  if (s->dtype == SRA_DTYPE_BF16) {
+    p.Mpad = (int)ceil_div((int64_t)Lq * g, 32) * 32;
+    p.max_blocks = (int64_t)n_req * (ceil_div(Lctx, 128) + n_chunks);
+    p.qrot_plane = (int64_t)n_req * n_chunks * Hkv * p.Mpad * D;
+    p.qrot = so; so = align256(so + (size_t)p.qrot_plane * 2 * sizeof(uint16_t));
+    p.ml_part = so; so = align256(so + (size_t)p.max_blocks * Hkv * p.Mpad * sizeof(float2));
+    p.ml_final = so; so = align256(so + (size_t)n_req * Hkv * p.Mpad * sizeof(float2));
+    p.colsum = so; so = align256(so + (size_t)n_req * Hkv * Lctx * sizeof(float));
+  } else {
+    p.prob = so; so = align256(so + (size_t)n_req * Hq * Lq * Lctx * sizeof(float));
+    p.parts = so; so = align256(so + (size_t)n_req * Lctx * sizeof(float));
+  }
+  p.scores_tmp = so; so = align256(so + (size_t)n_req * Lctx * sizeof(float));
+  p.score_end = so;
+  // attention region (same start: scoring is finished before attention runs)
+  size_t ao = off;
+  if (s->dtype == SRA_DTYPE_BF16) {
+    p.split = attn_split(n_req, Hkv, R, g, L);
+    if (p.split.n_splits > 1) {
+      const int64_t tiles = (int64_t)n_req * Hkv * ceil_div((int64_t)R * g, 128);
+      const int64_t slots = tiles * p.split.n_splits * 128;
+      p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(float));
+      p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float2));
+    }
+  }
+  p.attn_end = ao;
+  p.total = std::max(p.score_end, p.attn_end);
+  return p;
+}
+
+char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SRA_OK;
+  if (!ws) return fail(SRA_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(SRA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(SRA_E_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+  return SRA_OK;
+}
+
+// ------------------------------------------------------------------------------ table packing
+struct Entry {
+  int req, src, len, dst, delta, blocks;
+};
+
+// Pack entries into launch-sized tables; calls fn(tab, first_entry_index, first_block_index).
+template <typename Fn>
+hipError_t for_each_tab(const std::vector<Entry>& ents, Fn fn) {
+  size_t i = 0;
+  int64_t blk_base = 0;
+  while (i < ents.size()) {
+    sra::ChunkTab tab;
+    std::memset(&tab, 0, sizeof(tab));
+    const size_t first = i;
+    int blk = 0;
+    while (i < ents.size() && tab.n < sra::kMaxEntries) {
+      const Entry& e = ents[i];
+      tab.req[tab.n] = e.req;
+      tab.src[tab.n] = e.src;
+      tab.len[tab.n] = e.len;
+      tab.dst[tab.n] = e.dst;
+      tab.delta[tab.n] = e.delta;
+      tab.blk0[tab.n] = blk;
+      blk += e.blocks;
+      ++tab.n;
+      ++i;
+    }
+    tab.blk0[tab.n] = blk;
+    hipError_t err = fn(tab, (int)first, (int)blk_base);
+    if (err != hipSuccess) return err;
+    blk_base += blk;
+  }
+  return hipSuccess;
+}
+
+std::vector<Entry> chunk_entries(const sra_chunk* ch, int n_req, int n_chunks, int rows_per_blk) {
+  std::vector<Entry> v;
+  for (int q = 0; q < n_req; ++q)
+    for (int c = 0; c < n_chunks; ++c) {
+      const sra_chunk& k = ch[(int64_t)q * n_chunks + c];
+      if (k.n_tokens == 0) continue;
+      v.push_back({q, k.src_row, k.n_tokens, k.dst_row, k.dst_row - k.orig_pos,
+                   (int)ceil_div(k.n_tokens, rows_per_blk)});
+    }
+  return v;
+}
+
+// ------------------------------------------------------------------------------ stage bodies
+int do_rerotate(const sra_shape* s, int n_req, const void* ks, const void* vs,
+                const sra_chunk* ch, int n_chunks, void* kf, void* vf, int L, hipStream_t st) {
+  const int D = s->head_dim, Hkv = s->n_kv_heads;
+  const int64_t row_bytes = (int64_t)Hkv * D * elem_size(s);
+  const int rpb = (int)std::max<int64_t>(1, 32768 / (2 * row_bytes));
+  auto ents = chunk_entries(ch, n_req, n_chunks, rpb);
+  hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
+    return sra::launch_rerotate(s->dtype, D, Hkv, tab, rpb, ks, vs, kf, vf, L, s->rope_base, st);
+  });
+  if (e != hipSuccess) return hip_fail(e, "re-rotation launch");
+  return SRA_OK;
+}
+
+// Selection units and launch.
+int do_select(int n_req, int Lctx, int Lq, int R, int N, const int32_t* quota, const sra_chunk* ch,
+              int n_chunks, int nparts, const float* parts, float* scores, int32_t* row_pos,
+              hipStream_t st) {
+  struct U { int req, begin, len, quota, off, wq; };
+  std::vector<U> units;
+  for (int q = 0; q < n_req; ++q) {
+    if (!quota) {
+      units.push_back({q, 0, Lctx, N, 0, 1});
+    } else {
+      int off = 0;
+      for (int c = 0; c < n_chunks; ++c) {
+        const sra_chunk& k = ch[(int64_t)q * n_chunks + c];
+        const int qc = quota[(int64_t)q * n_chunks + c];
+        units.push_back({q, k.dst_row, k.n_tokens, qc, off, c == 0 ? 1 : 0});
+        off += qc;
+      }
+    }
+  }
+  size_t i = 0;
+  while (i < units.size()) {
+    sra::SelTab tab;
+    std::memset(&tab, 0, sizeof(tab));
+    while (i < units.size() && tab.n < sra::kMaxEntries) {
+      const U& u = units[i++];
+      tab.req[tab.n] = u.req;
+      tab.begin[tab.n] = u.begin;
+      tab.len[tab.n] = u.len;
+      tab.quota[tab.n] = u.quota;
+      tab.out_off[tab.n] = u.off;
+      tab.writes_query[tab.n] = u.wq;
+      ++tab.n;
+    }
+    hipError_t e = sra::launch_select(tab, nparts, Lctx, Lq, R, parts, scores, row_pos, st);
+    if (e != hipSuccess) return hip_fail(e, "selection launch");
+  }
+  return SRA_OK;
+}
+
+// Validates quota/n_select and returns N (selected context tokens per request).
+int resolve_count(int n_req, int n_chunks, const sra_chunk* ch, int Lctx, int n_select,
+                  const int32_t* quota, int* N) {
+  if (!quota) {
+    if (n_select < 0 || n_select > Lctx)
+      return fail(SRA_E_SHAPE, "n_select %d outside [0, %d]", n_select, Lctx);
+    *N = n_select;
+    return SRA_OK;
+  }
+  int first = -1;
+  for (int q = 0; q < n_req; ++q) {
+    int64_t tot = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int qc = quota[(int64_t)q * n_chunks + c];
+      const int len = ch[(int64_t)q * n_chunks + c].n_tokens;
+      if (qc < 0 || qc > len)
+        return fail(SRA_E_SHAPE, "request %d chunk %d: quota %d outside [0, %d]", q, c, qc, len);
+      tot += qc;
+    }
+    if (first < 0) first = (int)tot;
+    else if (tot != first)
+      return fail(SRA_E_SHAPE, "request %d selects %lld tokens, request 0 selects %d", q, (long long)tot, first);
+  }
+  *N = first;
+  return SRA_OK;
+}
+
+int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const void* kc,
+                    const sra_chunk* ch, int n_chunks, int Lctx, int N, const int32_t* quota,
+                    float* scores, int32_t* row_pos, void* ws, const Plan& p, hipStream_t st) {
+  const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads, g = Hq / Hkv;
+  const int R = N + Lq;
+  float* sc = scores ? scores : reinterpret_cast<float*>(wsp(ws, p.scores_tmp));
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipError_t e;
+  if (s->dtype == SRA_DTYPE_BF16) {
+    uint16_t* qrot = reinterpret_cast<uint16_t*>(wsp(ws, p.qrot));
+    float2* ml_part = reinterpret_cast<float2*>(wsp(ws, p.ml_part));
+    float2* ml_final = reinterpret_cast<float2*>(wsp(ws, p.ml_final));
+    float* colsum = reinterpret_cast<float*>(wsp(ws, p.colsum));
+    auto ents = chunk_entries(ch, n_req, n_chunks, 128);
+    // per-request block ranges in the global block numbering (entries are ordered by request)
+    std::vector<int> req_blk0(n_req + 1, 0);
+    for (const Entry& en : ents) req_blk0[en.req + 1] += en.blocks;
+    for (int q = 0; q < n_req; ++q) req_blk0[q + 1] += req_blk0[q];
+    e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int) {
+      return sra::launch_score_prep(D, tab, Lq, Hq, Hkv, p.Mpad, Lctx, qc, qrot, p.qrot_plane,
+                                    first, s->rope_base, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "score prep launch");
+    e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
+      return sra::launch_score_pass(1, D, tab, Hkv, p.Mpad, Lq * g, Lctx, kc, qrot, p.qrot_plane,
+                                    first, blk_base, ml_part, ml_final, colsum, scale_log2, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "score pass 1 launch");
+    e = sra::launch_score_merge(n_req, Hkv, p.Mpad, Lq * g, req_blk0.data(), ml_part, ml_final, st);
+    if (e != hipSuccess) return hip_fail(e, "score merge launch");
+    e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
+      return sra::launch_score_pass(2, D, tab, Hkv, p.Mpad, Lq * g, Lctx, kc, qrot, p.qrot_plane,
+                                    first, blk_base, ml_part, ml_final, colsum, scale_log2, st);
+    });
+    if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
+    return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, Hkv, colsum, sc, row_pos, st);
+  }
+  // float32 storage: one softmax row per query vector, then fixed-order column sums
+  auto ents = chunk_entries(ch, n_req, n_chunks, 1);
+  sra::ChunkTab tab;
+  std::memset(&tab, 0, sizeof(tab));
+  for (const Entry& en : ents) {
+    tab.req[tab.n] = en.req;
+    tab.src[tab.n] = en.src;
+    tab.len[tab.n] = en.len;
+    tab.dst[tab.n] = en.dst;
+    tab.delta[tab.n] = en.delta;
+    ++tab.n;
+  }
+  float* prob = reinterpret_cast<float*>(wsp(ws, p.prob));
+  float* parts = reinterpret_cast<float*>(wsp(ws, p.parts));
+  e = sra::launch_score_f32(D, tab, n_req, Lq, Hq, Hkv, Lctx, (const float*)qc, (const float*)kc,
+                            prob, scale_log2, s->rope_base, st);
+  if (e != hipSuccess) return hip_fail(e, "f32 score launch");
+  e = sra::launch_colsum_f32(n_req, Hq * Lq, Lctx, prob, parts, st);
+  if (e != hipSuccess) return hip_fail(e, "f32 column-sum launch");
+  return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, 1, parts, sc, row_pos, st);
+}
+
+int do_attn(const sra_shape* s, int n_req, const void* q, int q_rows, int indexed,
+            const int32_t* row_pos, int R, const void* kf, const void* vf, int L, void* out,
+            float* lse, const float2* cs, void* ws, const Plan& p, hipStream_t st) {
+  const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads;
+  hipError_t e;
+  if (s->dtype == SRA_DTYPE_BF16) {
+    e = sra::launch_attn_bf16(D, n_req, Hq, Hkv, R, L, (const uint16_t*)q, q_rows, indexed, row_pos,
+                              cs, (const uint16_t*)kf, (const uint16_t*)vf, (uint16_t*)out, lse,
+                              p.split.n_splits, p.split.key_split,
+                              reinterpret_cast<float*>(wsp(ws, p.part_o)),
+                              reinterpret_cast<float2*>(wsp(ws, p.part_ml)), st);
+  } else {
+    e = sra::launch_attn_f32(D, n_req, Hq, Hkv, R, L, (const float*)q, q_rows, indexed, row_pos, cs,
+                             (const float*)kf, (const float*)vf, (float*)out, lse, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return SRA_OK;
+}
+
+int check_attn_limits(const sra_shape* s, int R, int L) {
+  if (s->dtype == SRA_DTYPE_F32 && s->n_q_heads / s->n_kv_heads > 16)
+    return fail(SRA_E_LIMIT, "float32 attention supports at most 16 query heads per KV head");
+  if ((int64_t)R * (s->n_q_heads / s->n_kv_heads) > (int64_t)1 << 30)
+    return fail(SRA_E_LIMIT, "too many query vectors");
+  (void)L;
+  return SRA_OK;
+}
+
+int check_score_limits(const sra_shape* s, int n_req, int n_chunks, int Lq) {
+  const int g = s->n_q_heads / s->n_kv_heads;
+  if (n_req > sra::kMaxEntries) return fail(SRA_E_LIMIT, "at most %d requests per scoring call", sra::kMaxEntries);
+  if (s->dtype == SRA_DTYPE_BF16 && (int64_t)Lq * g > 2048)
+    return fail(SRA_E_LIMIT, "query rows x group size (%lld) exceeds 2048", (long long)Lq * g);
+  if (s->dtype == SRA_DTYPE_F32 && (int64_t)n_req * n_chunks > sra::kMaxEntries)
+    return fail(SRA_E_LIMIT, "float32 scoring supports at most %d chunks per call", sra::kMaxEntries);
+  return SRA_OK;
+}
+
+}  // namespace
+
+// ==================================================================================== C ABI
+extern "C" {
+
+const char* sra_error_string(int status) {
+  switch (status) {
+    case SRA_OK: return "success";
+    case SRA_E_NULL: return "a required pointer is NULL";
+    case SRA_E_SHAPE: return "invalid sizes or shape";
+    case SRA_E_CHUNKS: return "invalid chunk table";
+    case SRA_E_ALIAS: return "an input overlaps an output";
+    case SRA_E_WORKSPACE: return "workspace missing or too small";
+    case SRA_E_DTYPE: return "unknown dtype";
+    case SRA_E_ROWS: return "row positions unsorted, duplicated or out of range";
+    case SRA_E_HIP: return "HIP runtime error";
+    case SRA_E_LIMIT: return "size exceeds an implementation limit";
+    default: return "unknown status";
+  }
+}
+
+const char* sra_last_error(void) { return g_last_error.c_str(); }
+
+int sra_select_count(int64_t num, int64_t den, int32_t ctx_len, int32_t* n_out) {
+  if (!n_out) return fail(SRA_E_NULL, "n_out is NULL");
+  if (num < 0 || den <= 0 || ctx_len < 0) return fail(SRA_E_SHAPE, "need num >= 0, den > 0, ctx_len >= 0");
+  if (num > (int64_t)1 << 31) return fail(SRA_E_SHAPE, "num too large");
+  const int64_t prod = num * (int64_t)ctx_len;
+  const int64_t n = (prod + den - 1) / den;
+  if (n > ctx_len) return fail(SRA_E_SHAPE, "ratio %lld/%lld exceeds 1", (long long)num, (long long)den);
+  *n_out = (int32_t)n;
+  return ok();
+}
+
+size_t sra_workspace_size(const sra_shape* shape, int32_t n_req, int32_t n_chunks, int32_t L,
+                          int32_t R, int32_t Lq) {
+  if (!shape || shape->n_kv_heads <= 0 || shape->n_q_heads <= 0 ||
+      shape->n_q_heads % shape->n_kv_heads != 0 || (shape->head_dim != 64 && shape->head_dim != 128) ||
+      (shape->dtype != SRA_DTYPE_BF16 && shape->dtype != SRA_DTYPE_F32) || n_req <= 0 ||
+      n_chunks <= 0 || L <= 0 || R < 0 || Lq < 0 || Lq > L)
+    return 0;
+  return make_plan(shape, n_req, n_chunks, L, R, Lq).total;
+}
+
+int sra_fuse_rerotate(const sra_shape* shape, int32_t n_req, const void* k_store, const void* v_store,
+                      int64_t store_rows, const sra_chunk* chunks, int32_t n_chunks, void* k_fused,
+                      void* v_fused, int32_t L, hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (n_req <= 0) return fail(SRA_E_SHAPE, "n_req must be positive");
+  if ((rc = check_ptr(k_store, "k_store")) || (rc = check_ptr(v_store, "v_store")) ||
+      (rc = check_ptr(k_fused, "k_fused")) || (rc = check_ptr(v_fused, "v_fused")))
+    return rc;
+  int Lctx = 0;
+  if ((rc = check_chunks(chunks, n_req, n_chunks, store_rows, &Lctx))) return rc;
+  if (Lctx > L) return fail(SRA_E_SHAPE, "context length %d exceeds L = %d", Lctx, L);
+  const size_t es = elem_size(shape), row = (size_t)shape->n_kv_heads * shape->head_dim * es;
+  const size_t sb = (size_t)store_rows * row, fb = (size_t)n_req * L * row;
+  if (overlap(k_store, sb, k_fused, fb) || overlap(k_store, sb, v_fused, fb) ||
+      overlap(v_store, sb, k_fused, fb) || overlap(v_store, sb, v_fused, fb) ||
+      overlap(k_fused, fb, v_fused, fb))
+    return fail(SRA_E_ALIAS, "chunk store and fused cache buffers overlap");
+  if ((rc = do_rerotate(shape, n_req, k_store, v_store, chunks, n_chunks, k_fused, v_fused, L, stream)))
+    return rc;
+  return ok();
+}
+
+int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t store_rows,
+                        const sra_chunk* chunks, int32_t n_chunks, int32_t k, int32_t* anchor_rows,
+                        float* norms, hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if ((rc = check_ptr(k_store, "k_store"))) return rc;
+  if (!anchor_rows) return fail(SRA_E_NULL, "anchor_rows is NULL");
+  if (!chunks) return fail(SRA_E_NULL, "chunks is NULL");
+  if (n_chunks <= 0) return fail(SRA_E_SHAPE, "n_chunks must be positive");
+  if (k < 1) return fail(SRA_E_SHAPE, "k must be >= 1");
+  if (k > SRA_MAX_ANCHOR_K) return fail(SRA_E_LIMIT, "k = %d exceeds %d", k, SRA_MAX_ANCHOR_K);
+  std::vector<Entry> ents;
+  for (int c = 0; c < n_chunks; ++c) {
+    const sra_chunk& ch = chunks[c];
+    if (ch.src_row < 0 || ch.n_tokens < 0 || (int64_t)ch.src_row + ch.n_tokens > store_rows)
+      return fail(SRA_E_CHUNKS, "chunk %d reads outside the store", c);
+    if (ch.n_tokens < k) return fail(SRA_E_SHAPE, "chunk %d has %d tokens < k = %d", c, ch.n_tokens, k);
+    if (ch.n_tokens > SRA_MAX_ANCHOR_TOKENS)
+      return fail(SRA_E_LIMIT, "chunk %d has %d tokens > %d", c, ch.n_tokens, SRA_MAX_ANCHOR_TOKENS);
+    ents.push_back({0, ch.src_row, ch.n_tokens, c /* output slot */, 0, 1});
+  }
+  const int row_elems = shape->n_kv_heads * shape->head_dim;
+  hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
+    return sra::launch_anchors(shape->dtype, row_elems, tab, k, k_store, anchor_rows, norms, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "anchor launch");
+  return ok();
+}
+
+int sra_score_select(const sra_shape* shape, int32_t n_req, const void* q_crit, int32_t Lq,
+                     const void* k_crit_store, int64_t store_rows, const sra_chunk* chunks,
+                     int32_t n_chunks, int32_t n_select, const int32_t* chunk_quota, float* scores,
+                     int32_t* row_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (n_req <= 0) return fail(SRA_E_SHAPE, "n_req must be positive");
+  if (Lq < 1) return fail(SRA_E_SHAPE, "scoring needs at least one query row");
+  if ((rc = check_ptr(q_crit, "q_crit")) || (rc = check_ptr(k_crit_store, "k_crit_store"))) return rc;
+  if (!row_pos) return fail(SRA_E_NULL, "row_pos is NULL");
+  int Lctx = 0, N = 0;
+  if ((rc = check_chunks(chunks, n_req, n_chunks, store_rows, &Lctx))) return rc;
+  if (Lctx < 1) return fail(SRA_E_SHAPE, "empty context");
+  if ((rc = check_score_limits(shape, n_req, n_chunks, Lq))) return rc;
+  if ((rc = resolve_count(n_req, n_chunks, chunks, Lctx, n_select, chunk_quota, &N))) return rc;
+  const Plan p = make_plan(shape, n_req, n_chunks, Lctx + Lq, N + Lq, Lq);
+  if ((rc = check_ws(ws, ws_bytes, p.score_end))) return rc;
+  if ((rc = do_score_select(shape, n_req, q_crit, Lq, k_crit_store, chunks, n_chunks, Lctx, N,
+                            chunk_quota, scores, row_pos, ws, p, stream)))
+    return rc;
+  return ok();
+}
+
+int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t n_select,
+                    const int32_t* chunk_quota, const sra_chunk* chunks, int32_t n_chunks,
+                    int32_t Lq, int32_t* row_pos, hipStream_t stream) {
+  if (!scores) return fail(SRA_E_NULL, "scores is NULL");
+  if (!row_pos) return fail(SRA_E_NULL, "row_pos is NULL");
+  if (n_req <= 0 || ctx_len < 1 || Lq < 0) return fail(SRA_E_SHAPE, "need n_req > 0, ctx_len > 0, Lq >= 0");
+  int N = 0, rc;
+  if (chunk_quota) {
+    int Lctx = 0;
+    if ((rc = check_chunks(chunks, n_req, n_chunks, std::numeric_limits<int32_t>::max(), &Lctx))) return rc;
+    if (Lctx != ctx_len) return fail(SRA_E_CHUNKS, "chunks cover %d positions, ctx_len is %d", Lctx, ctx_len);
+  }
+  if ((rc = resolve_count(n_req, n_chunks, chunks, ctx_len, n_select, chunk_quota, &N))) return rc;
+  if ((rc = do_select(n_req, ctx_len, Lq, N + Lq, N, chunk_quota, chunks, n_chunks, 0, nullptr,
+                      const_cast<float*>(scores), row_pos, stream)))
+    return rc;
+  return ok();
+}
+
+int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, const void* v_new,
+                   const int32_t* row_pos, int32_t R, void* k_fused, void* v_fused, int32_t L,
+                   hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (n_req <= 0 || R < 0 || L <= 0 || R > L) return fail(SRA_E_SHAPE, "need n_req > 0, 0 <= R <= L");
+  if ((rc = check_ptr(k_new, "k_new")) || (rc = check_ptr(v_new, "v_new")) ||
+      (rc = check_ptr(k_fused, "k_fused")) || (rc = check_ptr(v_fused, "v_fused")))
+    return rc;
+  if (!row_pos) return fail(SRA_E_NULL, "row_pos is NULL");
+  const size_t row = (size_t)shape->n_kv_heads * shape->head_dim * elem_size(shape);
+  const size_t nb = (size_t)n_req * R * row, fb = (size_t)n_req * L * row;
+  if (overlap(k_new, nb, k_fused, fb) || overlap(k_new, nb, v_fused, fb) || overlap(v_new, nb, k_fused, fb) ||
+      overlap(v_new, nb, v_fused, fb) || overlap(k_fused, fb, v_fused, fb))
+    return fail(SRA_E_ALIAS, "fresh rows and fused cache overlap");
+  hipError_t e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_kv_heads, n_req, R, L, k_new,
+                                     v_new, R, 0, row_pos, k_fused, v_fused, nullptr, shape->rope_base, stream);
+  if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  return ok();
+}
+
+int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_new,
+                           const int32_t* row_pos, int32_t R, const void* k_fused,
+                           const void* v_fused, int32_t L, void* out, float* lse, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (n_req <= 0 || R < 0 || L <= 0 || R > L) return fail(SRA_E_SHAPE, "need n_req > 0, 0 <= R <= L");
+  if ((rc = check_ptr(q_new, "q_new")) || (rc = check_ptr(k_fused, "k_fused")) ||
+      (rc = check_ptr(v_fused, "v_fused")) || (rc = check_ptr(out, "out")))
+    return rc;
+  if (!row_pos) return fail(SRA_E_NULL, "row_pos is NULL");
+  if ((rc = check_attn_limits(shape, R, L))) return rc;
+  const size_t es = elem_size(shape);
+  const size_t ob = (size_t)n_req * R * shape->n_q_heads * shape->head_dim * es;
+  const size_t fb = (size_t)n_req * L * shape->n_kv_heads * shape->head_dim * es;
+  if (overlap(out, ob, k_fused, fb) || overlap(out, ob, v_fused, fb) || overlap(out, ob, q_new, ob))
+    return fail(SRA_E_ALIAS, "out overlaps an input");
+  const Plan p = make_plan(shape, n_req, 1, L, R, 1);
+  if ((rc = check_ws(ws, ws_bytes, p.attn_end))) return rc;
+  float2* cs = reinterpret_cast<float2*>(wsp(ws, p.cs));
+  hipError_t e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, cs, shape->rope_base, stream);
+  if (e != hipSuccess) return hip_fail(e, "rotary table launch");
+  if ((rc = do_attn(shape, n_req, q_new, R, 0, row_pos, R, k_fused, v_fused, L, out, lse, cs, ws, p, stream)))
+    return rc;
+  return ok();
+}
+
+int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  if (!a) return fail(SRA_E_NULL, "args is NULL");
+  const sra_shape* s = &a->shape;
+  if ((rc = check_shape(s))) return rc;
+  const int n_req = a->n_req, L = a->total_len, Lq = a->query_len, R = a->n_rows;
+  if (n_req <= 0 || Lq < 0 || L <= 0) return fail(SRA_E_SHAPE, "need n_req > 0, query_len >= 0, total_len > 0");
+  if ((rc = check_ptr(a->k_store, "k_store")) || (rc = check_ptr(a->v_store, "v_store")) ||
+      (rc = check_ptr(a->q_fresh, "q_fresh")) || (rc = check_ptr(a->k_fresh, "k_fresh")) ||
+      (rc = check_ptr(a->v_fresh, "v_fresh")) || (rc = check_ptr(a->k_fused, "k_fused")) ||
+      (rc = check_ptr(a->v_fused, "v_fused")) || (rc = check_ptr(a->out, "out")))
+    return rc;
+  if (!a->row_pos) return fail(SRA_E_NULL, "row_pos is NULL");
+  int Lctx = 0;
+  if ((rc = check_chunks(a->chunks, n_req, a->n_chunks, a->store_rows, &Lctx))) return rc;
+  if (Lctx + Lq != L) return fail(SRA_E_SHAPE, "total_len %d != context %d + query %d", L, Lctx, Lq);
+  if (R < Lq || R > L) return fail(SRA_E_SHAPE, "n_rows %d outside [query_len, total_len]", R);
+  if ((rc = check_attn_limits(s, R, L))) return rc;
+  const size_t es = elem_size(s);
+  const size_t kvrow = (size_t)s->n_kv_heads * s->head_dim * es;
+  const size_t sb = (size_t)a->store_rows * kvrow, fb = (size_t)n_req * L * kvrow;
+  const size_t ob = (size_t)n_req * R * s->n_q_heads * s->head_dim * es;
+  if (overlap(a->k_store, sb, a->k_fused, fb) || overlap(a->k_store, sb, a->v_fused, fb) ||
+      overlap(a->v_store, sb, a->k_fused, fb) || overlap(a->v_store, sb, a->v_fused, fb) ||
+      overlap(a->k_fused, fb, a->v_fused, fb) || overlap(a->out, ob, a->k_fused, fb) ||
+      overlap(a->out, ob, a->v_fused, fb) || overlap(a->k_fresh, fb, a->k_fused, fb) ||
+      overlap(a->v_fresh, fb, a->v_fused, fb) || overlap(a->k_fresh, fb, a->v_fused, fb) ||
+      overlap(a->v_fresh, fb, a->k_fused, fb))
+    return fail(SRA_E_ALIAS, "an input buffer overlaps an output buffer");
+  int N = R - Lq;
+  if (a->q_crit) {
+    if (Lq < 1) return fail(SRA_E_SHAPE, "scoring needs at least one query row");
+    if ((rc = check_ptr(a->k_crit_store, "k_crit_store"))) return rc;
+    int Lc2 = 0;
+    if ((rc = check_chunks(a->chunks, n_req, a->n_chunks, a->crit_store_rows, &Lc2))) return rc;
+    if ((rc = check_score_limits(s, n_req, a->n_chunks, Lq))) return rc;
+    if ((rc = resolve_count(n_req, a->n_chunks, a->chunks, Lctx, a->n_select, a->chunk_quota, &N))) return rc;
+    if (N + Lq != R) return fail(SRA_E_SHAPE, "n_rows %d != selected %d + query %d", R, N, Lq);
+  }
+  const Plan p = make_plan(s, n_req, a->n_chunks, L, R, Lq);
+  const size_t need = a->q_crit ? p.total : p.attn_end;
+  if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+
+  hipEvent_t* ev = a->stage_events;
+  auto mark = [&](int i) -> int {
+    if (!ev) return SRA_OK;
+    hipError_t er = hipEventRecord(ev[i], stream);
+    return er == hipSuccess ? SRA_OK : hip_fail(er, "stage event record");
+  };
+  if ((rc = mark(0))) return rc;
+  if ((rc = do_rerotate(s, n_req, a->k_store, a->v_store, a->chunks, a->n_chunks, a->k_fused,
+                        a->v_fused, L, stream)))
+    return rc;
+  if ((rc = mark(1)) || (rc = mark(2))) return rc;
+  if (a->q_crit) {
+    if ((rc = do_score_select(s, n_req, a->q_crit, Lq, a->k_crit_store, a->chunks, a->n_chunks, Lctx,
+                              N, a->chunk_quota, a->scores, a->row_pos, ws, p, stream)))
+      return rc;
+  }
+  if ((rc = mark(3)) || (rc = mark(4))) return rc;
+  float2* cs = reinterpret_cast<float2*>(wsp(ws, p.cs));
+  hipError_t e = sra::launch_scatter(s->dtype, s->head_dim, s->n_kv_heads, n_req, R, L, a->k_fresh,
+                                     a->v_fresh, L, 1, a->row_pos, a->k_fused, a->v_fused, cs,
+                                     s->rope_base, stream);
+  if (e != hipSuccess) return hip_fail(e, "scatter launch");
+  if ((rc = mark(5)) || (rc = mark(6))) return rc;
+  if ((rc = do_attn(s, n_req, a->q_fresh, L, 1, a->row_pos, R, a->k_fused, a->v_fused, L, a->out,
+                    a->lse, cs, ws, p, stream)))
+    return rc;
+  if ((rc = mark(7))) return rc;
+  return ok();
+}
+
+int sra_check_rows(const int32_t* row_pos, int32_t n_req, int32_t R, int32_t L, int32_t* first_bad,
+                   hipStream_t stream) {
+  if (!row_pos) return fail(SRA_E_NULL, "row_pos is NULL");
+  if (n_req <= 0 || R < 0 || L <= 0) return fail(SRA_E_SHAPE, "need n_req > 0, R >= 0, L > 0");
+  int* d_bad = nullptr;
+  hipError_t e = hipMalloc(&d_bad, sizeof(int));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+  int h_bad = std::numeric_limits<int>::max();
+  e = hipMemcpyAsync(d_bad, &h_bad, sizeof(int), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = sra::launch_check_rows(row_pos, n_req, R, L, d_bad, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(&h_bad, d_bad, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  hipFree(d_bad);
+  if (e != hipSuccess) return hip_fail(e, "row check");
+  if (h_bad != std::numeric_limits<int>::max()) {
+    if (first_bad) *first_bad = h_bad;
+    return fail(SRA_E_ROWS, "row_pos[%d] breaks strictly increasing order or range [0, %d)", h_bad, L);
+  }
+  if (first_bad) *first_bad = -1;
+  return ok();
+}
+
+}  // extern "C"

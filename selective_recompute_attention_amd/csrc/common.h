@@ -1,0 +1,105 @@
+// Shared definitions of the HIP kernels of the KV-cache fusion step (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sra {
+
+// Chunk/segment table passed by value as a kernel argument (no host-to-device copy).
+// Entry e covers rows [0, len[e]) of one chunk of request req[e]: store rows src[e] + t,
+// fused rows dst[e] + t, re-rotation delta[e]. blk0 is the exclusive prefix of the number
+// of thread blocks each entry gets; a launch handles blocks [0, blk0[n]). Longer tables are
+// split across several launches.
+constexpr int kMaxEntries = 80;
+struct ChunkTab {
+  int n;
+  int req[kMaxEntries];
+  int src[kMaxEntries];
+  int len[kMaxEntries];
+  int dst[kMaxEntries];
+  int delta[kMaxEntries];
+  int blk0[kMaxEntries + 1];
+};
+
+// Selection units: top-`quota` of fused context positions [begin, begin + len) of request
+// req, written at row_pos[req][out_off ...]; the unit with writes_query set also appends
+// the query positions.
+struct SelTab {
+  int n;
+  int req[kMaxEntries];
+  int begin[kMaxEntries];
+  int len[kMaxEntries];
+  int quota[kMaxEntries];
+  int out_off[kMaxEntries];
+  int writes_query[kMaxEntries];
+};
+
+__device__ __forceinline__ int find_entry(const ChunkTab& t, int blk) {
+  int e = 0;
+  while (e + 1 < t.n && t.blk0[e + 1] <= blk) ++e;
+  return e;
+}
+
+// bfloat16 <-> float32 (round to nearest, ties to even; NaN stays NaN).
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// theta_i = base^(-2i/d) and the rotation angle pos * theta_i, both in float64.
+__device__ __forceinline__ double rope_theta(int i, int d, double base) {
+  return pow(base, -2.0 * (double)i / (double)d);
+}
+__device__ __forceinline__ float2 rope_cs(double pos, int i, int d, double base) {
+  double s, c;
+  sincos(pos * rope_theta(i, d, base), &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
+}  // namespace sra
+
+// ---------------------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launch(es). dtype: 0 bf16, 1 f32.
+namespace sra {
+hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
+                           const void* ks, const void* vs, void* kf, void* vf, int64_t L,
+                           double base, hipStream_t st);
+hipError_t launch_scatter(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
+                          const void* vn, int fresh_rows, int indexed, const int* row_pos,
+                          void* kf, void* vf, float2* cs_out, double base, hipStream_t st);
+hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
+                             double base, hipStream_t st);
+hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
+                          int32_t* anchors, float* norms, hipStream_t st);
+hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv, int Mpad,
+                             int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
+                             int entry_base, double base, hipStream_t st);
+hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, int Hkv, int Mpad, int Mvalid,
+                             int Lctx, const void* kc, const uint16_t* qrot, int64_t plane,
+                             int entry_base, int blk_base, float2* ml_part, const float2* ml_final,
+                             float* colsum, float scale_log2, hipStream_t st);
+hipError_t launch_score_merge(int n_req, int Hkv, int Mpad, int Mvalid, const int* req_blk0,
+                              const float2* ml_part, float2* ml_final, hipStream_t st);
+hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,
+                            int Lctx, const float* qc, const float* kc, float* prob,
+                            float scale_log2, double base, hipStream_t st);
+hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, float* parts,
+                             hipStream_t st);
+hipError_t launch_select(const SelTab& tab, int nparts, int Lctx, int Lq, int R, const float* parts,
+                         float* scores, int* row_pos, hipStream_t st);
+hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* q,
+                            int q_rows, int indexed, const int* row_pos, const float2* cs,
+                            const uint16_t* kf, const uint16_t* vf, uint16_t* out, float* lse,
+                            int n_splits, int key_split, float* part_o, float2* part_ml,
+                            hipStream_t st);
+hipError_t launch_attn_f32(int D, int n_req, int Hq, int Hkv, int R, int L, const float* q,
+                           int q_rows, int indexed, const int* row_pos, const float2* cs,
+                           const float* kf, const float* vf, float* out, float* lse,
+                           hipStream_t st);
+hipError_t launch_check_rows(const int* row_pos, int n_req, int R, int L, int* bad,
+                             hipStream_t st);
+}  // namespace sra

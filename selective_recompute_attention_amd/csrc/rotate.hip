@@ -1,0 +1,230 @@
+// Streaming rotary kernels: S1 re-rotation of cached chunk keys into the fused cache, S3 scatter
+// of fresh K/V rows, the per-row angle table used by the sparse attention, and the row check.
+//
+// S1 follows "full KV reuse after adjusting the position encoding" (CacheBlend problem definition
+// page, §2.4): a chunk cached at original positions orig + t moves to fused rows n_c + t, so each
+// key pair (x_i, x_{i+d/2}) turns by delta_c * theta_i with delta_c = n_c - orig. S3 follows the
+// per-layer selective recompute flow (KVCache reuse 01, §1.3.4): fresh K/V of the selected tokens
+// replace the reused rows, K rotated at the token's absolute position.
+//
+// Both are pure HBM streams: every thread moves 16-byte vectors, rows are contiguous, angles are
+// formed once per block in float64 and kept in LDS as float32 cos/sin.
+#include "common.h"
+
+namespace sra {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Vec;  // 16-byte vector of T, unpacked to float
+template <>
+struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(v[k] << 16);
+      f[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+    }
+  }
+  __device__ static u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = pack_bf2(f[2 * k], f[2 * k + 1]);
+    return v;
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(u32x4 v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]);
+  }
+  __device__ static u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __float_as_uint(f[k]);
+    return v;
+  }
+};
+
+// Rotate `n_units` units of one or more rows. A unit is VW consecutive pairs of one head:
+// elements [i0, i0+VW) and [i0+H, i0+H+VW) of a D-element head vector.
+template <typename T, int D>
+__device__ __forceinline__ void rotate_rows(const T* __restrict__ src, T* __restrict__ dst,
+                                            int n_heads_total, const float2* cs, int tid,
+                                            int nthr) {
+  constexpr int H = D / 2;
+  constexpr int VW = Vec<T>::N;
+  constexpr int UPH = H / VW;  // units per head
+  const int n_units = n_heads_total * UPH;
+  for (int u = tid; u < n_units; u += nthr) {
+    const int hv = u / UPH;
+    const int i0 = (u % UPH) * VW;
+    const T* a = src + (int64_t)hv * D + i0;
+    T* o = dst + (int64_t)hv * D + i0;
+    float fa[VW], fb[VW], ra[VW], rb[VW];
+    Vec<T>::unpack(*reinterpret_cast<const u32x4*>(a), fa);
+    Vec<T>::unpack(*reinterpret_cast<const u32x4*>(a + H), fb);
+#pragma unroll
+    for (int k = 0; k < VW; ++k) {
+      const float c = cs[i0 + k].x, s = cs[i0 + k].y;
+      ra[k] = fa[k] * c - fb[k] * s;
+      rb[k] = fa[k] * s + fb[k] * c;
+    }
+    *reinterpret_cast<u32x4*>(o) = Vec<T>::pack(ra);
+    *reinterpret_cast<u32x4*>(o + H) = Vec<T>::pack(rb);
+  }
+}
+
+__device__ __forceinline__ void copy16(const void* __restrict__ src, void* __restrict__ dst,
+                                       int64_t n16, int tid, int nthr) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  for (int64_t u = tid; u < n16; u += nthr) d[u] = s[u];
+}
+
+// One block per (chunk entry, block of rows_per_blk rows of that chunk).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int rows_per_blk,
+                                                  const T* __restrict__ ks,
+                                                  const T* __restrict__ vs, T* __restrict__ kf,
+                                                  T* __restrict__ vf, int64_t L, double base) {
+  constexpr int H = D / 2;
+  __shared__ float2 cs[H];
+  const int e = find_entry(tab, blockIdx.x);
+  const int t0 = (blockIdx.x - tab.blk0[e]) * rows_per_blk;
+  const int nr = min(rows_per_blk, tab.len[e] - t0);
+  const int delta = tab.delta[e];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) cs[i] = rope_cs((double)delta, i, D, base);
+  __syncthreads();
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t src0 = ((int64_t)tab.src[e] + t0) * row_elems;
+  const int64_t dst0 = ((int64_t)tab.req[e] * L + tab.dst[e] + t0) * row_elems;
+  const int64_t n16 = (int64_t)nr * row_elems * sizeof(T) / 16;
+  copy16(vs + src0, vf + dst0, n16, threadIdx.x, blockDim.x);
+  if (delta == 0) {
+    // rotation by zero is the identity: keep the cached bits
+    copy16(ks + src0, kf + dst0, n16, threadIdx.x, blockDim.x);
+  } else {
+    rotate_rows<T, D>(ks + src0, kf + dst0, nr * Hkv, cs, threadIdx.x, blockDim.x);
+  }
+}
+
+// One block per (recomputed row r, request). Fresh rows are compact (row r) or position-indexed
+// (row row_pos[r]). Writes the row's cos/sin table when cs_out is given.
+template <typename T, int D>
+__global__ __launch_bounds__(128) void k_scatter(int Hkv, int R, int L, const T* __restrict__ kn,
+                                                 const T* __restrict__ vn, int fresh_rows,
+                                                 int indexed, const int* __restrict__ row_pos,
+                                                 T* __restrict__ kf, T* __restrict__ vf,
+                                                 float2* __restrict__ cs_out, double base) {
+  constexpr int H = D / 2;
+  __shared__ float2 cs[H];
+  const int r = blockIdx.x, q = blockIdx.y;
+  const int p = row_pos[(int64_t)q * R + r];
+  if (p < 0 || p >= L) return;  // rows outside the cache are never written
+  const int srow = indexed ? p : r;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float2 v = rope_cs((double)p, i, D, base);
+    cs[i] = v;
+    if (cs_out) cs_out[((int64_t)q * R + r) * H + i] = v;
+  }
+  __syncthreads();
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t src0 = ((int64_t)q * fresh_rows + srow) * row_elems;
+  const int64_t dst0 = ((int64_t)q * L + p) * row_elems;
+  copy16(vn + src0, vf + dst0, row_elems * sizeof(T) / 16, threadIdx.x, blockDim.x);
+  rotate_rows<T, D>(kn + src0, kf + dst0, Hkv, cs, threadIdx.x, blockDim.x);
+}
+
+template <int D>
+__global__ void k_rope_table(int R, const int* __restrict__ row_pos, float2* __restrict__ cs_out,
+                             double base) {
+  constexpr int H = D / 2;
+  const int r = blockIdx.x, q = blockIdx.y;
+  const int p = row_pos[(int64_t)q * R + r];
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    cs_out[((int64_t)q * R + r) * H + i] = rope_cs((double)p, i, D, base);
+}
+
+__global__ void k_check_rows(const int* __restrict__ row_pos, int n_req, int R, int L,
+                             int* __restrict__ bad) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n_req * R) return;
+  const int r = (int)(idx % R);
+  const int v = row_pos[idx];
+  bool ok = v >= 0 && v < L;
+  if (r > 0) ok = ok && row_pos[idx - 1] < v;
+  if (!ok) atomicMin(bad, (int)idx);
+}
+
+}  // namespace
+
+hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
+                           const void* ks, const void* vs, void* kf, void* vf, int64_t L,
+                           double base, hipStream_t st) {
+  const int nblk = tab.blk0[tab.n];
+  if (nblk == 0) return hipSuccess;
+  dim3 g(nblk), b(256);
+  if (dtype == 0 && D == 128)
+    k_rerotate<uint16_t, 128><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const uint16_t*)ks,
+                                                (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, base);
+  else if (dtype == 0 && D == 64)
+    k_rerotate<uint16_t, 64><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const uint16_t*)ks,
+                                               (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, base);
+  else if (dtype == 1 && D == 128)
+    k_rerotate<float, 128><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const float*)ks,
+                                             (const float*)vs, (float*)kf, (float*)vf, L, base);
+  else
+    k_rerotate<float, 64><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const float*)ks,
+                                            (const float*)vs, (float*)kf, (float*)vf, L, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
+                          const void* vn, int fresh_rows, int indexed, const int* row_pos,
+                          void* kf, void* vf, float2* cs_out, double base, hipStream_t st) {
+  if (R == 0 || n_req == 0) return hipSuccess;
+  dim3 g(R, n_req), b(128);
+  if (dtype == 0 && D == 128)
+    k_scatter<uint16_t, 128><<<g, b, 0, st>>>(Hkv, R, L, (const uint16_t*)kn, (const uint16_t*)vn,
+                                               fresh_rows, indexed, row_pos, (uint16_t*)kf,
+                                               (uint16_t*)vf, cs_out, base);
+  else if (dtype == 0 && D == 64)
+    k_scatter<uint16_t, 64><<<g, b, 0, st>>>(Hkv, R, L, (const uint16_t*)kn, (const uint16_t*)vn,
+                                              fresh_rows, indexed, row_pos, (uint16_t*)kf,
+                                              (uint16_t*)vf, cs_out, base);
+  else if (dtype == 1 && D == 128)
+    k_scatter<float, 128><<<g, b, 0, st>>>(Hkv, R, L, (const float*)kn, (const float*)vn,
+                                            fresh_rows, indexed, row_pos, (float*)kf, (float*)vf,
+                                            cs_out, base);
+  else
+    k_scatter<float, 64><<<g, b, 0, st>>>(Hkv, R, L, (const float*)kn, (const float*)vn,
+                                           fresh_rows, indexed, row_pos, (float*)kf, (float*)vf,
+                                           cs_out, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
+                             double base, hipStream_t st) {
+  if (R == 0 || n_req == 0) return hipSuccess;
+  dim3 g(R, n_req), b(64);
+  if (D == 128)
+    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
+  else
+    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_rows(const int* row_pos, int n_req, int R, int L, int* bad,
+                             hipStream_t st) {
+  const int64_t n = (int64_t)n_req * R;
+  if (n == 0) return hipSuccess;
+  k_check_rows<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(row_pos, n_req, R, L, bad);
+  return hipGetLastError();
+}
+
+}  // namespace sra

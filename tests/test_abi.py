@@ -1,0 +1,181 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and reports every
+host-detectable error with its status code before touching the device.
+
+Device pointers here are fake (aligned, non-NULL integers); every call below fails validation
+on the host, so no HIP call is made with them.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from selective_recompute_attention_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sra.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libsra.so not built")
+
+FAKE = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(16)]   # distinct, 16-byte aligned
+
+
+def shape(hq=32, hkv=8, d=128, dtype=L.DTYPE_BF16, base=10000.0):
+    return L.Shape(hq, hkv, d, dtype, base)
+
+
+def chunks(rows):
+    a = np.asarray(rows, dtype=np.int32).reshape(-1, 4)
+    arr = (L.Chunk * len(a))()
+    ctypes.memmove(arr, a.ctypes.data, a.nbytes)
+    return arr
+
+
+def last_error():
+    return L.lib().sra_last_error().decode()
+
+
+def test_every_declared_symbol_is_exported():
+    names = re.findall(r"^\s*(?:int|size_t|const char\*)\s+(sra_\w+)\s*\(", open(HEADER).read(), re.M)
+    assert len(names) >= 12
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L._SIGS), "binding declarations must mirror the header"
+
+
+def test_error_strings():
+    lib = L.lib()
+    for code in range(10):
+        assert lib.sra_error_string(code)
+    assert lib.sra_error_string(0) == b"success"
+
+
+@pytest.mark.parametrize("num,den,ctx", [(15, 100, 384), (9, 70, 17920), (10, 100, 7680), (0, 5, 9),
+                                         (100, 100, 2560), (1, 3, 10), (7, 70, 17920), (35, 100, 1)])
+def test_select_count_matches_oracle(num, den, ctx):
+    out = ctypes.c_int32(-7)
+    assert L.lib().sra_select_count(num, den, ctx, ctypes.byref(out)) == L.SRA_OK
+    assert out.value == O.select_count(num, den, ctx)
+
+
+def test_select_count_errors():
+    out = ctypes.c_int32()
+    lib = L.lib()
+    assert lib.sra_select_count(1, 0, 10, ctypes.byref(out)) == L.SRA_E_SHAPE
+    assert lib.sra_select_count(-1, 10, 10, ctypes.byref(out)) == L.SRA_E_SHAPE
+    assert lib.sra_select_count(11, 10, 10, ctypes.byref(out)) == L.SRA_E_SHAPE
+    assert lib.sra_select_count(1, 10, 10, None) == L.SRA_E_NULL
+
+
+def test_workspace_size_is_monotone_and_rejects_bad_sizes():
+    lib = L.lib()
+    s = shape()
+    a = lib.sra_workspace_size(ctypes.byref(s), 1, 5, 2592, 416, 32)
+    b = lib.sra_workspace_size(ctypes.byref(s), 4, 5, 2592, 416, 32)
+    assert a > 0 and b > a and a % 256 == 0
+    assert lib.sra_workspace_size(ctypes.byref(shape(hq=30, hkv=8)), 1, 5, 2592, 416, 32) == 0
+    assert lib.sra_workspace_size(ctypes.byref(shape(d=96)), 1, 5, 2592, 416, 32) == 0
+    assert lib.sra_workspace_size(None, 1, 5, 2592, 416, 32) == 0
+    assert lib.sra_workspace_size(ctypes.byref(s), 1, 5, 10, 4, 11) == 0
+
+
+def test_fuse_rerotate_host_errors():
+    lib = L.lib()
+    ok = chunks([[0, 4, 0, 0], [4, 4, 4, 0]])
+    st = None
+    call = lambda sh, ch, n, ks=FAKE[0], vs=FAKE[1], kf=FAKE[2], vf=FAKE[3], rows=8, Ln=10: \
+        lib.sra_fuse_rerotate(ctypes.byref(sh), 1, ks, vs, rows, ch, n, kf, vf, Ln, st)
+    assert call(shape(hq=30), ok, 2) == L.SRA_E_SHAPE
+    assert call(shape(d=80), ok, 2) == L.SRA_E_SHAPE
+    assert call(shape(dtype=5), ok, 2) == L.SRA_E_DTYPE
+    assert call(shape(), ok, 2, ks=None) == L.SRA_E_NULL
+    assert call(shape(), ok, 2, kf=ctypes.c_void_p(0x10000008)) == L.SRA_E_SHAPE     # misaligned
+    assert call(shape(), chunks([[0, 4, 0, 0], [4, 4, 5, 0]]), 2) == L.SRA_E_CHUNKS   # gap
+    assert "dst_row" in last_error()
+    assert call(shape(), chunks([[0, 4, 0, 0], [6, 4, 4, 0]]), 2) == L.SRA_E_CHUNKS   # past store end
+    assert call(shape(), ok, 2, Ln=7) == L.SRA_E_SHAPE                               # L < L_ctx
+    # the store overlaps the fused output
+    assert call(shape(), ok, 2, kf=FAKE[0]) == L.SRA_E_ALIAS
+    assert lib.sra_fuse_rerotate(ctypes.byref(shape()), 1, FAKE[0], FAKE[1], 8, None, 2, FAKE[2], FAKE[3],
+                                 10, None) == L.SRA_E_NULL
+
+
+def test_score_select_host_errors():
+    lib = L.lib()
+    ch = chunks([[0, 64, 0, 0], [64, 64, 64, 0]])
+    s = shape()
+    need = lib.sra_workspace_size(ctypes.byref(s), 1, 2, 136, 20, 8)
+    call = lambda n_select=12, quota=None, ws=FAKE[4], wsb=need, Lq=8, sh=s: lib.sra_score_select(
+        ctypes.byref(sh), 1, FAKE[0], Lq, FAKE[1], 128, ch, 2, n_select, quota, FAKE[2], FAKE[3], ws, wsb, None)
+    assert call(n_select=129) == L.SRA_E_SHAPE              # N > L_ctx
+    assert call(n_select=-1) == L.SRA_E_SHAPE
+    assert call(Lq=0) == L.SRA_E_SHAPE
+    assert call(ws=None) == L.SRA_E_WORKSPACE
+    assert call(wsb=need - 256) == L.SRA_E_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10000010)) == L.SRA_E_WORKSPACE   # not 256-byte aligned
+    bad_q = (ctypes.c_int32 * 2)(65, 1)
+    assert call(quota=ctypes.cast(bad_q, ctypes.POINTER(ctypes.c_int32))) == L.SRA_E_SHAPE
+    assert call(Lq=300, sh=shape(hq=64, hkv=8)) == L.SRA_E_LIMIT       # Lq * g > 2048
+
+
+def test_quota_totals_must_match_across_requests():
+    lib = L.lib()
+    ch = chunks([[0, 8, 0, 0], [8, 8, 8, 0], [16, 8, 0, 0], [24, 8, 8, 0]])
+    q = (ctypes.c_int32 * 4)(2, 3, 3, 3)
+    rc = lib.sra_select_topn(FAKE[0], 2, 16, -1, ctypes.cast(q, ctypes.POINTER(ctypes.c_int32)), ch, 2, 4,
+                             FAKE[1], None)
+    assert rc == L.SRA_E_SHAPE and "selects" in last_error()
+
+
+def test_attention_and_scatter_host_errors():
+    lib = L.lib()
+    s = shape()
+    assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 10, FAKE[2], FAKE[3], 20, FAKE[4],
+                                      None, None, 0, None) == L.SRA_E_WORKSPACE
+    assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 30, FAKE[2], FAKE[3], 20, FAKE[4],
+                                      None, FAKE[5], 1 << 30, None) == L.SRA_E_SHAPE       # R > L
+    assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 10, FAKE[2], FAKE[3], 20, FAKE[2],
+                                      None, FAKE[5], 1 << 30, None) == L.SRA_E_ALIAS       # out is k_fused
+    assert lib.sra_scatter_kv(ctypes.byref(s), 1, FAKE[0], FAKE[1], None, 4, FAKE[2], FAKE[3], 20,
+                              None) == L.SRA_E_NULL
+    assert lib.sra_scatter_kv(ctypes.byref(s), 1, FAKE[0], FAKE[1], FAKE[6], 4, FAKE[0], FAKE[3], 20,
+                              None) == L.SRA_E_ALIAS
+    assert lib.sra_check_rows(None, 1, 4, 10, None, None) == L.SRA_E_NULL
+
+
+def test_anchor_host_errors():
+    lib = L.lib()
+    s = shape()
+    ch = chunks([[0, 8, 0, 0]])
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 9, FAKE[1], None, None) == L.SRA_E_SHAPE
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 0, FAKE[1], None, None) == L.SRA_E_SHAPE
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 65, FAKE[1], None, None) == L.SRA_E_LIMIT
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 7, ch, 1, 2, FAKE[1], None, None) == L.SRA_E_CHUNKS
+    big = chunks([[0, 9000, 0, 0]])
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 9000, big, 1, 2, FAKE[1], None, None) == L.SRA_E_LIMIT
+
+
+def test_fused_layer_host_errors():
+    lib = L.lib()
+    ch = chunks([[0, 64, 0, 0], [64, 64, 64, 0]])
+    a = L.LayerArgs()
+    a.shape = shape()
+    a.n_req, a.n_chunks, a.chunks = 1, 2, ctypes.cast(ch, ctypes.POINTER(L.Chunk))
+    a.query_len, a.total_len = 8, 136
+    a.k_store, a.v_store, a.store_rows = FAKE[0], FAKE[1], 128
+    a.q_fresh, a.k_fresh, a.v_fresh = FAKE[2], FAKE[3], FAKE[4]
+    a.row_pos, a.n_rows = FAKE[5], 20
+    a.k_fused, a.v_fused, a.out = FAKE[6], FAKE[7], FAKE[8]
+    a.q_crit, a.k_crit_store, a.crit_store_rows, a.n_select = FAKE[9], FAKE[10], 128, 13   # 13 + 8 != 20
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[11], 1 << 30, None) == L.SRA_E_SHAPE
+    a.total_len = 137
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[11], 1 << 30, None) == L.SRA_E_SHAPE
+    a.total_len, a.n_select = 136, 12
+    a.out = FAKE[6]
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[11], 1 << 30, None) == L.SRA_E_ALIAS
+    a.out = FAKE[8]
+    assert lib.sra_fused_layer(ctypes.byref(a), None, 0, None) == L.SRA_E_WORKSPACE
+    assert lib.sra_fused_layer(None, None, 0, None) == L.SRA_E_NULL
