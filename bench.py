@@ -175,6 +175,7 @@ def main():
         }
         reps.append((ins, outs))
     ws = torch.empty(sra.workspace_size(shape, 1, n_chunks, L, R, Lq), dtype=torch.uint8, device="cuda")
+    anchor_ws = torch.empty(sra.anchor_workspace_size(w.chunks[0]), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     hip = Hip()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -183,7 +184,7 @@ def main():
         ins, outs = reps[i % len(reps)]
         if anchor_ev is not None:
             hip.record(anchor_ev[0], sp)
-        sra.extract_anchors(shape, ins["k_crit"], w.chunks[0], cfg.anchors_k, outs["anchors"])
+        sra.extract_anchors(shape, ins["k_crit"], w.chunks[0], cfg.anchors_k, outs["anchors"], anchor_ws)
         if anchor_ev is not None:
             hip.record(anchor_ev[1], sp)
         sra.fused_layer(shape, chunks=w.chunks, k_store=ins["k_store"], v_store=ins["v_store"],

@@ -64,7 +64,6 @@ extern "C" {
 
 /* Implementation limits (checked, reported as SRA_E_LIMIT). */
 #define SRA_MAX_ANCHOR_K        64      /* anchors per chunk                              */
-#define SRA_MAX_ANCHOR_TOKENS   8192    /* tokens of one chunk scanned for anchors        */
 
 /* Head geometry shared by every call. Hq must be a multiple of Hkv; query head h reads
  * KV head h / (Hq/Hkv) (contiguous groups, grouped-query attention). head_dim is 64 or 128. */
@@ -173,12 +172,14 @@ int sra_fuse_rerotate(const sra_shape* shape, int32_t n_req,
  * the first k tokens in the order (larger norm first, lower t on a tie).
  * chunks: host [n_chunks], any rows of the store (overlap allowed). anchor_rows: out
  * [n_chunks][k] int32 token offsets t within each chunk. norms: optional out [store_rows]
- * float32, written at the rows the chunks cover (others untouched).
- * Errors: SRA_E_NULL, SRA_E_SHAPE (k < 1 or k > n_tokens), SRA_E_LIMIT (k > 64 or
- * n_tokens > 8192), SRA_E_CHUNKS, SRA_E_DTYPE, SRA_E_HIP. */
+ * float32, written at the rows the chunks cover (others untouched). ws: device workspace of at
+ * least 8 bytes per chunk token (sum of n_tokens), 256-byte aligned (float64 sums of squares).
+ * Errors: SRA_E_NULL, SRA_E_SHAPE (k < 1 or k > n_tokens), SRA_E_LIMIT (k > 64),
+ * SRA_E_CHUNKS, SRA_E_DTYPE, SRA_E_WORKSPACE, SRA_E_HIP. */
 int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t store_rows,
                         const sra_chunk* chunks, int32_t n_chunks, int32_t k,
-                        int32_t* anchor_rows, float* norms, hipStream_t stream);
+                        int32_t* anchor_rows, float* norms, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Query-centric scores and top-N selection from one critical layer (QCFuse summary (zh)
  * §2.A critical-layer attention profiling: the attention distribution of the query's Q

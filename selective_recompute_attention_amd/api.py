@@ -12,7 +12,7 @@ import torch
 
 from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, check, lib)  # noqa: F401
 
-__all__ = ["make_shape", "select_count", "workspace_size", "fuse_rerotate", "extract_anchors",
+__all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors",
            "score_select", "select_topn", "scatter_kv", "sparse_causal_attn", "fused_layer",
            "check_rows", "chunk_array", "SRAError"]
 
@@ -77,10 +77,16 @@ def fuse_rerotate(shape, k_store, v_store, chunks, k_fused, v_fused, stream=None
                                   k_fused.shape[-3], _stream(stream)))
 
 
-def extract_anchors(shape, k_store, chunks, k, anchor_rows, norms=None, stream=None):
+def anchor_workspace_size(chunks) -> int:
+    """Bytes of workspace sra_extract_anchors needs: 8 per chunk token."""
+    return 8 * int(np.asarray(chunks, dtype=np.int64).reshape(-1, 4)[:, 1].sum())
+
+
+def extract_anchors(shape, k_store, chunks, k, anchor_rows, ws, norms=None, stream=None):
     ch = np.asarray(chunks, dtype=np.int32).reshape(-1, 4)
     check(lib().sra_extract_anchors(ctypes.byref(shape), _ptr(k_store), k_store.shape[0], chunk_array(ch),
-                                    len(ch), int(k), _ptr(anchor_rows), _ptr(norms), _stream(stream)))
+                                    len(ch), int(k), _ptr(anchor_rows), _ptr(norms), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def score_select(shape, q_crit, k_crit_store, chunks, n_select, quotas, scores, row_pos, ws, stream=None):

@@ -2,18 +2,16 @@
 // lightweight query probing: offline, each chunk keeps the few tokens with the largest key norm
 // as a compressed semantic summary).
 //
-// One block per chunk. Each wave reduces the squared entries of one token's key row (all KV
-// heads and dims) in float64 -- squares of bf16/f32 values are exact there, so the ranking
-// matches an exact computation up to the last float64 bit -- then k block-wide argmax rounds
-// pick the anchors in the order (larger norm first, lower token offset on a tie).
+// Two launches, both wide: (1) one wave per token row reduces the squares of its key (all KV heads
+// and dims) in float64 -- squares of bf16/f32 values are exact there, so the ranking matches an
+// exact computation up to the last float64 bit -- into the workspace; (2) one wave per chunk picks
+// the k largest in the order (larger norm first, lower token offset on a tie).
 #include <float.h>
 
 #include "common.h"
 
 namespace sra {
 namespace {
-
-constexpr int kAnchorTokens = 8192;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,65 +39,90 @@ __device__ __forceinline__ double sumsq16<float>(u32x4 v) {
   return acc;
 }
 
+// Table use: entry e = one chunk; src/len its store rows; dst its output slot; delta its offset in
+// the sum-of-squares workspace. blk0 counts blocks of 4 rows (one wave per row).
 template <typename T>
-__global__ __launch_bounds__(256) void k_anchors(ChunkTab tab, int row_elems, int k,
-                                                 const T* __restrict__ ks,
-                                                 int32_t* __restrict__ anchors,
-                                                 float* __restrict__ norms) {
-  __shared__ double ss[kAnchorTokens];
-  __shared__ double red_v[4];
-  __shared__ int red_t[4];
-  const int e = blockIdx.x;
-  const int src = tab.src[e], len = tab.len[e], out = tab.dst[e];
+__global__ __launch_bounds__(256) void k_row_sumsq(ChunkTab tab, int row_elems,
+                                                   const T* __restrict__ ks,
+                                                   double* __restrict__ ss,
+                                                   float* __restrict__ norms) {
+  const int e = find_entry(tab, blockIdx.x);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = (blockIdx.x - tab.blk0[e]) * 4 + wave;
+  if (t >= tab.len[e]) return;
+  const int64_t row = (int64_t)tab.src[e] + t;
+  const u32x4* p = reinterpret_cast<const u32x4*>(ks + row * row_elems);
   const int n16 = row_elems * (int)sizeof(T) / 16;
-  for (int t = wave; t < len; t += 4) {
-    const u32x4* row = reinterpret_cast<const u32x4*>(ks + ((int64_t)src + t) * row_elems);
-    double acc = 0.0;
-    for (int u = lane; u < n16; u += 64) acc += sumsq16<T>(row[u]);
-    // fixed-order tree: lane 0 ends with the same sum on every run
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);
-    if (lane == 0) {
-      ss[t] = acc;
-      if (norms) norms[(int64_t)src + t] = (float)sqrt(acc);
-    }
+  double acc = 0.0;
+  for (int u = lane; u < n16; u += 64) acc += sumsq16<T>(p[u]);
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);  // fixed-order tree
+  if (lane == 0) {
+    ss[tab.delta[e] + t] = acc;
+    if (norms) norms[row] = (float)sqrt(acc);
   }
-  __syncthreads();
+}
+
+// One wave per chunk. The ranking (larger sum first, lower offset on a tie) is a strict total
+// order, so round r picks the best element ranked after the pick of round r-1: nothing is written
+// back, every round reads the same sums.
+__global__ __launch_bounds__(256) void k_anchor_topk(ChunkTab tab, int k, const double* __restrict__ ss,
+                                                     int32_t* __restrict__ anchors) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= tab.n) return;
+  const int lane = threadIdx.x & 63;
+  const int len = tab.len[e];
+  const double* s = ss + tab.delta[e];
+  // the first 64*kCache sums stay in registers (one batch of independent loads); longer chunks
+  // read the rest from memory each round
+  constexpr int kCache = 16;
+  double cv[kCache];
+#pragma unroll
+  for (int u = 0; u < kCache; ++u) {
+    const int t = lane + 64 * u;
+    cv[u] = t < len ? s[t] : -DBL_MAX;   // below every sum: never picked (k <= len)
+  }
+  double pv = DBL_MAX;   // previous pick (value, offset); start above everything
+  int pt = -1;
   for (int round = 0; round < k; ++round) {
     double bv = -DBL_MAX;
     int bt = INT_MAX;
-    for (int t = threadIdx.x; t < len; t += blockDim.x) {
-      const double v = ss[t];
-      if (v > bv || (v == bv && t < bt)) { bv = v; bt = t; }
+#pragma unroll
+    for (int u = 0; u < kCache; ++u) {
+      const int t = lane + 64 * u;
+      const double v = cv[u];
+      const bool after = v < pv || (v == pv && t > pt);
+      if (after && (v > bv || (v == bv && t < bt))) { bv = v; bt = t; }
+    }
+    for (int t = lane + 64 * kCache; t < len; t += 64) {
+      const double v = s[t];
+      const bool after = v < pv || (v == pv && t > pt);
+      if (after && (v > bv || (v == bv && t < bt))) { bv = v; bt = t; }
     }
     for (int off = 32; off > 0; off >>= 1) {
-      const double ov = __shfl_down(bv, off, 64);
-      const int ot = __shfl_down(bt, off, 64);
+      const double ov = __shfl_xor(bv, off, 64);
+      const int ot = __shfl_xor(bt, off, 64);
       if (ov > bv || (ov == bv && ot < bt)) { bv = ov; bt = ot; }
     }
-    if (lane == 0) { red_v[wave] = bv; red_t[wave] = bt; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 1; w < 4; ++w)
-        if (red_v[w] > bv || (red_v[w] == bv && red_t[w] < bt)) { bv = red_v[w]; bt = red_t[w]; }
-      anchors[(int64_t)out * k + round] = bt;
-      ss[bt] = -1.0;  // below every sum of squares: never picked again
-    }
-    __syncthreads();
+    if (lane == 0) anchors[(int64_t)tab.dst[e] * k + round] = bt;
+    pv = bv;
+    pt = bt;
   }
 }
 
 }  // namespace
 
 hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
-                          int32_t* anchors, float* norms, hipStream_t st) {
+                          double* ss, int32_t* anchors, float* norms, hipStream_t st) {
+  // tab.blk0 counts blocks of 4 rows per chunk
   if (tab.n == 0) return hipSuccess;
+  const int nblk = tab.blk0[tab.n];
   if (dtype == 0)
-    k_anchors<uint16_t><<<dim3(tab.n), dim3(256), 0, st>>>(tab, row_elems, k, (const uint16_t*)ks,
-                                                           anchors, norms);
+    k_row_sumsq<uint16_t><<<dim3(nblk), dim3(256), 0, st>>>(tab, row_elems, (const uint16_t*)ks, ss, norms);
   else
-    k_anchors<float><<<dim3(tab.n), dim3(256), 0, st>>>(tab, row_elems, k, (const float*)ks,
-                                                        anchors, norms);
+    k_row_sumsq<float><<<dim3(nblk), dim3(256), 0, st>>>(tab, row_elems, (const float*)ks, ss, norms);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  k_anchor_topk<<<dim3((tab.n + 3) / 4), dim3(256), 0, st>>>(tab, k, ss, anchors);
   return hipGetLastError();
 }
 

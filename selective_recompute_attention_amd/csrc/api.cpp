@@ -11,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/sra.h"
+#include "sra.h"
 #include "common.h"
 
 namespace {
@@ -108,7 +108,7 @@ AttnSplit attn_split(int n_req, int Hkv, int R, int g, int L) {
   AttnSplit s{1, std::max(L, 1)};
   if (tiles == 0 || tiles >= 512 || L <= 256) return s;
   const int64_t want = ceil_div(1024, tiles);
-  const int64_t n = std::min<int64_t>(want, ceil_div(L, 256));
+  const int64_t n = std::min<int64_t>(std::min<int64_t>(want, ceil_div(L, 256)), 16);  // <= kMaxSplits
   const int ks = (int)(ceil_div(ceil_div(L, n), 64) * 64);
   s.key_split = ks;
   s.n_splits = (int)ceil_div(L, ks);
@@ -330,21 +330,26 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
     for (int q = 0; q < n_req; ++q) req_blk0[q + 1] += req_blk0[q];
     e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int) {
       return sra::launch_score_prep(D, tab, Lq, Hq, Hkv, p.Mpad, Lctx, qc, qrot, p.qrot_plane,
-                                    first, s->rope_base, st);
+                                    first, scale_log2, s->rope_base, st);
     });
     if (e != hipSuccess) return hip_fail(e, "score prep launch");
-    e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
-      return sra::launch_score_pass(1, D, tab, Hkv, p.Mpad, Lq * g, Lctx, kc, qrot, p.qrot_plane,
-                                    first, blk_base, ml_part, ml_final, colsum, scale_log2, st);
-    });
-    if (e != hipSuccess) return hip_fail(e, "score pass 1 launch");
-    e = sra::launch_score_merge(n_req, Hkv, p.Mpad, Lq * g, req_blk0.data(), ml_part, ml_final, st);
-    if (e != hipSuccess) return hip_fail(e, "score merge launch");
-    e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
-      return sra::launch_score_pass(2, D, tab, Hkv, p.Mpad, Lq * g, Lctx, kc, qrot, p.qrot_plane,
-                                    first, blk_base, ml_part, ml_final, colsum, scale_log2, st);
-    });
-    if (e != hipSuccess) return hip_fail(e, "score pass 2 launch");
+    // Pass 2 merges a request's (max, sum) partials itself when they are few; otherwise a wide
+    // merge kernel runs between the passes.
+    int max_blocks = 0;
+    for (int q = 0; q < n_req; ++q) max_blocks = std::max(max_blocks, req_blk0[q + 1] - req_blk0[q]);
+    const int fuse_merge = (int64_t)max_blocks * p.Mpad <= 4096 ? 1 : 0;
+    for (int pass = 1; pass <= 2; ++pass) {
+      if (pass == 2 && !fuse_merge) {
+        e = sra::launch_score_merge(req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, ml_part, ml_final, st);
+        if (e != hipSuccess) return hip_fail(e, "score merge launch");
+      }
+      e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
+        return sra::launch_score_pass(pass, D, tab, req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, Lctx, kc,
+                                      qrot, p.qrot_plane, first, blk_base, ml_part, ml_final, fuse_merge,
+                                      colsum, st);
+      });
+      if (e != hipSuccess) return hip_fail(e, pass == 1 ? "score pass 1 launch" : "score pass 2 launch");
+    }
     return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, Hkv, colsum, sc, row_pos, st);
   }
   // float32 storage: one softmax row per query vector, then fixed-order column sums
@@ -476,7 +481,7 @@ int sra_fuse_rerotate(const sra_shape* shape, int32_t n_req, const void* k_store
 
 int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t store_rows,
                         const sra_chunk* chunks, int32_t n_chunks, int32_t k, int32_t* anchor_rows,
-                        float* norms, hipStream_t stream) {
+                        float* norms, void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc;
   if ((rc = check_shape(shape))) return rc;
   if ((rc = check_ptr(k_store, "k_store"))) return rc;
@@ -486,18 +491,22 @@ int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t sto
   if (k < 1) return fail(SRA_E_SHAPE, "k must be >= 1");
   if (k > SRA_MAX_ANCHOR_K) return fail(SRA_E_LIMIT, "k = %d exceeds %d", k, SRA_MAX_ANCHOR_K);
   std::vector<Entry> ents;
+  int64_t total = 0;
   for (int c = 0; c < n_chunks; ++c) {
     const sra_chunk& ch = chunks[c];
     if (ch.src_row < 0 || ch.n_tokens < 0 || (int64_t)ch.src_row + ch.n_tokens > store_rows)
       return fail(SRA_E_CHUNKS, "chunk %d reads outside the store", c);
     if (ch.n_tokens < k) return fail(SRA_E_SHAPE, "chunk %d has %d tokens < k = %d", c, ch.n_tokens, k);
-    if (ch.n_tokens > SRA_MAX_ANCHOR_TOKENS)
-      return fail(SRA_E_LIMIT, "chunk %d has %d tokens > %d", c, ch.n_tokens, SRA_MAX_ANCHOR_TOKENS);
-    ents.push_back({0, ch.src_row, ch.n_tokens, c /* output slot */, 0, 1});
+    // dst: output slot; delta: offset of the chunk's sums of squares in the workspace
+    ents.push_back({0, ch.src_row, ch.n_tokens, c, (int)total, (int)ceil_div(ch.n_tokens, 4)});
+    total += ch.n_tokens;
   }
+  if (total > std::numeric_limits<int32_t>::max()) return fail(SRA_E_LIMIT, "too many chunk tokens");
+  if ((rc = check_ws(ws, ws_bytes, (size_t)total * sizeof(double)))) return rc;
   const int row_elems = shape->n_kv_heads * shape->head_dim;
+  double* ss = static_cast<double*>(ws);
   hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
-    return sra::launch_anchors(shape->dtype, row_elems, tab, k, k_store, anchor_rows, norms, stream);
+    return sra::launch_anchors(shape->dtype, row_elems, tab, k, k_store, ss, anchor_rows, norms, stream);
   });
   if (e != hipSuccess) return hip_fail(e, "anchor launch");
   return ok();
@@ -561,7 +570,8 @@ int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, con
       overlap(v_new, nb, v_fused, fb) || overlap(k_fused, fb, v_fused, fb))
     return fail(SRA_E_ALIAS, "fresh rows and fused cache overlap");
   hipError_t e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_kv_heads, n_req, R, L, k_new,
-                                     v_new, R, 0, row_pos, k_fused, v_fused, nullptr, shape->rope_base, stream);
+                                     v_new, R, 0, row_pos, k_fused, v_fused, nullptr, nullptr, 0,
+                                     shape->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   return ok();
 }
@@ -586,7 +596,8 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
   const Plan p = make_plan(shape, n_req, 1, L, R, 1);
   if ((rc = check_ws(ws, ws_bytes, p.attn_end))) return rc;
   float2* cs = reinterpret_cast<float2*>(wsp(ws, p.cs));
-  hipError_t e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, cs, shape->rope_base, stream);
+  hipError_t e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, cs, nullptr, 0,
+                                        shape->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "rotary table launch");
   if ((rc = do_attn(shape, n_req, q_new, R, 0, row_pos, R, k_fused, v_fused, L, out, lse, cs, ws, p, stream)))
     return rc;
@@ -654,9 +665,10 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
   }
   if ((rc = mark(3)) || (rc = mark(4))) return rc;
   float2* cs = reinterpret_cast<float2*>(wsp(ws, p.cs));
+  // the scatter kernel also writes the rows' rotary table for the attention
   hipError_t e = sra::launch_scatter(s->dtype, s->head_dim, s->n_kv_heads, n_req, R, L, a->k_fresh,
-                                     a->v_fresh, L, 1, a->row_pos, a->k_fused, a->v_fused, cs,
-                                     s->rope_base, stream);
+                                     a->v_fresh, L, 1, a->row_pos, a->k_fused, a->v_fused, cs, nullptr,
+                                     0, s->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   if ((rc = mark(5)) || (rc = mark(6))) return rc;
   if ((rc = do_attn(s, n_req, a->q_fresh, L, 1, a->row_pos, R, a->k_fused, a->v_fused, L, a->out,

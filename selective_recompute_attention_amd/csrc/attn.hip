@@ -14,8 +14,8 @@
 //     feed O^T = V^T P^T directly from registers (keys permuted consistently on both operands).
 //   * 64-key tiles of K (row-major, padded) and V (transposed on the way into LDS) are shared by
 //     the four waves; float32 accumulation, exp2 with log2(e)/sqrt(d) folded into the logits.
-//   * Small problems split the key range (flash-decoding style); a second kernel merges the splits
-//     in split order. Blocks are ordered with the (request, KV head) index fastest, so every block
+//   * Small problems split the key range (flash-decoding style, at most kMaxSplits pieces); a wide
+//     second kernel merges the splits of every query vector in split order. Blocks are ordered with the (request, KV head) index fastest, so every block
 //     of one KV head lands on the same XCD (blocks are dealt round-robin over the 8 XCDs) and its
 //     K/V stay in that XCD's L2; longest tiles are dispatched first.
 // f32 path: plain float32 arithmetic, one block per (row, KV head), exact online softmax.
@@ -33,6 +33,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kMaxSplits = 16;   // key splits per tile (the host's split plan never exceeds it)
 
 struct AttnArgs {
   const uint16_t* q;
@@ -52,7 +53,7 @@ struct AttnArgs {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int NKS = D / 16;   // K-steps of S^T = K Q^T
   constexpr int NDT = D / 32;   // 32-row d tiles of O^T
   constexpr int H = D / 2;
@@ -84,8 +85,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
   const int hq = kvh * g + (qvalid ? v % g : 0);
   const int pq = qvalid ? min(rp[r], a.L - 1) : -1;
 
-  // Q as the B operand of S^T: this lane holds dims 16*ks + 8*hh + s, rotated at position pq.
-  bf16x8 qreg[NKS];
+  // Q as the B operand of S^T: this lane holds dims 16*ks + 8*hh + s, rotated at position pq. The
+  // rotated float32 query is split into hi = bf16(q) and lo = bf16(q - hi): rounding it to a single
+  // bf16 would move the logits by ~1e-3 relative, the dominant error of the output.
+  bf16x8 qhi[NKS], qlo[NKS];
   {
     float qf[NKS][8];
 #pragma unroll
@@ -115,14 +118,24 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
           qf[ks + NKS / 2][s] = x * c.y + y * c.x;
         }
     }
+    // log2(e)/sqrt(d) is folded into the query, so the products come out as exp2 exponents
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 w;
+      u32x4 wh, wl;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w[k] = pack_bf2(qf[ks][2 * k], qf[ks][2 * k + 1]);
-      qreg[ks] = as_bf16x8(w);
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = qf[ks][2 * k] * a.scale_log2, x1 = qf[ks][2 * k + 1] * a.scale_log2;
+        wh[k] = pack_bf2(x0, x1);
+        wl[k] = pack_bf2(x0 - bf2f(wh[k] & 0xffffu), x1 - bf2f(wh[k] >> 16));
+      }
+      qhi[ks] = as_bf16x8(wh);
+      qlo[ks] = as_bf16x8(wl);
     }
   }
+  // smallest position among this wave's query vectors: tiles entirely at or below it need no mask
+  int pmin = qvalid ? pq : INT_MAX;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) pmin = min(pmin, __shfl_xor(pmin, off, 64));
 
   f32x16 o[NDT];
 #pragma unroll
@@ -131,36 +144,52 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
   const int64_t kv_base = ((int64_t)req * a.L * a.Hkv + kvh) * D;
   const int64_t kv_row = (int64_t)a.Hkv * D;
 
+  // Tile loads. K: 16-byte chunks, dims fastest (coalesced rows). V: each task holds 4 keys x 8
+  // dims and writes them transposed; key quads vary fastest across lanes, so the 16 lanes an LDS
+  // write serves together hit 16 distinct bank pairs. The next tile's loads are issued into
+  // registers before the current tile is computed, hiding the global-memory latency.
+  constexpr int NKL = KT * (D / 8) / 256;           // K chunks per thread
+  const bool vtask = threadIdx.x < (KT / 4) * (D / 8);
+  const int vkq = threadIdx.x % (KT / 4), vc = threadIdx.x / (KT / 4);
+  u32x4 kr[NKL], vr[4];
+  auto prefetch = [&](int kt0) {
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      const int j = kt0 + u / (D / 8);
+      kr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (j < kend) kr[i] = *reinterpret_cast<const u32x4*>(a.kf + kv_base + j * kv_row + 8 * (u % (D / 8)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = kt0 + 4 * vkq + i;
+      vr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (vtask && j < kend) vr[i] = *reinterpret_cast<const u32x4*>(a.vf + kv_base + j * kv_row + 8 * vc);
+    }
+  };
+  prefetch(kbeg);
+
   for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
     __syncthreads();
-    for (int u = threadIdx.x; u < KT * (D / 8); u += 256) {
-      const int key = u / (D / 8), c = u % (D / 8);
-      const int j = kt0 + key;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (j < kend) w = *reinterpret_cast<const u32x4*>(a.kf + kv_base + j * kv_row + 8 * c);
-      *reinterpret_cast<u32x4*>(Ks + key * KST + 8 * c) = w;
-    }
-    for (int u = threadIdx.x; u < (KT / 4) * (D / 8); u += 256) {
-      const int kq = u / (D / 8), c = u % (D / 8);
-      u32x4 w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = kt0 + 4 * kq + i;
-        w[i] = u32x4{0u, 0u, 0u, 0u};
-        if (j < kend) w[i] = *reinterpret_cast<const u32x4*>(a.vf + kv_base + j * kv_row + 8 * c);
-      }
+    for (int i = 0; i < NKL; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) = kr[i];
+    }
+    if (vtask) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {  // word p: dims 8c+2p (low half) and 8c+2p+1 (high half)
         u32x2 lo, hi;
-        lo[0] = (w[0][p] & 0xffffu) | (w[1][p] << 16);
-        lo[1] = (w[2][p] & 0xffffu) | (w[3][p] << 16);
-        hi[0] = (w[0][p] >> 16) | (w[1][p] & 0xffff0000u);
-        hi[1] = (w[2][p] >> 16) | (w[3][p] & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(Vt + (8 * c + 2 * p) * VST + 4 * kq) = lo;
-        *reinterpret_cast<u32x2*>(Vt + (8 * c + 2 * p + 1) * VST + 4 * kq) = hi;
+        lo[0] = (vr[0][p] & 0xffffu) | (vr[1][p] << 16);
+        lo[1] = (vr[2][p] & 0xffffu) | (vr[3][p] << 16);
+        hi[0] = (vr[0][p] >> 16) | (vr[1][p] & 0xffff0000u);
+        hi[1] = (vr[2][p] >> 16) | (vr[3][p] & 0xffff0000u);
+        *reinterpret_cast<u32x2*>(Vt + (8 * vc + 2 * p) * VST + 4 * vkq) = lo;
+        *reinterpret_cast<u32x2*>(Vt + (8 * vc + 2 * p + 1) * VST + 4 * vkq) = hi;
       }
     }
     __syncthreads();
+    if (kt0 + KT < kend) prefetch(kt0 + KT);
 
     // S^T[key][q] for two 32-key sub-tiles
     f32x16 s[2];
@@ -171,37 +200,48 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 ka =
             as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (32 * st + l32) * KST + 16 * ks + 8 * hh));
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], s[st], 0, 0, 0);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qhi[ks], s[st], 0, 0, 0);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qlo[ks], s[st], 0, 0, 0);
       }
     }
-    // causal mask by absolute position, online softmax (log2 domain)
+    // causal mask by absolute position (only on tiles that reach past the wave's smallest
+    // position or the split's end), online softmax in the log2 domain
     float mt = -INFINITY;
+    if (kt0 + KT <= kend && kt0 + KT - 1 <= pmin) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int key = kt0 + 32 * st + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-        const float y = (key < kend && key <= pq) ? s[st][rr] * a.scale_log2 : -INFINITY;
-        s[st][rr] = y;
-        mt = fmaxf(mt, y);
-      }
+        for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, s[st][rr]);
+    } else {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = kt0 + 32 * st + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          if (!(key < kend && key <= pq)) s[st][rr] = -INFINITY;
+          mt = fmaxf(mt, s[st][rr]);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all masked so far: every p is 0
+    const float alpha = exp2f(m_run - m_use);
     float lsum = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float y = s[st][rr];
-        const float p = (y == -INFINITY) ? 0.f : exp2f(y - m_new);
+        const float p = exp2f(s[st][rr] - m_use);
         s[st][rr] = p;
         lsum += p;
       }
     l_run = l_run * alpha + lsum;
-    m_run = m_new;
+    // rescale the accumulator only when some lane's running max grew (alpha is 1 elsewhere)
+    if (__any(m_new > m_run)) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    m_run = m_new;
 
     // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4
 #pragma unroll
@@ -257,41 +297,51 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
   }
 }
 
-// Merge the key splits of one (group, tile) in split order.
+// Merge the key splits in split order. One thread per (query vector, 4 dims): every load of a
+// thread is independent of the others (fixed-size unrolled split loop), so the kernel runs at
+// memory speed instead of a chain of load latencies.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  const int group = blockIdx.x % a.n_groups;
-  const int tile = blockIdx.x / a.n_groups;
+  constexpr int TPV = D / 4;                 // threads per query vector
+  constexpr int VPB = 256 / TPV;             // query vectors per block
+  const int slab = blockIdx.x % (128 / VPB);
+  const int gt = blockIdx.x / (128 / VPB);   // group-major (group, tile) index
+  const int group = gt % a.n_groups, tile = gt / a.n_groups;
   const int req = group / a.Hkv, kvh = group % a.Hkv;
   const int g = a.g, Mv = a.R * g, v0 = tile * 128;
+  const int ql = slab * VPB + threadIdx.x / TPV, dc = threadIdx.x % TPV;
+  const int v = v0 + ql;
+  if (v >= Mv) return;
   const int* rp = a.row_pos + (int64_t)req * a.R;
   const int maxkey = min(rp[min(v0 + 127, Mv - 1) / g], a.L - 1);
+  if (maxkey < 0) return;
   const int nvalid = min(a.n_splits, maxkey / a.key_split + 1);
-  const int64_t base = (int64_t)(group * a.n_tiles + tile) * a.n_splits * 128;
-  for (int idx = threadIdx.x; idx < 128 * (D / 4); idx += blockDim.x) {
-    const int ql = idx / (D / 4), dc = idx % (D / 4);
-    const int v = v0 + ql;
-    if (v >= Mv) continue;
-    const int r = v / g, hq = kvh * g + v % g;
-    float M = -INFINITY;
-    for (int s = 0; s < nvalid; ++s) M = fmaxf(M, a.part_ml[base + s * 128 + ql].x);
-    float Ls = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nvalid; ++s) {
-      const float2 ml = a.part_ml[base + s * 128 + ql];
-      if (ml.x == -INFINITY) continue;
-      const float w = exp2f(ml.x - M);
-      Ls += ml.y * w;
-      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + (base + s * 128 + ql) * D + 4 * dc);
+  const int64_t base = (int64_t)(group * a.n_tiles + tile) * a.n_splits * 128 + ql;
+  float2 ml[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    ml[s] = s < nvalid ? a.part_ml[base + s * 128] : make_float2(-INFINITY, 0.f);
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ml[s].x);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float Ls = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < nvalid && ml[s].x != -INFINITY) {
+      const float w = exp2f(ml[s].x - M);
+      Ls += ml[s].y * w;
+      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + (base + s * 128) * D + 4 * dc);
     }
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-    u32x2 w;
-    w[0] = pack_bf2(acc[0] * inv, acc[1] * inv);
-    w[1] = pack_bf2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 4 * dc) = w;
-    if (dc == 0 && a.lse)
-      a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
   }
+  const int r = v / g, hq = kvh * g + v % g;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  u32x2 w;
+  w[0] = pack_bf2(acc[0] * inv, acc[1] * inv);
+  w[1] = pack_bf2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 4 * dc) = w;
+  if (dc == 0 && a.lse)
+    a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------- float32 path
@@ -417,7 +467,7 @@ hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, con
     else k_attn_mfma<64, true><<<dim3(nblk), dim3(256), 0, st>>>(a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const unsigned ncomb = (unsigned)(a.n_groups * a.n_tiles);
+    const unsigned ncomb = (unsigned)(a.n_groups * a.n_tiles * (D == 128 ? 16 : 8));
     if (D == 128) k_attn_combine<128><<<dim3(ncomb), dim3(256), 0, st>>>(a);
     else k_attn_combine<64><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   }

@@ -40,15 +40,17 @@ __device__ __forceinline__ int find_entry(const ChunkTab& t, int blk) {
   return e;
 }
 
-// bfloat16 <-> float32 (round to nearest, ties to even; NaN stays NaN).
+// bfloat16 <-> float32. The narrowing conversion is the hardware's round-to-nearest-even
+// (v_cvt_pk_bf16_f32 on gfx950: two values per instruction).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // theta_i = base^(-2i/d) and the rotation angle pos * theta_i, both in float64.
 __device__ __forceinline__ double rope_theta(int i, int d, double base) {
@@ -68,21 +70,25 @@ namespace sra {
 hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
                            const void* ks, const void* vs, void* kf, void* vf, int64_t L,
                            double base, hipStream_t st);
+// launch_scatter / launch_rope_table also zero `n_zero` ints at `zero` (the attention's arrival
+// counters) when zero is non-NULL.
 hipError_t launch_scatter(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
                           const void* vn, int fresh_rows, int indexed, const int* row_pos,
-                          void* kf, void* vf, float2* cs_out, double base, hipStream_t st);
+                          void* kf, void* vf, float2* cs_out, int* zero, int n_zero, double base,
+                          hipStream_t st);
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
-                             double base, hipStream_t st);
+                             int* zero, int n_zero, double base, hipStream_t st);
 hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
-                          int32_t* anchors, float* norms, hipStream_t st);
+                          double* ss, int32_t* anchors, float* norms, hipStream_t st);
 hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv, int Mpad,
                              int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
-                             int entry_base, double base, hipStream_t st);
-hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, int Hkv, int Mpad, int Mvalid,
-                             int Lctx, const void* kc, const uint16_t* qrot, int64_t plane,
-                             int entry_base, int blk_base, float2* ml_part, const float2* ml_final,
-                             float* colsum, float scale_log2, hipStream_t st);
-hipError_t launch_score_merge(int n_req, int Hkv, int Mpad, int Mvalid, const int* req_blk0,
+                             int entry_base, float scale_log2, double base, hipStream_t st);
+hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
+                             int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
+                             const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
+                             float2* ml_part, const float2* ml_final, int fuse_merge,
+                             float* colsum, hipStream_t st);
+hipError_t launch_score_merge(const int* req_blk0, int n_req, int Hkv, int Mpad, int Mvalid,
                               const float2* ml_part, float2* ml_final, hipStream_t st);
 hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,
                             int Lctx, const float* qc, const float* kc, float* prob,

@@ -120,10 +120,13 @@ __global__ __launch_bounds__(128) void k_scatter(int Hkv, int R, int L, const T*
                                                  const T* __restrict__ vn, int fresh_rows,
                                                  int indexed, const int* __restrict__ row_pos,
                                                  T* __restrict__ kf, T* __restrict__ vf,
-                                                 float2* __restrict__ cs_out, double base) {
+                                                 float2* __restrict__ cs_out, int* __restrict__ zero,
+                                                 int n_zero, double base) {
   constexpr int H = D / 2;
   __shared__ float2 cs[H];
   const int r = blockIdx.x, q = blockIdx.y;
+  if (zero && r == 0 && q == 0)
+    for (int u = threadIdx.x; u < n_zero; u += blockDim.x) zero[u] = 0;
   const int p = row_pos[(int64_t)q * R + r];
   if (p < 0 || p >= L) return;  // rows outside the cache are never written
   const int srow = indexed ? p : r;
@@ -142,9 +145,11 @@ __global__ __launch_bounds__(128) void k_scatter(int Hkv, int R, int L, const T*
 
 template <int D>
 __global__ void k_rope_table(int R, const int* __restrict__ row_pos, float2* __restrict__ cs_out,
-                             double base) {
+                             int* __restrict__ zero, int n_zero, double base) {
   constexpr int H = D / 2;
   const int r = blockIdx.x, q = blockIdx.y;
+  if (zero && r == 0 && q == 0)
+    for (int u = threadIdx.x; u < n_zero; u += blockDim.x) zero[u] = 0;
   const int p = row_pos[(int64_t)q * R + r];
   for (int i = threadIdx.x; i < H; i += blockDim.x)
     cs_out[((int64_t)q * R + r) * H + i] = rope_cs((double)p, i, D, base);
@@ -186,36 +191,37 @@ hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int r
 
 hipError_t launch_scatter(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
                           const void* vn, int fresh_rows, int indexed, const int* row_pos,
-                          void* kf, void* vf, float2* cs_out, double base, hipStream_t st) {
+                          void* kf, void* vf, float2* cs_out, int* zero, int n_zero, double base,
+                          hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(128);
   if (dtype == 0 && D == 128)
     k_scatter<uint16_t, 128><<<g, b, 0, st>>>(Hkv, R, L, (const uint16_t*)kn, (const uint16_t*)vn,
                                                fresh_rows, indexed, row_pos, (uint16_t*)kf,
-                                               (uint16_t*)vf, cs_out, base);
+                                               (uint16_t*)vf, cs_out, zero, n_zero, base);
   else if (dtype == 0 && D == 64)
     k_scatter<uint16_t, 64><<<g, b, 0, st>>>(Hkv, R, L, (const uint16_t*)kn, (const uint16_t*)vn,
                                               fresh_rows, indexed, row_pos, (uint16_t*)kf,
-                                              (uint16_t*)vf, cs_out, base);
+                                              (uint16_t*)vf, cs_out, zero, n_zero, base);
   else if (dtype == 1 && D == 128)
     k_scatter<float, 128><<<g, b, 0, st>>>(Hkv, R, L, (const float*)kn, (const float*)vn,
                                             fresh_rows, indexed, row_pos, (float*)kf, (float*)vf,
-                                            cs_out, base);
+                                            cs_out, zero, n_zero, base);
   else
     k_scatter<float, 64><<<g, b, 0, st>>>(Hkv, R, L, (const float*)kn, (const float*)vn,
                                            fresh_rows, indexed, row_pos, (float*)kf, (float*)vf,
-                                           cs_out, base);
+                                           cs_out, zero, n_zero, base);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
-                             double base, hipStream_t st) {
+                             int* zero, int n_zero, double base, hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(64);
   if (D == 128)
-    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
+    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, zero, n_zero, base);
   else
-    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
+    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, zero, n_zero, base);
   return hipGetLastError();
 }
 

@@ -11,11 +11,14 @@
 // and both halves are multiplied against the same keys (two MFMAs), which keeps the logits within a
 // few 1e-6 of the exact value -- tight enough that the top-N choice matches an exact computation.
 //   prep   : q'' hi/lo per (request, chunk, KV head), laid out as 32x32x16 MFMA operands.
-//   pass 1 : per 128-key block, per query vector, the block's (max, sum of exp) of the logits.
-//   merge  : per query vector, the (max, 1/sum) over all key blocks, in block order.
-//   pass 2 : per key, the sum over its KV head's query vectors of exp(logit - max) / sum, written
-//            per KV head; the selection kernel adds the KV heads in order. No float atomics.
-// f32 path (exact float32 storage): plain dot products, one block per query vector.
+//   pass 1 : per 128-key block, per query vector, the block's (max, sum of exp2) of the logits.
+//   merge  : per query vector, (max, 1/sum) over all blocks of its request in block order -- inside
+//            pass 2 when a request's partials are small, else as its own wide kernel.
+//   pass 2 : per key, the sum over its KV head's query vectors of exp2(logit - max) / sum, written
+//            per KV head; the selection kernel adds the KV heads in order.
+// Every reduction has a fixed order and there are no float atomics: runs are bit-reproducible.
+// Cross-block results only meet at kernel boundaries (no device-scope fences, which on this GPU
+// write back the L2).
 #include <float.h>
 
 #include "common.h"
@@ -29,12 +32,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// grid (Lq, entries): one block per (query row i, chunk entry).
+// grid (Lq, entries): one block per (query row i, chunk entry); a thread rotates 8 pairs of one
+// head with 16-byte loads and stores.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq, int Hkv, int Mpad,
                                                     int Lctx, const uint16_t* __restrict__ qc,
                                                     uint16_t* __restrict__ qrot, int64_t plane,
-                                                    int entry_base, double base) {
+                                                    int entry_base, float scale_log2, double base) {
   constexpr int H = D / 2;
   __shared__ float2 cs[H];
   const int i = blockIdx.x, e = blockIdx.y;
@@ -45,19 +49,36 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
   const int g = Hq / Hkv;
   const int eg = entry_base + e;
   const uint16_t* q = qc + ((int64_t)req * Lq + i) * Hq * D;
-  for (int u = threadIdx.x; u < Hq * H; u += blockDim.x) {
-    const int h = u / H, j = u % H;
-    const float a = bf2f(q[h * D + j]), b = bf2f(q[h * D + j + H]);
-    const float c = cs[j].x, s = cs[j].y;
-    const float r0 = a * c - b * s, r1 = a * s + b * c;
-    const uint32_t h0 = f2bf(r0), h1 = f2bf(r1);
-    const uint32_t l0 = f2bf(r0 - bf2f(h0)), l1 = f2bf(r1 - bf2f(h1));
+  for (int u = threadIdx.x; u < Hq * (H / 8); u += blockDim.x) {
+    const int h = u / (H / 8), j0 = (u % (H / 8)) * 8;
+    const u32x4 wa = *reinterpret_cast<const u32x4*>(q + h * D + j0);
+    const u32x4 wb = *reinterpret_cast<const u32x4*>(q + h * D + j0 + H);
+    u32x4 hi0, hi1, lo0, lo1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t ha[2], hb[2], la[2], lb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float a = bf2f((wa[k] >> (16 * t)) & 0xffffu), b = bf2f((wb[k] >> (16 * t)) & 0xffffu);
+        const float2 c = cs[j0 + 2 * k + t];
+        // log2(e)/sqrt(d) is folded in: the products come out as exp2 exponents
+        const float r0 = (a * c.x - b * c.y) * scale_log2, r1 = (a * c.y + b * c.x) * scale_log2;
+        ha[t] = f2bf(r0);
+        hb[t] = f2bf(r1);
+        la[t] = f2bf(r0 - bf2f(ha[t]));
+        lb[t] = f2bf(r1 - bf2f(hb[t]));
+      }
+      hi0[k] = ha[0] | (ha[1] << 16);
+      hi1[k] = hb[0] | (hb[1] << 16);
+      lo0[k] = la[0] | (la[1] << 16);
+      lo1[k] = lb[0] | (lb[1] << 16);
+    }
     const int kvh = h / g, v = i * g + (h % g);
-    const int64_t o = ((int64_t)(eg * Hkv + kvh) * Mpad + v) * D;
-    qrot[o + j] = (uint16_t)h0;
-    qrot[o + j + H] = (uint16_t)h1;
-    qrot[plane + o + j] = (uint16_t)l0;
-    qrot[plane + o + j + H] = (uint16_t)l1;
+    const int64_t o = ((int64_t)(eg * Hkv + kvh) * Mpad + v) * D + j0;
+    *reinterpret_cast<u32x4*>(qrot + o) = hi0;
+    *reinterpret_cast<u32x4*>(qrot + o + H) = hi1;
+    *reinterpret_cast<u32x4*>(qrot + plane + o) = lo0;
+    *reinterpret_cast<u32x4*>(qrot + plane + o + H) = lo1;
   }
   if (i == 0) {  // zero the padding query vectors [Lq*g, Mpad) of every KV head
     const int pad = Mpad - Lq * g;
@@ -70,17 +91,86 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
   }
 }
 
-// grid (key blocks, Hkv); 4 waves, each owning 32 keys of a 128-key block of one chunk.
+// Online merge of one (max, sum of exp2(y - max)) pair into a running pair.
+__device__ __forceinline__ void ml_merge(float& M, float& S, float2 p) {
+  if (p.x == -INFINITY) return;
+  const float nm = fmaxf(M, p.x);
+  S = S * exp2f(M - nm) + p.y * exp2f(p.x - nm);
+  M = nm;
+}
+
+// (max, 1/sum) over blocks [b0, b1) of query vectors [v_lo, v_lo + v_cnt) of one (request, KV head),
+// written to out[v]. T = 256 / v_cnt threads share a vector; thread j covers blocks b0+j, b0+j+T,
+// ... in order (loads issued 8 at a time), then thread 0 of the vector merges j = 0..T-1 in order.
+__device__ void merge_rows(int b0, int b1, int Hkv, int kvh, int Mpad, int v_lo, int v_cnt,
+                           int Mvalid, const float2* __restrict__ ml_part, float2* out) {
+  __shared__ float2 part[256];
+  const int T = v_cnt >= 256 ? 1 : 256 / v_cnt;
+  const int j = threadIdx.x % T;
+  for (int vb = 0; vb < v_cnt; vb += 256 / T) {
+    const int vl = vb + threadIdx.x / T;
+    const int v = v_lo + vl;
+    float M = -INFINITY, S = 0.f;
+    if (vl < v_cnt && v < Mvalid) {
+      for (int b = b0 + j; b < b1; b += 8 * T) {
+        float2 p[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int bb = b + u * T;
+          p[u] = bb < b1 ? ml_part[((int64_t)bb * Hkv + kvh) * Mpad + v] : make_float2(-INFINITY, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ml_merge(M, S, p[u]);
+      }
+    }
+    part[threadIdx.x] = make_float2(M, S);
+    __syncthreads();
+    if (j == 0 && vl < v_cnt) {
+      float MM = -INFINITY, SS = 0.f;
+      for (int i = 0; i < T; ++i) ml_merge(MM, SS, part[threadIdx.x + i]);
+      out[v] = (v < Mvalid && SS > 0.f) ? make_float2(MM, 1.f / SS) : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+  }
+}
+
+// Global block index ranges of each request: blocks [blk0[q], blk0[q+1]).
+struct ReqBlocks {
+  int blk0[kMaxEntries + 1];
+};
+
+// grid (n_req * Hkv, ceil(Mpad / 64)): the separate merge for large partial sets.
+__global__ __launch_bounds__(256) void k_score_merge(ReqBlocks rb, int Hkv, int Mpad, int Mvalid,
+                                                     const float2* __restrict__ ml_part,
+                                                     float2* __restrict__ ml_final) {
+  const int req = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+  const int v_lo = blockIdx.y * 64;
+  merge_rows(rb.blk0[req], rb.blk0[req + 1], Hkv, kvh, Mpad, v_lo, min(64, Mpad - v_lo), Mvalid,
+             ml_part, ml_final + ((int64_t)req * Hkv + kvh) * Mpad);
+}
+
+template <int NKS>
+__device__ __forceinline__ void load_q(const uint16_t* qp, int64_t plane, bf16x8* h, bf16x8* l) {
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    h[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
+    l[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + plane + 16 * ks));
+  }
+}
+
+// grid (key blocks, Hkv); 4 waves, each owning 32 keys of a 128-key block of one chunk. The next
+// query tile's operands are loaded while the current tile is multiplied.
 // PASS 1 writes ml_part[blk][kvh][v] = (max, sum exp2(y - max)) over the block's keys;
 // PASS 2 writes colsum[req][kvh][j] = sum_v exp2(y - M_v) * invS_v.
 template <int D, int PASS>
-__global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, int Hkv, int Mpad, int Mvalid,
-                                                    int Lctx, const uint16_t* __restrict__ kc,
+__global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, int Hkv, int Mpad,
+                                                    int Mvalid, int Lctx,
+                                                    const uint16_t* __restrict__ kc,
                                                     const uint16_t* __restrict__ qrot,
                                                     int64_t plane, int entry_base, int blk_base,
                                                     float2* __restrict__ ml_part,
                                                     const float2* __restrict__ ml_final,
-                                                    float* __restrict__ colsum, float scale_log2) {
+                                                    int fuse_merge, float* __restrict__ colsum) {
   constexpr int NKS = D / 16;
   extern __shared__ float2 smem[];
   const int blk = blockIdx.x, kvh = blockIdx.y;
@@ -101,201 +191,109 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, int Hkv, int M
 
   const uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;
   const int nqt = Mpad / 32;
+  bf16x8 qh[NKS], ql[NKS], nh[NKS], nl[NKS];
+  load_q<NKS>(qb + (int64_t)l32 * D, plane, qh, ql);
 
   if constexpr (PASS == 1) {
     float2* wpart = smem;  // [4][Mpad]
     for (int qt = 0; qt < nqt; ++qt) {
-      const uint16_t* qp = qb + (int64_t)(32 * qt + l32) * D;
+      if (qt + 1 < nqt) load_q<NKS>(qb + (int64_t)(32 * (qt + 1) + l32) * D, plane, nh, nl);
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 qh = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
-        const bf16x8 ql = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + plane + 16 * ks));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[ks], qh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[ks], ql, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[ks], qh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[ks], ql[ks], acc, 0, 0, 0);
       }
-      // acc[r] = logit of key t_base + 8*(r/4) + 4*hh + r%4 for query vector 32*qt + l32
+      // acc[r] = exp2 exponent of key t_base + 8*(r/4) + 4*hh + r%4 for query vector 32*qt + l32
+      if (t_base + 32 > len) {   // partial block: drop the keys past the chunk's end
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t_base + 8 * (r >> 2) + 4 * hh + (r & 3) >= len) acc[r] = -INFINITY;
+      }
       float m = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t_base + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (key < len) m = fmaxf(m, acc[r] * scale_log2);
-      }
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[r]);
       m = fmaxf(m, __shfl_xor(m, 32, 64));
+      const float m_use = (m == -INFINITY) ? 0.f : m;
       float s = 0.f;
-      if (m != -INFINITY) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t_base + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key < len) s += exp2f(acc[r] * scale_log2 - m);
-        }
-      }
+      for (int r = 0; r < 16; ++r) s += exp2f(acc[r] - m_use);
       s += __shfl_xor(s, 32, 64);
       if (hh == 0) wpart[wave * Mpad + 32 * qt + l32] = make_float2(m, s);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) { qh[ks] = nh[ks]; ql[ks] = nl[ks]; }
     }
     __syncthreads();
     float2* dst = ml_part + ((int64_t)(blk_base + blk) * Hkv + kvh) * Mpad;
     for (int v = threadIdx.x; v < Mpad; v += blockDim.x) {
-      float M = -INFINITY;
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, wpart[w * Mpad + v].x);
-      float S = 0.f;
-      if (M != -INFINITY)
-        for (int w = 0; w < 4; ++w) {
-          const float2 p = wpart[w * Mpad + v];
-          if (p.x != -INFINITY) S += p.y * exp2f(p.x - M);
-        }
+      float M = -INFINITY, S = 0.f;
+      for (int w = 0; w < 4; ++w) ml_merge(M, S, wpart[w * Mpad + v]);
       dst[v] = make_float2(M, S);
     }
   } else {
     float2* mlf = smem;  // [Mpad]
-    const float2* src = ml_final + ((int64_t)req * Hkv + kvh) * Mpad;
-    for (int v = threadIdx.x; v < Mpad; v += blockDim.x) mlf[v] = src[v];
-    __syncthreads();
+    if (fuse_merge) {
+      merge_rows(rb.blk0[req], rb.blk0[req + 1], Hkv, kvh, Mpad, 0, Mpad, Mvalid, ml_part, mlf);
+    } else {
+      const float2* src = ml_final + ((int64_t)req * Hkv + kvh) * Mpad;
+      for (int v = threadIdx.x; v < Mpad; v += blockDim.x) mlf[v] = src[v];
+      __syncthreads();
+    }
     float col = 0.f;
     for (int qt = 0; qt < nqt; ++qt) {
-      const uint16_t* qp = qb + (int64_t)(32 * qt + l32) * D;
+      if (qt + 1 < nqt) load_q<NKS>(qb + (int64_t)(32 * (qt + 1) + l32) * D, plane, nh, nl);
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 qh = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
-        const bf16x8 ql = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + plane + 16 * ks));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh, kreg[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql, kreg[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[ks], kreg[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[ks], kreg[ks], acc, 0, 0, 0);
       }
       // acc[r] = logit of query vector 32*qt + 8*(r/4) + 4*hh + r%4 against key t_base + l32
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float2 ml = mlf[32 * qt + 8 * (r >> 2) + 4 * hh + (r & 3)];
-        col += exp2f(acc[r] * scale_log2 - ml.x) * ml.y;
+        col += exp2f(acc[r] - ml.x) * ml.y;
       }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) { qh[ks] = nh[ks]; ql[ks] = nl[ks]; }
     }
     col += __shfl_xor(col, 32, 64);
     if (hh == 0 && kvalid) colsum[((int64_t)req * Hkv + kvh) * Lctx + tab.dst[e] + tk] = col;
   }
 }
 
-struct ReqBlocks {
-  int blk0[kMaxEntries + 1];
-};
-
-__global__ void k_score_merge(int n_req, int Hkv, int Mpad, int Mvalid, ReqBlocks rb,
-                              const float2* __restrict__ ml_part, float2* __restrict__ ml_final) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)n_req * Hkv * Mpad) return;
-  const int v = (int)(idx % Mpad);
-  const int kvh = (int)((idx / Mpad) % Hkv);
-  const int req = (int)(idx / ((int64_t)Mpad * Hkv));
-  if (v >= Mvalid) {
-    ml_final[idx] = make_float2(0.f, 0.f);
-    return;
-  }
-  float M = -INFINITY;
-  for (int b = rb.blk0[req]; b < rb.blk0[req + 1]; ++b)
-    M = fmaxf(M, ml_part[((int64_t)b * Hkv + kvh) * Mpad + v].x);
-  float S = 0.f;
-  for (int b = rb.blk0[req]; b < rb.blk0[req + 1]; ++b) {
-    const float2 p = ml_part[((int64_t)b * Hkv + kvh) * Mpad + v];
-    if (p.x != -INFINITY) S += p.y * exp2f(p.x - M);
-  }
-  ml_final[idx] = make_float2(M, S > 0.f ? 1.f / S : 0.f);
-}
-
-// ---------------------------------------------------------------------------- float32 path
-// grid (Hq*Lq, n_req): one block per query vector (i, h) of one request; writes its softmax row
-// prob[req][i*Hq + h][0..Lctx).
-template <int D>
-__global__ __launch_bounds__(256) void k_score_f32(ChunkTab tab, int Lq, int Hq, int Hkv, int Lctx,
-                                                   const float* __restrict__ qc,
-                                                   const float* __restrict__ kc,
-                                                   float* __restrict__ prob, float scale_log2,
-                                                   double base) {
-  constexpr int H = D / 2;
-  __shared__ float qr[D];
-  __shared__ float red[256];
-  const int qv = blockIdx.x, req = blockIdx.y;
-  const int i = qv / Hq, h = qv % Hq, kvh = h / (Hq / Hkv);
-  const float* q = qc + (((int64_t)req * Lq + i) * Hq + h) * D;
-  float* row = prob + ((int64_t)req * Lq * Hq + qv) * Lctx;
-  for (int e = 0; e < tab.n; ++e) {
-    if (tab.req[e] != req) continue;
-    const double pos = (double)Lctx + (double)i - (double)tab.delta[e];
-    if (threadIdx.x < H) {
-      const float2 c = rope_cs(pos, threadIdx.x, D, base);
-      const float a = q[threadIdx.x], b = q[threadIdx.x + H];
-      qr[threadIdx.x] = a * c.x - b * c.y;
-      qr[threadIdx.x + H] = a * c.y + b * c.x;
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < tab.len[e]; t += blockDim.x) {
-      const float* k = kc + (((int64_t)tab.src[e] + t) * Hkv + kvh) * D;
-      float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot += qr[d] * k[d];
-      row[tab.dst[e] + t] = dot * scale_log2;
-    }
-    __syncthreads();
-  }
-  float m = -INFINITY;
-  for (int j = threadIdx.x; j < Lctx; j += blockDim.x) m = fmaxf(m, row[j]);
-  red[threadIdx.x] = m;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float sum = 0.f;
-  for (int j = threadIdx.x; j < Lctx; j += blockDim.x) sum += exp2f(row[j] - M);
-  red[threadIdx.x] = sum;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const float inv = 1.f / red[0];
-  for (int j = threadIdx.x; j < Lctx; j += blockDim.x) row[j] = exp2f(row[j] - M) * inv;
-}
-
-__global__ void k_colsum_f32(int n_req, int rows, int Lctx, const float* __restrict__ prob,
-                             float* __restrict__ parts) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)n_req * Lctx) return;
-  const int j = (int)(idx % Lctx), req = (int)(idx / Lctx);
-  const float* p = prob + (int64_t)req * rows * Lctx + j;
-  float s = 0.f;
-  for (int v = 0; v < rows; ++v) s += p[(int64_t)v * Lctx];
-  parts[idx] = s;
-}
-
 }  // namespace
 
 hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv, int Mpad,
                              int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
-                             int entry_base, double base, hipStream_t st) {
+                             int entry_base, float scale_log2, double base, hipStream_t st) {
   if (tab.n == 0 || Lq == 0) return hipSuccess;
   dim3 g(Lq, tab.n), b(256);
   if (D == 128)
     k_score_prep<128><<<g, b, 0, st>>>(tab, Lq, Hq, Hkv, Mpad, Lctx, (const uint16_t*)qc, qrot,
-                                        plane, entry_base, base);
+                                        plane, entry_base, scale_log2, base);
   else
     k_score_prep<64><<<g, b, 0, st>>>(tab, Lq, Hq, Hkv, Mpad, Lctx, (const uint16_t*)qc, qrot,
-                                       plane, entry_base, base);
+                                       plane, entry_base, scale_log2, base);
   return hipGetLastError();
 }
 
-hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, int Hkv, int Mpad, int Mvalid,
-                             int Lctx, const void* kc, const uint16_t* qrot, int64_t plane,
-                             int entry_base, int blk_base, float2* ml_part, const float2* ml_final,
-                             float* colsum, float scale_log2, hipStream_t st) {
+hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
+                             int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
+                             const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
+                             float2* ml_part, const float2* ml_final, int fuse_merge,
+                             float* colsum, hipStream_t st) {
   const int nblk = tab.blk0[tab.n];
   if (nblk == 0) return hipSuccess;
+  ReqBlocks rb;
+  for (int r = 0; r <= n_req; ++r) rb.blk0[r] = req_blk0[r];
   dim3 g(nblk, Hkv), b(256);
   const size_t lds = (pass == 1 ? 4 : 1) * (size_t)Mpad * sizeof(float2);
   const uint16_t* k = (const uint16_t*)kc;
 #define SRA_PASS(DD, PP)                                                                        \
-  k_score_pass<DD, PP><<<g, b, lds, st>>>(tab, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,         \
-                                          entry_base, blk_base, ml_part, ml_final, colsum,      \
-                                          scale_log2)
+  k_score_pass<DD, PP><<<g, b, lds, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
+                                          entry_base, blk_base, ml_part, ml_final, fuse_merge,  \
+                                          colsum)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);
   else if (D == 128) SRA_PASS(128, 2);
   else if (pass == 1) SRA_PASS(64, 1);
@@ -304,33 +302,12 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, int Hkv, int 
   return hipGetLastError();
 }
 
-hipError_t launch_score_merge(int n_req, int Hkv, int Mpad, int Mvalid, const int* req_blk0,
+hipError_t launch_score_merge(const int* req_blk0, int n_req, int Hkv, int Mpad, int Mvalid,
                               const float2* ml_part, float2* ml_final, hipStream_t st) {
   ReqBlocks rb;
   for (int r = 0; r <= n_req; ++r) rb.blk0[r] = req_blk0[r];
-  const int64_t n = (int64_t)n_req * Hkv * Mpad;
-  k_score_merge<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(n_req, Hkv, Mpad, Mvalid,
-                                                                         rb, ml_part, ml_final);
-  return hipGetLastError();
-}
-
-hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,
-                            int Lctx, const float* qc, const float* kc, float* prob,
-                            float scale_log2, double base, hipStream_t st) {
-  dim3 g(Hq * Lq, n_req), b(256);
-  if (D == 128)
-    k_score_f32<128><<<g, b, 0, st>>>(tab_req, Lq, Hq, Hkv, Lctx, qc, kc, prob, scale_log2, base);
-  else
-    k_score_f32<64><<<g, b, 0, st>>>(tab_req, Lq, Hq, Hkv, Lctx, qc, kc, prob, scale_log2, base);
-  return hipGetLastError();
-}
-
-hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, float* parts,
-                             hipStream_t st) {
-  const int64_t n = (int64_t)n_req * Lctx;
-  if (n == 0) return hipSuccess;
-  k_colsum_f32<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(n_req, rows, Lctx, prob,
-                                                                       parts);
+  dim3 g(n_req * Hkv, (Mpad + 63) / 64), b(256);
+  k_score_merge<<<g, b, 0, st>>>(rb, Hkv, Mpad, Mvalid, ml_part, ml_final);
   return hipGetLastError();
 }
 

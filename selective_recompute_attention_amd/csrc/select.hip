@@ -13,6 +13,8 @@
 namespace sra {
 namespace {
 
+constexpr int kSelLdsKeys = 12288;   // keys of one selection unit kept in LDS (48 KB)
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -44,21 +46,37 @@ __global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lct
   __shared__ unsigned hist[256];
   __shared__ unsigned sh_prefix, sh_remaining;
   __shared__ int wsum[16];
+  __shared__ uint32_t kl[kSelLdsKeys];   // the unit's keys when they fit
   const int e = blockIdx.x;
   const int req = tab.req[e], begin = tab.begin[e], len = tab.len[e];
   const int quota = tab.quota[e], off = tab.out_off[e];
   float* srow = scores + (int64_t)req * Lctx + begin;
   int* out = row_pos + (int64_t)req * R;
+  const bool in_lds = len <= kSelLdsKeys;
 
-  if (nparts > 0) {
-    const float* prow = parts + (int64_t)req * nparts * Lctx + begin;
-    for (int j = threadIdx.x; j < len; j += blockDim.x) {
-      float s = 0.f;
-      for (int p = 0; p < nparts; ++p) s += prow[(int64_t)p * Lctx + j];
+  // scores: per-KV-head partial column sums added in head order (loads issued 8 at a time)
+  const float* prow = parts + (int64_t)req * nparts * Lctx + begin;
+  for (int j = threadIdx.x; j < len; j += blockDim.x) {
+    float s = 0.f;
+    if (nparts > 0) {
+      int p = 0;
+      for (; p + 8 <= nparts; p += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = prow[(int64_t)(p + u) * Lctx + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      for (; p < nparts; ++p) s += prow[(int64_t)p * Lctx + j];
       srow[j] = s;
+    } else {
+      s = srow[j];
     }
-    __syncthreads();
+    if (in_lds) kl[j] = order_key(s);
   }
+  __syncthreads();
+  // every thread reads back only keys it wrote itself or keys in LDS after the barrier
+  auto key_at = [&](int j) -> uint32_t { return in_lds ? kl[j] : order_key(srow[j]); };
 
   if (quota > 0) {
     uint32_t thr = 0, need_eq = 0;
@@ -68,19 +86,43 @@ __global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lct
         if (threadIdx.x < 256) hist[threadIdx.x] = 0;
         __syncthreads();
         for (int j = threadIdx.x; j < len; j += blockDim.x) {
-          const uint32_t u = order_key(srow[j]);
+          const uint32_t u = key_at(j);
           if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-          uint32_t cum = 0;
-          int b = 255;
-          for (; b > 0; --b) {
-            if (cum + hist[b] >= remaining) break;
-            cum += hist[b];
+        if (threadIdx.x < 64) {
+          // one wave scans the 256 bins from the top: lane l holds bins 255-4l .. 252-4l
+          const int lane = threadIdx.x;
+          uint32_t c[4], tot = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            c[i] = hist[255 - 4 * lane - i];
+            tot += c[i];
           }
-          sh_prefix = prefix | ((uint32_t)b << shift);
-          sh_remaining = remaining - cum;
+          uint32_t incl = tot;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
+          }
+          uint32_t cum = incl - tot, before = 0;
+          int found = -1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (found < 0 && cum + c[i] >= remaining) {
+              found = 255 - 4 * lane - i;
+              before = cum;
+            }
+            cum += c[i];
+          }
+          // the lowest lane with a hit holds the highest qualifying bin
+          const int first = __ffsll((unsigned long long)__ballot(found >= 0)) - 1;
+          const int b = __shfl(found, first, 64);
+          const uint32_t bef = __shfl(before, first, 64);
+          if (lane == 0) {
+            sh_prefix = prefix | ((uint32_t)b << shift);
+            sh_remaining = remaining - bef;
+          }
         }
         __syncthreads();
         prefix = sh_prefix;
@@ -96,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lct
     for (int base = 0; base < len; base += blockDim.x) {
       const int j = base + threadIdx.x;
       const bool valid = j < len;
-      const uint32_t u = valid ? order_key(srow[j]) : 0u;
+      const uint32_t u = valid ? key_at(j) : 0u;
       const bool gt = valid && (quota >= len || u > thr);
       const bool eq = valid && quota < len && u == thr;
       int tot_eq, tot_sel;

@@ -150,12 +150,13 @@ def test_anchor_host_errors():
     lib = L.lib()
     s = shape()
     ch = chunks([[0, 8, 0, 0]])
-    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 9, FAKE[1], None, None) == L.SRA_E_SHAPE
-    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 0, FAKE[1], None, None) == L.SRA_E_SHAPE
-    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 65, FAKE[1], None, None) == L.SRA_E_LIMIT
-    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 7, ch, 1, 2, FAKE[1], None, None) == L.SRA_E_CHUNKS
-    big = chunks([[0, 9000, 0, 0]])
-    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 9000, big, 1, 2, FAKE[1], None, None) == L.SRA_E_LIMIT
+    ws = FAKE[2]
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 9, FAKE[1], None, ws, 64, None) == L.SRA_E_SHAPE
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 0, FAKE[1], None, ws, 64, None) == L.SRA_E_SHAPE
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 65, FAKE[1], None, ws, 64, None) == L.SRA_E_LIMIT
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 7, ch, 1, 2, FAKE[1], None, ws, 64, None) == L.SRA_E_CHUNKS
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 2, FAKE[1], None, ws, 56, None) == L.SRA_E_WORKSPACE
+    assert lib.sra_extract_anchors(ctypes.byref(s), FAKE[0], 8, ch, 1, 2, FAKE[1], None, None, 64, None) == L.SRA_E_WORKSPACE
 
 
 def test_fused_layer_host_errors():

@@ -262,7 +262,8 @@ def test_anchors_match_oracle(idx):
     say(f"case anchors config {idx}")
     anchors = torch.empty((len(ch), k), dtype=torch.int32, device="cuda")
     norms = torch.zeros((w.store_rows,), dtype=torch.float32, device="cuda")
-    sra.extract_anchors(shape, dev(w.k_crit, cfg.dtype), ch, k, anchors, norms)
+    ws = torch.empty(sra.anchor_workspace_size(ch), dtype=torch.uint8, device="cuda")
+    sra.extract_anchors(shape, dev(w.k_crit, cfg.dtype), ch, k, anchors, ws, norms)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(anchors.cpu().numpy(), O.extract_anchors(w.k_crit, ch, k, cfg.dtype))
     np.testing.assert_allclose(norms.cpu().numpy(), O.key_norms(w.k_crit, cfg.dtype), rtol=1e-6)
