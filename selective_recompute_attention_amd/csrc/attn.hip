@@ -225,13 +225,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all masked so far: every p is 0
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = fast_exp2(m_run - m_use);
     float lsum = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float p = exp2f(s[st][rr] - m_use);
+        const float p = fast_exp2(s[st][rr] - m_use);
         s[st][rr] = p;
         lsum += p;
       }

@@ -52,6 +52,11 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 2^x with the bare hardware instruction (v_exp_f32: about 1 ulp; results below 2^-126 flush to
+// zero, which softmax weights can afford; -inf gives exactly 0). exp2f adds a denormal-range fixup
+// of four more instructions per call.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // theta_i = base^(-2i/d) and the rotation angle pos * theta_i, both in float64.
 __device__ __forceinline__ double rope_theta(int i, int d, double base) {
   return pow(base, -2.0 * (double)i / (double)d);

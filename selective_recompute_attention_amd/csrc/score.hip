@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
       const float m_use = (m == -INFINITY) ? 0.f : m;
       float s = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += exp2f(acc[r] - m_use);
+      for (int r = 0; r < 16; ++r) s += fast_exp2(acc[r] - m_use);
       s += __shfl_xor(s, 32, 64);
       if (hh == 0) wpart[wave * Mpad + 32 * qt + l32] = make_float2(m, s);
 #pragma unroll
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float2 ml = mlf[32 * qt + 8 * (r >> 2) + 4 * hh + (r & 3)];
-        col += exp2f(acc[r] - ml.x) * ml.y;
+        col += fast_exp2(acc[r] - ml.x) * ml.y;
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) { qh[ks] = nh[ks]; ql[ks] = nl[ks]; }
