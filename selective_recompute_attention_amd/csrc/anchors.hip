@@ -64,44 +64,49 @@ __global__ __launch_bounds__(256) void k_row_sumsq(ChunkTab tab, int row_elems,
 
 // One wave per chunk. The ranking (larger sum first, lower offset on a tie) is a strict total
 // order, so round r picks the best element ranked after the pick of round r-1: nothing is written
-// back, every round reads the same sums.
+// back, every round reads the same sums. Sums of squares are non-negative, so their float64 bit
+// patterns order like the values and every comparison is a branch-free 64-bit integer select.
 __global__ __launch_bounds__(256) void k_anchor_topk(ChunkTab tab, int k, const double* __restrict__ ss,
                                                      int32_t* __restrict__ anchors) {
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= tab.n) return;
   const int lane = threadIdx.x & 63;
   const int len = tab.len[e];
-  const double* s = ss + tab.delta[e];
+  const unsigned long long* s = reinterpret_cast<const unsigned long long*>(ss + tab.delta[e]);
   // the first 64*kCache sums stay in registers (one batch of independent loads); longer chunks
   // read the rest from memory each round
   constexpr int kCache = 16;
-  double cv[kCache];
+  unsigned long long cv[kCache];
 #pragma unroll
   for (int u = 0; u < kCache; ++u) {
     const int t = lane + 64 * u;
-    cv[u] = t < len ? s[t] : -DBL_MAX;   // below every sum: never picked (k <= len)
+    cv[u] = s[min(t, len - 1)];
   }
-  double pv = DBL_MAX;   // previous pick (value, offset); start above everything
+  unsigned long long pv = ~0ull;   // previous pick (value, offset); starts above everything
   int pt = -1;
+  auto consider = [&](unsigned long long v, int t, bool& have, unsigned long long& bv, int& bt) {
+    const bool after = t < len && (v < pv || (v == pv && t > pt));
+    const bool better = after && (!have || v > bv || (v == bv && t < bt));
+    bv = better ? v : bv;
+    bt = better ? t : bt;
+    have = have || better;
+  };
   for (int round = 0; round < k; ++round) {
-    double bv = -DBL_MAX;
+    bool have = false;
+    unsigned long long bv = 0;
     int bt = INT_MAX;
 #pragma unroll
-    for (int u = 0; u < kCache; ++u) {
-      const int t = lane + 64 * u;
-      const double v = cv[u];
-      const bool after = v < pv || (v == pv && t > pt);
-      if (after && (v > bv || (v == bv && t < bt))) { bv = v; bt = t; }
-    }
-    for (int t = lane + 64 * kCache; t < len; t += 64) {
-      const double v = s[t];
-      const bool after = v < pv || (v == pv && t > pt);
-      if (after && (v > bv || (v == bv && t < bt))) { bv = v; bt = t; }
-    }
+    for (int u = 0; u < kCache; ++u) consider(cv[u], lane + 64 * u, have, bv, bt);
+    for (int t = lane + 64 * kCache; t < len; t += 64) consider(s[t], t, have, bv, bt);
+#pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-      const double ov = __shfl_xor(bv, off, 64);
+      const unsigned long long ov = __shfl_xor(bv, off, 64);
       const int ot = __shfl_xor(bt, off, 64);
-      if (ov > bv || (ov == bv && ot < bt)) { bv = ov; bt = ot; }
+      const bool oh = __shfl_xor((int)have, off, 64) != 0;
+      const bool better = oh && (!have || ov > bv || (ov == bv && ot < bt));
+      bv = better ? ov : bv;
+      bt = better ? ot : bt;
+      have = have || oh;
     }
     if (lane == 0) anchors[(int64_t)tab.dst[e] * k + round] = bt;
     pv = bv;

@@ -99,20 +99,10 @@ int check_chunks(const sra_chunk* ch, int n_req, int n_chunks, int64_t store_row
 }
 
 // ------------------------------------------------------------------------------ workspace plan
-struct AttnSplit {
-  int n_splits, key_split;
-};
-
-AttnSplit attn_split(int n_req, int Hkv, int R, int g, int L) {
-  const int64_t tiles = (int64_t)n_req * Hkv * ceil_div((int64_t)R * g, 128);
-  AttnSplit s{1, std::max(L, 1)};
-  if (tiles == 0 || tiles >= 512 || L <= 256) return s;
-  const int64_t want = ceil_div(1024, tiles);
-  const int64_t n = std::min<int64_t>(std::min<int64_t>(want, ceil_div(L, 256)), 16);  // <= kMaxSplits
-  const int ks = (int)(ceil_div(ceil_div(L, n), 64) * 64);
-  s.key_split = ks;
-  s.n_splits = (int)ceil_div(L, ks);
-  return s;
+// Attention work groups per (request, KV head) group: the resident capacity shared out.
+int attn_pieces(int n_req, int Hkv) {
+  const int64_t groups = (int64_t)n_req * Hkv;
+  return (int)std::max<int64_t>(1, sra::kAttnSlots / std::max<int64_t>(groups, 1));
 }
 
 struct Plan {
@@ -126,9 +116,9 @@ struct Plan {
   int64_t qrot_plane = 0;  // elements per hi/lo plane
   // score (f32)
   size_t prob = 0, parts = 0;
-  // attention
-  AttnSplit split{1, 1};
-  size_t part_o = 0, part_ml = 0;
+  // attention (bf16): prepared query operand, tile prefix sums, partial results
+  int n_tiles = 0, qop_blocks = 0, pieces = 1;
+  size_t qop = 0, tilecum = 0, part_o = 0, part_ml = 0;
   size_t score_end = 0, attn_end = 0, total = 0;
 };
 
@@ -137,8 +127,8 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
   const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads, g = Hq / Hkv;
   const int Lctx = std::max(L - Lq, 0);
   size_t off = 0;
-  p.cs = off;
-  off = align256(off + (size_t)n_req * R * (D / 2) * sizeof(float2));
+  p.cs = off;  // the float32 attention's angle table
+  if (s->dtype == SRA_DTYPE_F32) off = align256(off + (size_t)n_req * R * (D / 2) * sizeof(float2));
   p.region = off;
   // score region
   size_t so = off;
@@ -156,16 +146,18 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
   }
   p.scores_tmp = so; so = align256(so + (size_t)n_req * Lctx * sizeof(float));
   p.score_end = so;
-  // attention region (same start: scoring is finished before attention runs)
+  // attention region (same start: scoring is finished before the scatter writes it)
   size_t ao = off;
   if (s->dtype == SRA_DTYPE_BF16) {
-    p.split = attn_split(n_req, Hkv, R, g, L);
-    if (p.split.n_splits > 1) {
-      const int64_t tiles = (int64_t)n_req * Hkv * ceil_div((int64_t)R * g, 128);
-      const int64_t slots = tiles * p.split.n_splits * 128;
-      p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(float));
-      p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float2));
-    }
+    const int64_t groups = (int64_t)n_req * Hkv;
+    p.n_tiles = (int)ceil_div((int64_t)R * g, 128);
+    p.qop_blocks = 4 * p.n_tiles;
+    p.pieces = attn_pieces(n_req, Hkv);
+    p.qop = ao; ao = align256(ao + (size_t)groups * p.qop_blocks * 32 * 2 * D * sizeof(uint16_t));
+    p.tilecum = ao; ao = align256(ao + (size_t)n_req * (p.n_tiles + 1) * sizeof(int));
+    const int64_t slots = groups * p.pieces * 2 * 128;
+    p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(float));
+    p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float2));
   }
   p.attn_end = ao;
   p.total = std::max(p.score_end, p.attn_end);
@@ -337,7 +329,8 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
     // merge kernel runs between the passes.
     int max_blocks = 0;
     for (int q = 0; q < n_req; ++q) max_blocks = std::max(max_blocks, req_blk0[q + 1] - req_blk0[q]);
-    const int fuse_merge = (int64_t)max_blocks * p.Mpad <= 4096 ? 1 : 0;
+    // pass 2 merges in place while each wave's share (blocks x its query tiles) stays small
+    const int fuse_merge = (int64_t)max_blocks * ceil_div(p.Mpad / 32, 4) <= 128 ? 1 : 0;
     for (int pass = 1; pass <= 2; ++pass) {
       if (pass == 2 && !fuse_merge) {
         e = sra::launch_score_merge(req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, ml_part, ml_final, st);
@@ -374,30 +367,37 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
   return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, 1, parts, sc, row_pos, st);
 }
 
+// S4 on rows whose per-row inputs are ready: the prepared query operand (bf16) or the angle
+// table (f32) in the workspace.
 int do_attn(const sra_shape* s, int n_req, const void* q, int q_rows, int indexed,
             const int32_t* row_pos, int R, const void* kf, const void* vf, int L, void* out,
-            float* lse, const float2* cs, void* ws, const Plan& p, hipStream_t st) {
+            float* lse, void* ws, const Plan& p, hipStream_t st) {
   const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads;
   hipError_t e;
   if (s->dtype == SRA_DTYPE_BF16) {
-    e = sra::launch_attn_bf16(D, n_req, Hq, Hkv, R, L, (const uint16_t*)q, q_rows, indexed, row_pos,
-                              cs, (const uint16_t*)kf, (const uint16_t*)vf, (uint16_t*)out, lse,
-                              p.split.n_splits, p.split.key_split,
+    e = sra::launch_attn_bf16(D, n_req, Hq, Hkv, R, L, reinterpret_cast<const uint16_t*>(wsp(ws, p.qop)),
+                              p.qop_blocks, row_pos, (const uint16_t*)kf, (const uint16_t*)vf,
+                              (uint16_t*)out, lse, p.pieces, reinterpret_cast<int*>(wsp(ws, p.tilecum)),
                               reinterpret_cast<float*>(wsp(ws, p.part_o)),
                               reinterpret_cast<float2*>(wsp(ws, p.part_ml)), st);
   } else {
-    e = sra::launch_attn_f32(D, n_req, Hq, Hkv, R, L, (const float*)q, q_rows, indexed, row_pos, cs,
-                             (const float*)kf, (const float*)vf, (float*)out, lse, st);
+    e = sra::launch_attn_f32(D, n_req, Hq, Hkv, R, L, (const float*)q, q_rows, indexed, row_pos,
+                             reinterpret_cast<const float2*>(wsp(ws, p.cs)), (const float*)kf,
+                             (const float*)vf, (float*)out, lse, st);
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return SRA_OK;
 }
 
+float attn_scale_log2(int D) { return 1.4426950408889634f / std::sqrt((float)D); }
+
 int check_attn_limits(const sra_shape* s, int R, int L) {
   if (s->dtype == SRA_DTYPE_F32 && s->n_q_heads / s->n_kv_heads > 16)
     return fail(SRA_E_LIMIT, "float32 attention supports at most 16 query heads per KV head");
-  if ((int64_t)R * (s->n_q_heads / s->n_kv_heads) > (int64_t)1 << 30)
-    return fail(SRA_E_LIMIT, "too many query vectors");
+  if (s->dtype == SRA_DTYPE_BF16 &&
+      ceil_div((int64_t)R * (s->n_q_heads / s->n_kv_heads), 128) > sra::kAttnMaxTiles)
+    return fail(SRA_E_LIMIT, "bf16 attention supports at most %d query vectors per KV head and request",
+                sra::kAttnMaxTiles * 128);
   (void)L;
   return SRA_OK;
 }
@@ -569,9 +569,9 @@ int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, con
   if (overlap(k_new, nb, k_fused, fb) || overlap(k_new, nb, v_fused, fb) || overlap(v_new, nb, k_fused, fb) ||
       overlap(v_new, nb, v_fused, fb) || overlap(k_fused, fb, v_fused, fb))
     return fail(SRA_E_ALIAS, "fresh rows and fused cache overlap");
-  hipError_t e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_kv_heads, n_req, R, L, k_new,
-                                     v_new, R, 0, row_pos, k_fused, v_fused, nullptr, nullptr, 0,
-                                     shape->rope_base, stream);
+  hipError_t e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads,
+                                     n_req, R, L, nullptr, k_new, v_new, R, 0, row_pos, k_fused, v_fused,
+                                     nullptr, nullptr, 0, 0.f, shape->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   return ok();
 }
@@ -595,11 +595,17 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
     return fail(SRA_E_ALIAS, "out overlaps an input");
   const Plan p = make_plan(shape, n_req, 1, L, R, 1);
   if ((rc = check_ws(ws, ws_bytes, p.attn_end))) return rc;
-  float2* cs = reinterpret_cast<float2*>(wsp(ws, p.cs));
-  hipError_t e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, cs, nullptr, 0,
-                                        shape->rope_base, stream);
-  if (e != hipSuccess) return hip_fail(e, "rotary table launch");
-  if ((rc = do_attn(shape, n_req, q_new, R, 0, row_pos, R, k_fused, v_fused, L, out, lse, cs, ws, p, stream)))
+  hipError_t e;
+  if (shape->dtype == SRA_DTYPE_BF16)
+    e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads, n_req, R, L,
+                            q_new, nullptr, nullptr, R, 0, row_pos, nullptr, nullptr, nullptr,
+                            reinterpret_cast<uint16_t*>(wsp(ws, p.qop)), p.qop_blocks,
+                            attn_scale_log2(shape->head_dim), shape->rope_base, stream);
+  else
+    e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, reinterpret_cast<float2*>(wsp(ws, p.cs)),
+                               shape->rope_base, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention row-input launch");
+  if ((rc = do_attn(shape, n_req, q_new, R, 0, row_pos, R, k_fused, v_fused, L, out, lse, ws, p, stream)))
     return rc;
   return ok();
 }
@@ -653,6 +659,7 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
     hipError_t er = hipEventRecord(ev[i], stream);
     return er == hipSuccess ? SRA_OK : hip_fail(er, "stage event record");
   };
+  // one stream: a second stream's fork/join costs more host and GPU time than S1 || S2 saves
   if ((rc = mark(0))) return rc;
   if ((rc = do_rerotate(s, n_req, a->k_store, a->v_store, a->chunks, a->n_chunks, a->k_fused,
                         a->v_fused, L, stream)))
@@ -664,15 +671,17 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
       return rc;
   }
   if ((rc = mark(3)) || (rc = mark(4))) return rc;
-  float2* cs = reinterpret_cast<float2*>(wsp(ws, p.cs));
-  // the scatter kernel also writes the rows' rotary table for the attention
-  hipError_t e = sra::launch_scatter(s->dtype, s->head_dim, s->n_kv_heads, n_req, R, L, a->k_fresh,
-                                     a->v_fresh, L, 1, a->row_pos, a->k_fused, a->v_fused, cs, nullptr,
-                                     0, s->rope_base, stream);
+  // the scatter kernel also writes the attention's per-row inputs (query operand or angle table)
+  const bool bf = s->dtype == SRA_DTYPE_BF16;
+  hipError_t e = sra::launch_scatter(
+      s->dtype, s->head_dim, s->n_q_heads, s->n_kv_heads, n_req, R, L, a->q_fresh, a->k_fresh, a->v_fresh,
+      L, 1, a->row_pos, a->k_fused, a->v_fused, bf ? nullptr : reinterpret_cast<float2*>(wsp(ws, p.cs)),
+      bf ? reinterpret_cast<uint16_t*>(wsp(ws, p.qop)) : nullptr, p.qop_blocks, attn_scale_log2(s->head_dim),
+      s->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   if ((rc = mark(5)) || (rc = mark(6))) return rc;
   if ((rc = do_attn(s, n_req, a->q_fresh, L, 1, a->row_pos, R, a->k_fused, a->v_fused, L, a->out,
-                    a->lse, cs, ws, p, stream)))
+                    a->lse, ws, p, stream)))
     return rc;
   if ((rc = mark(7))) return rc;
   return ok();

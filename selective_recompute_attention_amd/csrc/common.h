@@ -67,6 +67,34 @@ __device__ __forceinline__ float2 rope_cs(double pos, int i, int d, double base)
   return make_float2((float)c, (float)s);
 }
 
+// Prepared query operand of the bf16 attention (written by the row kernel, read by the attention).
+// Query vectors of one (request, KV head) group are numbered v = r * g + (h % g) and cut into
+// blocks of 32. For block b, 16-dimension step ks and plane (0: hi = bf16(x), 1: lo = bf16(x - hi))
+// the 32 vectors' dimensions 16 ks + 8 hh + s (hh = 0, 1; s = 0..7) are contiguous, lane-major: one
+// wave reads the B operand of one matrix instruction as 1 KB of consecutive bytes.
+__host__ __device__ __forceinline__ int64_t qop_index(int64_t group, int b, int ks, int plane, int l,
+                                                      int hh, int n_blk, int nks) {
+  return ((((group * n_blk + b) * nks + ks) * 2 + plane) * 32 + l) * 16 + hh * 8;
+}
+
+// Work split of the bf16 attention. A group's 128-vector tiles need ceil((p_last + 1) / 64) units
+// of 64 keys each; the U units of a group are dealt to `pieces_used` work groups as contiguous
+// ranges [U i / P, U (i + 1) / P). kAttnSlots is the number of resident attention work groups on
+// 256 compute units (two per unit).
+constexpr int kAttnSlots = 512;
+constexpr int kAttnMinUnits = 3;
+constexpr int kAttnMaxTiles = 2048;
+__host__ __device__ __forceinline__ int attn_pieces_used(int U, int pieces) {
+  const int p = (U + kAttnMinUnits - 1) / kAttnMinUnits;
+  return p < 1 ? 1 : (p < pieces ? p : pieces);
+}
+__host__ __device__ __forceinline__ int attn_piece_start(int U, int P, int i) {
+  return (int)((int64_t)U * i / P);
+}
+__host__ __device__ __forceinline__ int attn_piece_of(int U, int P, int u) {
+  return (int)(((int64_t)(u + 1) * P - 1) / U);
+}
+
 }  // namespace sra
 
 // ---------------------------------------------------------------------------- launchers
@@ -75,14 +103,17 @@ namespace sra {
 hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
                            const void* ks, const void* vs, void* kf, void* vf, int64_t L,
                            double base, hipStream_t st);
-// launch_scatter / launch_rope_table also zero `n_zero` ints at `zero` (the attention's arrival
-// counters) when zero is non-NULL.
-hipError_t launch_scatter(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
-                          const void* vn, int fresh_rows, int indexed, const int* row_pos,
-                          void* kf, void* vf, float2* cs_out, int* zero, int n_zero, double base,
+// Per recomputed row (row_pos[r] = p in [0, L)): the row's cos/sin table (cs_out, optional), the
+// fresh K/V scatter (kn/vn optional) and, for bf16, the attention's prepared query operand (qn/qop
+// optional; rows outside [0, L) get zeros). Fresh rows are compact (row r) or, when indexed,
+// position-indexed (row p); fresh_rows is their count per request.
+hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, int L,
+                          const void* qn, const void* kn, const void* vn, int fresh_rows,
+                          int indexed, const int* row_pos, void* kf, void* vf, float2* cs_out,
+                          uint16_t* qop, int qop_blocks, float scale_log2, double base,
                           hipStream_t st);
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
-                             int* zero, int n_zero, double base, hipStream_t st);
+                             double base, hipStream_t st);
 hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
                           double* ss, int32_t* anchors, float* norms, hipStream_t st);
 hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv, int Mpad,
@@ -102,11 +133,12 @@ hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, f
                              hipStream_t st);
 hipError_t launch_select(const SelTab& tab, int nparts, int Lctx, int Lq, int R, const float* parts,
                          float* scores, int* row_pos, hipStream_t st);
-hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* q,
-                            int q_rows, int indexed, const int* row_pos, const float2* cs,
-                            const uint16_t* kf, const uint16_t* vf, uint16_t* out, float* lse,
-                            int n_splits, int key_split, float* part_o, float2* part_ml,
-                            hipStream_t st);
+// qop: prepared query operand (qop_blocks blocks of 32 vectors per group); tilecum: [n_req][tiles+1]
+// ints; part_o / part_ml: [n_groups][pieces][2][128] partial results.
+hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,
+                            int qop_blocks, const int* row_pos, const uint16_t* kf,
+                            const uint16_t* vf, uint16_t* out, float* lse, int pieces,
+                            int* tilecum, float* part_o, float2* part_ml, hipStream_t st);
 hipError_t launch_attn_f32(int D, int n_req, int Hq, int Hkv, int R, int L, const float* q,
                            int q_rows, int indexed, const int* row_pos, const float2* cs,
                            const float* kf, const float* vf, float* out, float* lse,

@@ -1,5 +1,6 @@
 // Streaming rotary kernels: S1 re-rotation of cached chunk keys into the fused cache, S3 scatter
-// of fresh K/V rows, the per-row angle table used by the sparse attention, and the row check.
+// of fresh K/V rows together with the sparse attention's per-row inputs (angle table or prepared
+// query operand), and the row check.
 //
 // S1 follows "full KV reuse after adjusting the position encoding" (CacheBlend problem definition
 // page, §2.4): a chunk cached at original positions orig + t moves to fused rows n_c + t, so each
@@ -113,43 +114,91 @@ __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int row
   }
 }
 
-// One block per (recomputed row r, request). Fresh rows are compact (row r) or position-indexed
-// (row row_pos[r]). Writes the row's cos/sin table when cs_out is given.
+// One block per (recomputed row r, request) at position p = row_pos[r]: forms the row's angles
+// once, then (each part optional) writes them out, scatters the fresh K/V row to fused row p with
+// K rotated at p, and writes the attention's query operand: every query head rotated at p, scaled
+// by log2(e)/sqrt(d) and split into bf16 hi/lo planes in the matrix-operand order of qop_index.
+// Fresh rows are compact (row r) or position-indexed (row p). Rows outside [0, L) write nothing
+// but zero query operands.
 template <typename T, int D>
-__global__ __launch_bounds__(128) void k_scatter(int Hkv, int R, int L, const T* __restrict__ kn,
+__global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
+                                                 const T* __restrict__ qn, const T* __restrict__ kn,
                                                  const T* __restrict__ vn, int fresh_rows,
                                                  int indexed, const int* __restrict__ row_pos,
                                                  T* __restrict__ kf, T* __restrict__ vf,
-                                                 float2* __restrict__ cs_out, int* __restrict__ zero,
-                                                 int n_zero, double base) {
+                                                 float2* __restrict__ cs_out, uint16_t* __restrict__ qop,
+                                                 int qop_blocks, float scale_log2, double base) {
   constexpr int H = D / 2;
+  constexpr int NKS = D / 16;
   __shared__ float2 cs[H];
   const int r = blockIdx.x, q = blockIdx.y;
-  if (zero && r == 0 && q == 0)
-    for (int u = threadIdx.x; u < n_zero; u += blockDim.x) zero[u] = 0;
   const int p = row_pos[(int64_t)q * R + r];
-  if (p < 0 || p >= L) return;  // rows outside the cache are never written
+  const bool valid = p >= 0 && p < L;  // rows outside the cache are never written
   const int srow = indexed ? p : r;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    const float2 v = rope_cs((double)p, i, D, base);
-    cs[i] = v;
-    if (cs_out) cs_out[((int64_t)q * R + r) * H + i] = v;
+  if (valid) {
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+      const float2 v = rope_cs((double)p, i, D, base);
+      cs[i] = v;
+      if (cs_out) cs_out[((int64_t)q * R + r) * H + i] = v;
+    }
   }
   __syncthreads();
   const int64_t row_elems = (int64_t)Hkv * D;
-  const int64_t src0 = ((int64_t)q * fresh_rows + srow) * row_elems;
-  const int64_t dst0 = ((int64_t)q * L + p) * row_elems;
-  copy16(vn + src0, vf + dst0, row_elems * sizeof(T) / 16, threadIdx.x, blockDim.x);
-  rotate_rows<T, D>(kn + src0, kf + dst0, Hkv, cs, threadIdx.x, blockDim.x);
+  if (valid && kn) {
+    const int64_t src0 = ((int64_t)q * fresh_rows + srow) * row_elems;
+    const int64_t dst0 = ((int64_t)q * L + p) * row_elems;
+    copy16(vn + src0, vf + dst0, row_elems * sizeof(T) / 16, threadIdx.x, blockDim.x);
+    rotate_rows<T, D>(kn + src0, kf + dst0, Hkv, cs, threadIdx.x, blockDim.x);
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (qop) {
+      // unit = (head, 16-dim step ks < NKS/2, half hh): dims 16 ks + 8 hh + s pair with + D/2
+      const int g = Hq / Hkv;
+      const int n_units = Hq * NKS;
+      for (int u = threadIdx.x; u < n_units; u += blockDim.x) {
+        const int h = u / NKS, ks = (u % NKS) >> 1, hh = u & 1;
+        const int d0 = 16 * ks + 8 * hh;
+        float x[8], y[8];
+        if (valid) {
+          const T* src = qn + (((int64_t)q * fresh_rows + srow) * Hq + h) * D + d0;
+          Vec<T>::unpack(*reinterpret_cast<const u32x4*>(src), x);
+          Vec<T>::unpack(*reinterpret_cast<const u32x4*>(src + H), y);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float2 c = cs[d0 + k];
+            const float a = x[k] * c.x - y[k] * c.y, b = x[k] * c.y + y[k] * c.x;
+            x[k] = a * scale_log2;
+            y[k] = b * scale_log2;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = y[k] = 0.f;
+        }
+        const int v = r * g + h % g;
+        const int64_t grp = (int64_t)q * Hkv + h / g;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const float* f = half ? y : x;
+          u32x4 wh, wl;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            wh[k] = pack_bf2(f[2 * k], f[2 * k + 1]);
+            wl[k] = pack_bf2(f[2 * k] - bf2f(wh[k] & 0xffffu), f[2 * k + 1] - bf2f(wh[k] >> 16));
+          }
+          const int kss = ks + half * (NKS / 2);
+          *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 0, v & 31, hh, qop_blocks, NKS)) = wh;
+          *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 1, v & 31, hh, qop_blocks, NKS)) = wl;
+        }
+      }
+    }
+  }
 }
 
 template <int D>
 __global__ void k_rope_table(int R, const int* __restrict__ row_pos, float2* __restrict__ cs_out,
-                             int* __restrict__ zero, int n_zero, double base) {
+                             double base) {
   constexpr int H = D / 2;
   const int r = blockIdx.x, q = blockIdx.y;
-  if (zero && r == 0 && q == 0)
-    for (int u = threadIdx.x; u < n_zero; u += blockDim.x) zero[u] = 0;
   const int p = row_pos[(int64_t)q * R + r];
   for (int i = threadIdx.x; i < H; i += blockDim.x)
     cs_out[((int64_t)q * R + r) * H + i] = rope_cs((double)p, i, D, base);
@@ -189,39 +238,42 @@ hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int r
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
-                          const void* vn, int fresh_rows, int indexed, const int* row_pos,
-                          void* kf, void* vf, float2* cs_out, int* zero, int n_zero, double base,
+hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, int L,
+                          const void* qn, const void* kn, const void* vn, int fresh_rows,
+                          int indexed, const int* row_pos, void* kf, void* vf, float2* cs_out,
+                          uint16_t* qop, int qop_blocks, float scale_log2, double base,
                           hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(128);
   if (dtype == 0 && D == 128)
-    k_scatter<uint16_t, 128><<<g, b, 0, st>>>(Hkv, R, L, (const uint16_t*)kn, (const uint16_t*)vn,
-                                               fresh_rows, indexed, row_pos, (uint16_t*)kf,
-                                               (uint16_t*)vf, cs_out, zero, n_zero, base);
+    k_scatter<uint16_t, 128><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const uint16_t*)qn, (const uint16_t*)kn,
+                                               (const uint16_t*)vn, fresh_rows, indexed, row_pos,
+                                               (uint16_t*)kf, (uint16_t*)vf, cs_out, qop, qop_blocks,
+                                               scale_log2, base);
   else if (dtype == 0 && D == 64)
-    k_scatter<uint16_t, 64><<<g, b, 0, st>>>(Hkv, R, L, (const uint16_t*)kn, (const uint16_t*)vn,
-                                              fresh_rows, indexed, row_pos, (uint16_t*)kf,
-                                              (uint16_t*)vf, cs_out, zero, n_zero, base);
+    k_scatter<uint16_t, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const uint16_t*)qn, (const uint16_t*)kn,
+                                              (const uint16_t*)vn, fresh_rows, indexed, row_pos,
+                                              (uint16_t*)kf, (uint16_t*)vf, cs_out, qop, qop_blocks,
+                                              scale_log2, base);
   else if (dtype == 1 && D == 128)
-    k_scatter<float, 128><<<g, b, 0, st>>>(Hkv, R, L, (const float*)kn, (const float*)vn,
-                                            fresh_rows, indexed, row_pos, (float*)kf, (float*)vf,
-                                            cs_out, zero, n_zero, base);
+    k_scatter<float, 128><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
+                                            (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
+                                            (float*)vf, cs_out, nullptr, 0, scale_log2, base);
   else
-    k_scatter<float, 64><<<g, b, 0, st>>>(Hkv, R, L, (const float*)kn, (const float*)vn,
-                                           fresh_rows, indexed, row_pos, (float*)kf, (float*)vf,
-                                           cs_out, zero, n_zero, base);
+    k_scatter<float, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
+                                           (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
+                                           (float*)vf, cs_out, nullptr, 0, scale_log2, base);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
-                             int* zero, int n_zero, double base, hipStream_t st) {
+                             double base, hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(64);
   if (D == 128)
-    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, zero, n_zero, base);
+    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
   else
-    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, zero, n_zero, base);
+    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
   return hipGetLastError();
 }
 

@@ -115,10 +115,11 @@ __device__ void merge_rows(int b0, int b1, int Hkv, int kvh, int Mpad, int v_lo,
       for (int b = b0 + j; b < b1; b += 8 * T) {
         float2 p[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int bb = b + u * T;
-          p[u] = bb < b1 ? ml_part[((int64_t)bb * Hkv + kvh) * Mpad + v] : make_float2(-INFINITY, 0.f);
-        }
+        for (int u = 0; u < 8; ++u)
+          p[u] = ml_part[((int64_t)min(b + u * T, b1 - 1) * Hkv + kvh) * Mpad + v];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (b + u * T >= b1) p[u] = make_float2(-INFINITY, 0.f);
 #pragma unroll
         for (int u = 0; u < 8; ++u) ml_merge(M, S, p[u]);
       }
@@ -158,10 +159,14 @@ __device__ __forceinline__ void load_q(const uint16_t* qp, int64_t plane, bf16x8
   }
 }
 
-// grid (key blocks, Hkv); 4 waves, each owning 32 keys of a 128-key block of one chunk. The next
-// query tile's operands are loaded while the current tile is multiplied.
-// PASS 1 writes ml_part[blk][kvh][v] = (max, sum exp2(y - max)) over the block's keys;
-// PASS 2 writes colsum[req][kvh][j] = sum_v exp2(y - M_v) * invS_v.
+// grid (key blocks, Hkv). A block owns 128 keys of one chunk (staged once in LDS, rows padded for
+// conflict-free 16-byte reads); wave w owns the 32-vector query tiles w, w+4, ... with their
+// operands in registers. Every global load of a tile (K, Q and, in pass 2, the merge inputs) is
+// issued before any of them is waited on, so each block pays about one memory latency.
+// PASS 1 writes ml_part[blk][kvh][v] = (max, sum exp2(y - max)) over the block's keys (S^T = K Q^T:
+// one query vector per lane column, its 128 keys across the registers of both half-waves).
+// PASS 2 writes colsum[req][kvh][j] = sum_v exp2(y - M_v) * invS_v (S = Q K^T: one key per lane
+// column), the four waves' sums added in wave order.
 template <int D, int PASS>
 __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, int Hkv, int Mpad,
                                                     int Mvalid, int Lctx,
@@ -172,93 +177,152 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
                                                     const float2* __restrict__ ml_final,
                                                     int fuse_merge, float* __restrict__ colsum) {
   constexpr int NKS = D / 16;
-  extern __shared__ float2 smem[];
+  constexpr int KB = 128;          // keys per block
+  constexpr int KST = D + 8;       // LDS row stride (elements)
+  constexpr int NKL = KB * (D / 8) / 256;
+  constexpr int MB = 16;           // merge inputs per lane per batch
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KST];
+  __shared__ float colred[4][KB];
+  __shared__ float2 mlw[4][32];
   const int blk = blockIdx.x, kvh = blockIdx.y;
   const int e = find_entry(tab, blk);
-  const int kb = blk - tab.blk0[e];
-  const int req = tab.req[e], len = tab.len[e];
+  const int t0 = (blk - tab.blk0[e]) * KB;
+  const int req = tab.req[e];
+  const int nk = min(KB, tab.len[e] - t0);   // valid keys of this block (>= 1)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
-  const int t_base = kb * 128 + wave * 32;
-  const int tk = t_base + l32;
-  const bool kvalid = tk < len;
-  const int64_t trow = (int64_t)tab.src[e] + min(tk, len - 1);
-
-  // this lane's key row (32x32x16 operand: key = l32, dims 16*ks + 8*hh .. +8)
-  bf16x8 kreg[NKS];
-  const uint16_t* kp = kc + (trow * Hkv + kvh) * D + 8 * hh;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 16 * ks));
-
-  const uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;
   const int nqt = Mpad / 32;
-  bf16x8 qh[NKS], ql[NKS], nh[NKS], nl[NKS];
-  load_q<NKS>(qb + (int64_t)l32 * D, plane, qh, ql);
 
-  if constexpr (PASS == 1) {
-    float2* wpart = smem;  // [4][Mpad]
-    for (int qt = 0; qt < nqt; ++qt) {
-      if (qt + 1 < nqt) load_q<NKS>(qb + (int64_t)(32 * (qt + 1) + l32) * D, plane, nh, nl);
-      f32x16 acc = {};
+  // K rows of the block (dims fastest, 16 bytes per load); rows past the chunk's end are zero. The
+  // loads are unconditional (clamped row, zeroed afterwards) so they all go out before any wait.
+  u32x4 kr[NKL];
+  const uint16_t* kbase = kc + (((int64_t)tab.src[e] + t0) * Hkv + kvh) * D;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[ks], qh[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[ks], ql[ks], acc, 0, 0, 0);
+  for (int i = 0; i < NKL; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    const int row = u / (D / 8);
+    kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)min(row, nk - 1) * Hkv * D + 8 * (u % (D / 8)));
+  }
+#pragma unroll
+  for (int i = 0; i < NKL; ++i)
+    if ((threadIdx.x + 256 * i) / (D / 8) >= nk) kr[i] = u32x4{0u, 0u, 0u, 0u};
+  const uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;
+  bf16x8 qh[NKS], ql[NKS];
+  if (wave < nqt) load_q<NKS>(qb + (int64_t)(32 * wave + l32) * D, plane, qh, ql);
+
+  // pass 2: (max, 1/sum) of query vector 32 qt + l32 over the request's blocks; the two half-waves
+  // take alternate blocks and merge in a fixed order
+  auto merged_ml = [&](int qt) -> float2 {
+    const int v = 32 * qt + l32;
+    float M = -INFINITY, S = 0.f;
+    if (fuse_merge) {
+      const int b0 = rb.blk0[req], b1 = rb.blk0[req + 1];
+      for (int b = b0 + hh; b < b1; b += 2 * MB) {
+        float2 pm[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u)
+          pm[u] = ml_part[((int64_t)min(b + 2 * u, b1 - 1) * Hkv + kvh) * Mpad + v];
+#pragma unroll
+        for (int u = 0; u < MB; ++u)
+          if (b + 2 * u >= b1) pm[u] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int u = 0; u < MB; ++u) ml_merge(M, S, pm[u]);
       }
-      // acc[r] = exp2 exponent of key t_base + 8*(r/4) + 4*hh + r%4 for query vector 32*qt + l32
-      if (t_base + 32 > len) {   // partial block: drop the keys past the chunk's end
+      float Mo = __shfl_xor(M, 32, 64), So = __shfl_xor(S, 32, 64);
+      if (hh == 1) { const float tm = M, ts = S; M = Mo; S = So; Mo = tm; So = ts; }
+      ml_merge(M, S, make_float2(Mo, So));   // half 0's blocks first, then half 1's
+      return (v < Mvalid && S > 0.f) ? make_float2(M, 1.f / S) : make_float2(0.f, 0.f);
+    }
+    return ml_final[((int64_t)req * Hkv + kvh) * Mpad + v];
+  };
+  float2 mlv = make_float2(0.f, 0.f);
+  if constexpr (PASS == 2) {
+    if (wave < nqt) mlv = merged_ml(wave);
+  }
+
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t_base + 8 * (r >> 2) + 4 * hh + (r & 3) >= len) acc[r] = -INFINITY;
+  for (int i = 0; i < NKL; ++i) {
+    const int u = threadIdx.x + 256 * i;
+    *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) = kr[i];
+  }
+  __syncthreads();
+
+  float col[4] = {0.f, 0.f, 0.f, 0.f};   // pass 2: keys 32 st + l32
+  for (int qt = wave; qt < nqt; qt += 4) {
+    if (qt != wave) {
+      load_q<NKS>(qb + (int64_t)(32 * qt + l32) * D, plane, qh, ql);
+      if constexpr (PASS == 2) mlv = merged_ml(qt);
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc[st] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 kb =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (32 * st + l32) * KST + 16 * ks + 8 * hh));
+        if constexpr (PASS == 1) {
+          acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qh[ks], acc[st], 0, 0, 0);
+          acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, ql[ks], acc[st], 0, 0, 0);
+        } else {
+          acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[ks], kb, acc[st], 0, 0, 0);
+          acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[ks], kb, acc[st], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (PASS == 1) {
+      // acc[st][r] = exp2 exponent of key 32 st + 8 (r/4) + 4 hh + r%4 for query vector 32 qt + l32
+      if (nk < KB) {   // partial block: drop the keys past the chunk's end
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * st + 8 * (r >> 2) + 4 * hh + (r & 3) >= nk) acc[st][r] = -INFINITY;
       }
       float m = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[r]);
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[st][r]);
       m = fmaxf(m, __shfl_xor(m, 32, 64));
       const float m_use = (m == -INFINITY) ? 0.f : m;
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s += fast_exp2(acc[r] - m_use);
-      s += __shfl_xor(s, 32, 64);
-      if (hh == 0) wpart[wave * Mpad + 32 * qt + l32] = make_float2(m, s);
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) { qh[ks] = nh[ks]; ql[ks] = nl[ks]; }
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(acc[st][r] - m_use);
+      sum += __shfl_xor(sum, 32, 64);
+      if (hh == 0)
+        ml_part[((int64_t)(blk_base + blk) * Hkv + kvh) * Mpad + 32 * qt + l32] = make_float2(m, sum);
+    } else {
+      // acc[st][r] = logit of query vector 32 qt + 8 (r/4) + 4 hh + r%4 against key 32 st + l32;
+      // that vector's (max, 1/sum) sits in lane 8 (r/4) + 4 hh + r%4 of this wave
+      // (a wave's LDS accesses complete in program order, so no barrier is needed here)
+      mlw[wave][l32] = mlv;   // both halves hold the same value
+      float2 mr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mr[r] = mlw[wave][8 * (r >> 2) + 4 * hh + (r & 3)];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float c = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c += fast_exp2(acc[st][r] - mr[r].x) * mr[r].y;
+        col[st] += c;
+      }
+    }
+  }
+  if constexpr (PASS == 2) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const float c = col[st] + __shfl_xor(col[st], 32, 64);
+      if (hh == 0) colred[wave][32 * st + l32] = c;
     }
     __syncthreads();
-    float2* dst = ml_part + ((int64_t)(blk_base + blk) * Hkv + kvh) * Mpad;
-    for (int v = threadIdx.x; v < Mpad; v += blockDim.x) {
-      float M = -INFINITY, S = 0.f;
-      for (int w = 0; w < 4; ++w) ml_merge(M, S, wpart[w * Mpad + v]);
-      dst[v] = make_float2(M, S);
+    if (threadIdx.x < nk) {
+      const int j = threadIdx.x;
+      const float c = ((colred[0][j] + colred[1][j]) + colred[2][j]) + colred[3][j];
+      colsum[((int64_t)req * Hkv + kvh) * Lctx + tab.dst[e] + t0 + j] = c;
     }
-  } else {
-    float2* mlf = smem;  // [Mpad]
-    if (fuse_merge) {
-      merge_rows(rb.blk0[req], rb.blk0[req + 1], Hkv, kvh, Mpad, 0, Mpad, Mvalid, ml_part, mlf);
-    } else {
-      const float2* src = ml_final + ((int64_t)req * Hkv + kvh) * Mpad;
-      for (int v = threadIdx.x; v < Mpad; v += blockDim.x) mlf[v] = src[v];
-      __syncthreads();
-    }
-    float col = 0.f;
-    for (int qt = 0; qt < nqt; ++qt) {
-      if (qt + 1 < nqt) load_q<NKS>(qb + (int64_t)(32 * (qt + 1) + l32) * D, plane, nh, nl);
-      f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qh[ks], kreg[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ql[ks], kreg[ks], acc, 0, 0, 0);
-      }
-      // acc[r] = logit of query vector 32*qt + 8*(r/4) + 4*hh + r%4 against key t_base + l32
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float2 ml = mlf[32 * qt + 8 * (r >> 2) + 4 * hh + (r & 3)];
-        col += fast_exp2(acc[r] - ml.x) * ml.y;
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) { qh[ks] = nh[ks]; ql[ks] = nl[ks]; }
-    }
-    col += __shfl_xor(col, 32, 64);
-    if (hh == 0 && kvalid) colsum[((int64_t)req * Hkv + kvh) * Lctx + tab.dst[e] + tk] = col;
   }
 }
 
@@ -288,10 +352,9 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
   ReqBlocks rb;
   for (int r = 0; r <= n_req; ++r) rb.blk0[r] = req_blk0[r];
   dim3 g(nblk, Hkv), b(256);
-  const size_t lds = (pass == 1 ? 4 : 1) * (size_t)Mpad * sizeof(float2);
   const uint16_t* k = (const uint16_t*)kc;
 #define SRA_PASS(DD, PP)                                                                        \
-  k_score_pass<DD, PP><<<g, b, lds, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
+  k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
                                           entry_base, blk_base, ml_part, ml_final, fuse_merge,  \
                                           colsum)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);

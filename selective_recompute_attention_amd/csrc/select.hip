@@ -2,17 +2,19 @@
 // context token indices from the critical-layer attention distribution; ties follow a stable
 // sort by descending score, Cache-Craft CSDN article §2.2.2, so the lower index wins).
 //
-// One block of 1024 threads per selection unit (a whole request, or one chunk of a request when
+// One block of 256 threads per selection unit (a whole request, or one chunk of a request when
 // per-chunk quotas are given). The block first sums the per-KV-head partial column sums in a fixed
-// order (the scores), then finds the score of the N-th best token exactly with a 4-pass 8-bit radix
-// select over order-preserving 32-bit keys, and finally writes, in ascending position order,
-// every token above that score plus the lowest-index tokens equal to it. All decisions are integer
-// comparisons of the same float32 bits, so the result is deterministic.
+// order (the scores), then finds the score of the N-th best token exactly with an 8-bit radix
+// select over order-preserving 32-bit keys (leading bytes shared by every key are skipped), and
+// finally writes, in ascending position order, every token above that score plus the lowest-index
+// tokens equal to it. All decisions are integer comparisons of the same float32 bits, so the result
+// is deterministic.
 #include "common.h"
 
 namespace sra {
 namespace {
 
+constexpr int kSelThreads = 256;
 constexpr int kSelLdsKeys = 12288;   // keys of one selection unit kept in LDS (48 KB)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -20,90 +22,190 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix count of `flag` over the block (1024 threads = 16 waves); also the total.
-__device__ __forceinline__ int block_excl_count(bool flag, int* wsum, int& total) {
+// Exclusive prefix sum of x over the block (4 waves, in thread order); also the total.
+__device__ __forceinline__ int block_excl_sum(int x, int* wsum, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(flag);
-  const int before = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[wave] = __popcll(m);
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int off = 0, tot = 0;
-  const int nw = blockDim.x >> 6;
-  for (int w = 0; w < nw; ++w) {
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
     const int c = wsum[w];
-    off += (w < wave) ? c : 0;
+    before += (w < wave) ? c : 0;
     tot += c;
   }
   __syncthreads();
   total = tot;
-  return off + before;
+  return before + incl - x;
 }
 
-__global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lctx, int Lq, int R,
-                                                 const float* __restrict__ parts,
-                                                 float* __restrict__ scores,
-                                                 int* __restrict__ row_pos) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned sh_prefix, sh_remaining;
-  __shared__ int wsum[16];
-  __shared__ uint32_t kl[kSelLdsKeys];   // the unit's keys when they fit
+__global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, int nparts, int Lctx, int Lq, int R,
+                                                        const float* __restrict__ parts,
+                                                        float* __restrict__ scores,
+                                                        int* __restrict__ row_pos) {
+  constexpr int NW = kSelThreads / 64;
+  constexpr int KREG = 16;   // keys per thread held in registers (units up to 4096 keys)
+  __shared__ unsigned hist[4][NW][256];   // one histogram per radix pass and wave
+  __shared__ uint32_t sh_prefix, sh_remaining;
+  __shared__ uint32_t sh_and[NW], sh_or[NW];
+  __shared__ int wsum[NW];
+  __shared__ uint32_t kl[kSelLdsKeys];   // larger units' keys when they fit
   const int e = blockIdx.x;
   const int req = tab.req[e], begin = tab.begin[e], len = tab.len[e];
   const int quota = tab.quota[e], off = tab.out_off[e];
   float* srow = scores + (int64_t)req * Lctx + begin;
   int* out = row_pos + (int64_t)req * R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // thread t owns the contiguous positions [jlo, jhi): block prefix sums of per-thread counts then
+  // give ascending output slots
+  const int per = (len + kSelThreads - 1) / kSelThreads;
+  const int jlo = min((int)threadIdx.x * per, len), jhi = min(jlo + per, len), cnt = jhi - jlo;
+  const bool in_regs = len > 0 && per <= KREG;
   const bool in_lds = len <= kSelLdsKeys;
+  for (int i = threadIdx.x; i < 4 * NW * 256; i += kSelThreads) (&hist[0][0][0])[i] = 0;
 
-  // scores: per-KV-head partial column sums added in head order (loads issued 8 at a time)
+  // scores: per-KV-head partial column sums added in head order, then order-preserving keys. The
+  // loads are coalesced (position j = tid + 256 i); small units then pass their keys through LDS
+  // into this thread's contiguous range of registers.
   const float* prow = parts + (int64_t)req * nparts * Lctx + begin;
-  for (int j = threadIdx.x; j < len; j += blockDim.x) {
-    float s = 0.f;
+  uint32_t kreg[KREG];
+  uint32_t kand = ~0u, kor = 0u;
+  if (in_regs) {
+    float sv[KREG];
     if (nparts > 0) {
-      int p = 0;
-      for (; p + 8 <= nparts; p += 8) {
-        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = prow[(int64_t)(p + u) * Lctx + j];
+      for (int i = 0; i < KREG; ++i) sv[i] = 0.f;
+      for (int p0 = 0; p0 < nparts; p0 += 8) {
+        float v[KREG][8];   // clamped, unconditional loads: the whole batch is in flight at once
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
+        for (int i = 0; i < KREG; ++i)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[i][u] = (i < per) ? prow[(int64_t)min(p0 + u, nparts - 1) * Lctx +
+                                       min((int)threadIdx.x + kSelThreads * i, len - 1)] : 0.f;
+#pragma unroll
+        for (int i = 0; i < KREG; ++i)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (p0 + u < nparts) sv[i] += v[i][u];
       }
-      for (; p < nparts; ++p) s += prow[(int64_t)p * Lctx + j];
-      srow[j] = s;
     } else {
-      s = srow[j];
+#pragma unroll
+      for (int i = 0; i < KREG; ++i)
+        sv[i] = (i < per) ? srow[min((int)threadIdx.x + kSelThreads * i, len - 1)] : 0.f;
     }
-    if (in_lds) kl[j] = order_key(s);
+#pragma unroll
+    for (int i = 0; i < KREG; ++i) {
+      const int j = threadIdx.x + kSelThreads * i;
+      if (i < per && j < len) {
+        if (nparts > 0) srow[j] = sv[i];
+        kl[j] = order_key(sv[i]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KREG; ++i) {
+      kreg[i] = kl[min(jlo + i, len - 1)];
+      if (i < cnt) {
+        kand &= kreg[i];
+        kor |= kreg[i];
+      }
+    }
+  } else {
+    for (int i = 0; i < per; ++i) {
+      const int j = threadIdx.x + kSelThreads * i;
+      if (j >= len) break;
+      float sv = 0.f;
+      if (nparts > 0) {
+        for (int p0 = 0; p0 < nparts; p0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = prow[(int64_t)min(p0 + u, nparts - 1) * Lctx + j];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (p0 + u < nparts) sv += v[u];
+        }
+        srow[j] = sv;
+      } else {
+        sv = srow[j];
+      }
+      const uint32_t u = order_key(sv);
+      if (in_lds) kl[j] = u;
+      kand &= u;
+      kor |= u;
+    }
   }
+  // bits shared by every key of the unit
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kand &= __shfl_xor(kand, o, 64);
+    kor |= __shfl_xor(kor, o, 64);
+  }
+  if (lane == 0) { sh_and[wave] = kand; sh_or[wave] = kor; }
   __syncthreads();
-  // every thread reads back only keys it wrote itself or keys in LDS after the barrier
+#pragma unroll
+  for (int w = 0; w < NW; ++w) { kand &= sh_and[w]; kor |= sh_or[w]; }
+  // keys are read back after the barrier below (LDS, or global writes of this block)
   auto key_at = [&](int j) -> uint32_t { return in_lds ? kl[j] : order_key(srow[j]); };
 
-  if (quota > 0) {
+  if (quota > 0 && len > 0) {
     uint32_t thr = 0, need_eq = 0;
     if (quota < len) {
       uint32_t prefix = 0, mask = 0, remaining = (uint32_t)quota;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-        __syncthreads();
-        for (int j = threadIdx.x; j < len; j += blockDim.x) {
-          const uint32_t u = key_at(j);
-          if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      int shift = 24;
+      // a byte equal in every key is the N-th key's byte too
+      for (; shift >= 0 && (((kand ^ kor) >> shift) & 255u) == 0; shift -= 8) {
+        prefix |= kand & (255u << shift);
+        mask |= 255u << shift;
+      }
+      for (; shift >= 0; shift -= 8) {
+        unsigned* h = &hist[shift >> 3][wave][0];
+        auto count = [&](uint32_t u, bool valid) {
+          const bool match = valid && (u & mask) == prefix;
+          const uint32_t digit = (u >> shift) & 255u;
+          const unsigned long long act = __ballot(match);
+          if (act) {
+            const int leader = __ffsll(act) - 1;
+            const uint32_t d0 = __builtin_amdgcn_readlane(digit, leader);
+            if (__ballot(match && digit == d0) == act) {
+              // the whole wave agrees: one atomic instead of a queue of same-address ones
+              if (lane == leader) atomicAdd(&h[d0], (unsigned)__popcll(act));
+            } else if (match) {
+              atomicAdd(&h[digit], 1u);
+            }
+          }
+        };
+        if (in_regs) {
+#pragma unroll
+          for (int i = 0; i < KREG; ++i)
+            if (i < per) count(kreg[i], i < cnt);
+        } else {
+          for (int i = 0; i < per; ++i) count(key_at(min(jlo + i, len - 1)), i < cnt);
         }
         __syncthreads();
         if (threadIdx.x < 64) {
           // one wave scans the 256 bins from the top: lane l holds bins 255-4l .. 252-4l
-          const int lane = threadIdx.x;
           uint32_t c[4], tot = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            c[i] = hist[255 - 4 * lane - i];
-            tot += c[i];
+            const int bin = 255 - 4 * lane - i;
+            uint32_t cc = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) cc += hist[shift >> 3][w][bin];
+            c[i] = cc;
+            tot += cc;
           }
           uint32_t incl = tot;
 #pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += o;
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
           }
           uint32_t cum = incl - tot, before = 0;
           int found = -1;
@@ -117,10 +219,10 @@ __global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lct
           }
           // the lowest lane with a hit holds the highest qualifying bin
           const int first = __ffsll((unsigned long long)__ballot(found >= 0)) - 1;
-          const int b = __shfl(found, first, 64);
-          const uint32_t bef = __shfl(before, first, 64);
+          const int bsel = __builtin_amdgcn_readlane(found, first);
+          const uint32_t bef = __builtin_amdgcn_readlane(before, first);
           if (lane == 0) {
-            sh_prefix = prefix | ((uint32_t)b << shift);
+            sh_prefix = prefix | ((uint32_t)bsel << shift);
             sh_remaining = remaining - bef;
           }
         }
@@ -128,26 +230,48 @@ __global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lct
         prefix = sh_prefix;
         remaining = sh_remaining;
         mask |= 255u << shift;
-        __syncthreads();
       }
       thr = prefix;
       need_eq = remaining;
     }
-    // quota >= len: thr = 0 and need_eq = 0 take every token (all keys of real scores exceed 0)
-    int run_eq = 0, run_sel = 0;
-    for (int base = 0; base < len; base += blockDim.x) {
-      const int j = base + threadIdx.x;
-      const bool valid = j < len;
-      const uint32_t u = valid ? key_at(j) : 0u;
-      const bool gt = valid && (quota >= len || u > thr);
-      const bool eq = valid && quota < len && u == thr;
-      int tot_eq, tot_sel;
-      const int eq_rank = run_eq + block_excl_count(eq, wsum, tot_eq);
-      const bool take = gt || (eq && (uint32_t)eq_rank < need_eq);
-      const int pos = run_sel + block_excl_count(take, wsum, tot_sel);
-      if (take && pos < quota) out[off + pos] = begin + j;
-      run_eq += tot_eq;
-      run_sel += tot_sel;
+    // quota >= len: take every token
+    const bool all = quota >= len;
+    int n_gt = 0, n_eq = 0;
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < KREG; ++i)
+        if (i < cnt) {
+          n_gt += (all || kreg[i] > thr) ? 1 : 0;
+          n_eq += (!all && kreg[i] == thr) ? 1 : 0;
+        }
+    } else {
+      for (int j = jlo; j < jhi; ++j) {
+        const uint32_t u = key_at(j);
+        n_gt += (all || u > thr) ? 1 : 0;
+        n_eq += (!all && u == thr) ? 1 : 0;
+      }
+    }
+    int tot;
+    int eq_rank = block_excl_sum(n_eq, wsum, tot);
+    const int eq_take = max(0, min(n_eq, (int)need_eq - eq_rank));   // the lowest-index ties win
+    int pos = block_excl_sum(n_gt + eq_take, wsum, tot);
+    auto emit = [&](uint32_t u, int j) {
+      bool take = all || u > thr;
+      if (!all && u == thr) {
+        take = (uint32_t)eq_rank < need_eq;
+        ++eq_rank;
+      }
+      if (take) {
+        if (pos < quota) out[off + pos] = begin + j;
+        ++pos;
+      }
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < KREG; ++i)
+        if (i < cnt) emit(kreg[i], jlo + i);
+    } else {
+      for (int j = jlo; j < jhi; ++j) emit(key_at(j), j);
     }
   }
   if (tab.writes_query[e]) {
@@ -160,7 +284,7 @@ __global__ __launch_bounds__(1024) void k_select(SelTab tab, int nparts, int Lct
 hipError_t launch_select(const SelTab& tab, int nparts, int Lctx, int Lq, int R, const float* parts,
                          float* scores, int* row_pos, hipStream_t st) {
   if (tab.n == 0) return hipSuccess;
-  k_select<<<dim3(tab.n), dim3(1024), 0, st>>>(tab, nparts, Lctx, Lq, R, parts, scores, row_pos);
+  k_select<<<dim3(tab.n), dim3(kSelThreads), 0, st>>>(tab, nparts, Lctx, Lq, R, parts, scores, row_pos);
   return hipGetLastError();
 }
 

@@ -114,7 +114,7 @@ def test_score_select_host_errors():
     assert call(n_select=-1) == L.SRA_E_SHAPE
     assert call(Lq=0) == L.SRA_E_SHAPE
     assert call(ws=None) == L.SRA_E_WORKSPACE
-    assert call(wsb=need - 256) == L.SRA_E_WORKSPACE
+    assert call(wsb=256) == L.SRA_E_WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10000010)) == L.SRA_E_WORKSPACE   # not 256-byte aligned
     bad_q = (ctypes.c_int32 * 2)(65, 1)
     assert call(quota=ctypes.cast(bad_q, ctypes.POINTER(ctypes.c_int32))) == L.SRA_E_SHAPE

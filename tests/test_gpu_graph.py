@@ -1,0 +1,87 @@
+"""HIP graph capture of the whole step (anchors on a second stream, the fused layer with its own
+internal fork/join): every replay must leave exactly what eager calls leave, also when eager work
+on other inputs has run in between and overwritten the shared workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import selective_recompute_attention_amd as sra
+from workloads import make_workload, make_custom
+
+from gpu_helpers import dev, say, shape_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(w, n_select, ws=None):
+    cfg = w.cfg
+    dt = cfg.dtype
+    lay = w.layer(0)
+    n_req, n_chunks = w.chunks.shape[0], w.chunks.shape[1]
+    Lctx = int(w.chunks[0, :, 1].sum())
+    Lq = cfg.query_len
+    L, R = Lctx + Lq, n_select + Lq
+    shape = shape_of(cfg)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    ins = {k: dev(v, dt) for k, v in lay.items()}
+    ins["q_crit"], ins["k_crit"] = dev(w.q_crit, dt), dev(w.k_crit, dt)
+    outs = {
+        "k_fused": torch.empty((n_req, L, cfg.n_kv_heads, cfg.head_dim), dtype=tdt, device="cuda"),
+        "v_fused": torch.empty((n_req, L, cfg.n_kv_heads, cfg.head_dim), dtype=tdt, device="cuda"),
+        "out": torch.empty((n_req, R, cfg.n_q_heads, cfg.head_dim), dtype=tdt, device="cuda"),
+        "lse": torch.empty((n_req, R, cfg.n_q_heads), dtype=torch.float32, device="cuda"),
+        "row_pos": torch.empty((n_req, R), dtype=torch.int32, device="cuda"),
+        "scores": torch.empty((n_req, Lctx), dtype=torch.float32, device="cuda"),
+        "anchors": torch.empty((n_chunks, cfg.anchors_k), dtype=torch.int32, device="cuda"),
+    }
+    if ws is None:
+        ws = torch.empty(sra.workspace_size(shape, n_req, n_chunks, L, R, Lq), dtype=torch.uint8, device="cuda")
+    aws = torch.empty(sra.anchor_workspace_size(w.chunks[0]), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            sra.extract_anchors(shape, ins["k_crit"], w.chunks[0], cfg.anchors_k, outs["anchors"], aws)
+        sra.fused_layer(shape, chunks=w.chunks, k_store=ins["k_store"], v_store=ins["v_store"],
+                        q_fresh=ins["q_new"], k_fresh=ins["k_new"], v_fresh=ins["v_new"],
+                        row_pos=outs["row_pos"], k_fused=outs["k_fused"], v_fused=outs["v_fused"],
+                        out=outs["out"], lse=outs["lse"], ws=ws, q_crit=ins["q_crit"],
+                        k_crit_store=ins["k_crit"], n_select=n_select, scores=outs["scores"])
+        cur.wait_stream(side)
+
+    return step, outs, ws
+
+
+@pytest.mark.parametrize("which", ["mistral7b_layer", "custom_bf16"])
+def test_graph_replay_matches_eager(which):
+    if which == "mistral7b_layer":
+        w, w2 = make_workload(1), make_workload(1, seed=7)
+    else:
+        kw = dict(dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128, chunk_lens=[200, 97, 300],
+                  orig_pos=[0, 0, 50], query_len=24, n_req=1, anchors_k=4)
+        w, w2 = make_custom(seed=3, **kw), make_custom(seed=4, **kw)
+    Lctx = int(w.chunks[0, :, 1].sum())
+    N = sra.select_count(15, 100, Lctx)
+    say(f"graph replay: {which}, L_ctx={Lctx}, N={N}")
+    step, outs, ws = _setup(w, N)
+    step_other, _, _ = _setup(w2, N, ws)   # same workspace: its contents change between replays
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():   # poison every output between replays
+            (v.view(torch.int16) if v.dtype == torch.bfloat16 else v.view(torch.int32)).fill_(0x7F01 + rep)
+        step_other()              # eager work on other inputs rewrites the shared kernels' state
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert torch.equal(outs[k], ref[k]), f"replay {rep}: {k} differs from the eager result"
+        say(f"replay {rep}: all outputs equal the eager result")
