@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int KT = 64;        // keys per LDS tile (one unit)
   constexpr int KST = D + 8;    // K row stride in LDS (elements): conflict-free 16-byte reads
   constexpr int VST = KT + 4;   // V^T row stride in LDS (elements): conflict-free 8-byte reads
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VST];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KST];   // double-buffered tiles
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VST];
   __shared__ int cum[kAttnMaxTiles + 1];
   __shared__ int wsum[4];
 
@@ -201,27 +201,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
-      __syncthreads();
+    // K row-major; V transposed on the way in (word pp of a task: dims 8c+2pp in the low half
+    // and 8c+2pp+1 in the high half, four keys each)
+    auto store_tile = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
         const int uu = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(Ks + (uu / (D / 8)) * KST + 8 * (uu % (D / 8))) = kr[i];
+        *reinterpret_cast<u32x4*>(&Ks[buf][(uu / (D / 8)) * KST + 8 * (uu % (D / 8))]) = kr[i];
       }
       if (vtask) {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {  // word pp: dims 8c+2pp (low half) and 8c+2pp+1 (high half)
+        for (int pp = 0; pp < 4; ++pp) {
           u32x2 lo, hi;
           lo[0] = (vr[0][pp] & 0xffffu) | (vr[1][pp] << 16);
           lo[1] = (vr[2][pp] & 0xffffu) | (vr[3][pp] << 16);
           hi[0] = (vr[0][pp] >> 16) | (vr[1][pp] & 0xffff0000u);
           hi[1] = (vr[2][pp] >> 16) | (vr[3][pp] & 0xffff0000u);
-          *reinterpret_cast<u32x2*>(Vt + (8 * vc + 2 * pp) * VST + 4 * vkq) = lo;
-          *reinterpret_cast<u32x2*>(Vt + (8 * vc + 2 * pp + 1) * VST + 4 * vkq) = hi;
+          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp) * VST + 4 * vkq]) = lo;
+          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp + 1) * VST + 4 * vkq]) = hi;
         }
       }
-      __syncthreads();
-      if (kt0 + KT < kend) prefetch(kt0 + KT, kend);
+    };
+    // Both buffers are free here: the previous segment's loop ended with a barrier. Tile t is
+    // computed from buffer t%2 while tile t+1 is written to the other one, so one barrier per tile
+    // both publishes the next tile and retires the current one.
+    store_tile(0);
+    if (kbeg + KT < kend) prefetch(kbeg + KT, kend);
+    __syncthreads();
+    int cur = 0;
+    for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
+      const uint16_t* Kc = Ks[cur];
+      const uint16_t* Vc = Vt[cur];
 
       // S^T[key][q] for two 32-key sub-tiles
       f32x16 sc[2];
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const bf16x8 ka =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + (32 * st + l32) * KST + 16 * ks + 8 * hh));
+              as_bf16x8(*reinterpret_cast<const u32x4*>(Kc + (32 * st + l32) * KST + 16 * ks + 8 * hh));
           sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qhi[ks], sc[st], 0, 0, 0);
           sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qlo[ks], sc[st], 0, 0, 0);
         }
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             mt = fmaxf(mt, sc[st][rr]);
           }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = half_max(mt);
       const float m_new = fmaxf(m_run, mt);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all masked so far: every p is 0
       const float alpha = fast_exp2(m_run - m_use);
@@ -286,16 +296,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const uint16_t* vrow = Vt + (32 * dt + l32) * VST + 32 * st + 16 * mp + 4 * hh;
+            const uint16_t* vrow = Vc + (32 * dt + l32) * VST + 32 * st + 16 * mp + 4 * hh;
             const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
             const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
             const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pb, o[dt], 0, 0, 0);
           }
         }
+
+      if (kt0 + KT < kend) {
+        store_tile(cur ^ 1);   // its previous tile was retired by the last barrier
+        if (kt0 + 2 * KT < kend) prefetch(kt0 + 2 * KT, kend);
+      }
+      __syncthreads();
+      cur ^= 1;
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = half_sum(l_run);
     // o[dt][rr] holds dim 32*dt + 8*(rr/4) + 4*hh + rr%4 of query vector v
     if (direct) {
       if (qvalid) {

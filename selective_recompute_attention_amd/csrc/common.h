@@ -57,6 +57,23 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // of four more instructions per call.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the two 32-lane halves of a wave with v_permlane32_swap (a VALU lane swap)
+// instead of an LDS permute. With both operands x, the swap returns (x[l], x[l+32]) in lanes 0-31
+// and (x[l-32], x[l]) in lanes 32-63, so each lane sees the pair in the same order.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// The value of lane l ^ 32.
+__device__ __forceinline__ float half_partner(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // theta_i = base^(-2i/d) and the rotation angle pos * theta_i, both in float64.
 __device__ __forceinline__ double rope_theta(int i, int d, double base) {
   return pow(base, -2.0 * (double)i / (double)d);

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
 #pragma unroll
         for (int u = 0; u < MB; ++u) ml_merge(M, S, pm[u]);
       }
-      float Mo = __shfl_xor(M, 32, 64), So = __shfl_xor(S, 32, 64);
+      float Mo = half_partner(M), So = half_partner(S);
       if (hh == 1) { const float tm = M, ts = S; M = Mo; S = So; Mo = tm; So = ts; }
       ml_merge(M, S, make_float2(Mo, So));   // half 0's blocks first, then half 1's
       return (v < Mvalid && S > 0.f) ? make_float2(M, 1.f / S) : make_float2(0.f, 0.f);
@@ -284,14 +284,14 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[st][r]);
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      m = half_max(m);
       const float m_use = (m == -INFINITY) ? 0.f : m;
       float sum = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sum += fast_exp2(acc[st][r] - m_use);
-      sum += __shfl_xor(sum, 32, 64);
+      sum = half_sum(sum);
       if (hh == 0)
         ml_part[((int64_t)(blk_base + blk) * Hkv + kvh) * Mpad + 32 * qt + l32] = make_float2(m, sum);
     } else {
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
   if constexpr (PASS == 2) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const float c = col[st] + __shfl_xor(col[st], 32, 64);
+      const float c = half_sum(col[st]);
       if (hh == 0) colred[wave][32 * st + l32] = c;
     }
     __syncthreads();
