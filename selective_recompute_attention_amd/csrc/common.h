@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace sra {
 
 // Chunk/segment table passed by value as a kernel argument (no host-to-device copy).
@@ -74,13 +76,19 @@ __device__ __forceinline__ float half_partner(float x) {
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// theta_i = base^(-2i/d) and the rotation angle pos * theta_i, both in float64.
-__device__ __forceinline__ double rope_theta(int i, int d, double base) {
-  return pow(base, -2.0 * (double)i / (double)d);
+// Rotary frequencies theta_i = base^(-2i/d), i < d/2, formed once on the host in float64 and passed
+// by value; a kernel forms the angle pos * theta_i and its cos/sin in float64, rounded to float32.
+struct Theta {
+  double v[64];
+};
+inline Theta make_theta(int d, double base) {
+  Theta t;
+  for (int i = 0; i < 64; ++i) t.v[i] = i < d / 2 ? std::pow(base, -2.0 * (double)i / (double)d) : 0.0;
+  return t;
 }
-__device__ __forceinline__ float2 rope_cs(double pos, int i, int d, double base) {
+__device__ __forceinline__ float2 rope_cs(double pos, double theta) {
   double s, c;
-  sincos(pos * rope_theta(i, d, base), &s, &c);
+  sincos(pos * theta, &s, &c);
   return make_float2((float)c, (float)s);
 }
 

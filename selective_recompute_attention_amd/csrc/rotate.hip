@@ -51,66 +51,74 @@ struct Vec<float> {
   }
 };
 
-// Rotate `n_units` units of one or more rows. A unit is VW consecutive pairs of one head:
-// elements [i0, i0+VW) and [i0+H, i0+H+VW) of a D-element head vector.
-template <typename T, int D>
-__device__ __forceinline__ void rotate_rows(const T* __restrict__ src, T* __restrict__ dst,
-                                            int n_heads_total, const float2* cs, int tid,
-                                            int nthr) {
-  constexpr int H = D / 2;
-  constexpr int VW = Vec<T>::N;
-  constexpr int UPH = H / VW;  // units per head
-  const int n_units = n_heads_total * UPH;
-  for (int u = tid; u < n_units; u += nthr) {
-    const int hv = u / UPH;
-    const int i0 = (u % UPH) * VW;
-    const T* a = src + (int64_t)hv * D + i0;
-    T* o = dst + (int64_t)hv * D + i0;
-    float fa[VW], fb[VW], ra[VW], rb[VW];
-    Vec<T>::unpack(*reinterpret_cast<const u32x4*>(a), fa);
-    Vec<T>::unpack(*reinterpret_cast<const u32x4*>(a + H), fb);
-#pragma unroll
-    for (int k = 0; k < VW; ++k) {
-      const float c = cs[i0 + k].x, s = cs[i0 + k].y;
-      ra[k] = fa[k] * c - fb[k] * s;
-      rb[k] = fa[k] * s + fb[k] * c;
-    }
-    *reinterpret_cast<u32x4*>(o) = Vec<T>::pack(ra);
-    *reinterpret_cast<u32x4*>(o + H) = Vec<T>::pack(rb);
-  }
-}
-
-__device__ __forceinline__ void copy16(const void* __restrict__ src, void* __restrict__ dst,
-                                       int64_t n16, int tid, int nthr) {
-  const u32x4* s = reinterpret_cast<const u32x4*>(src);
-  u32x4* d = reinterpret_cast<u32x4*>(dst);
-  for (int64_t u = tid; u < n16; u += nthr) d[u] = s[u];
-}
-
-// One block per (chunk entry, block of rows_per_blk rows of that chunk).
+// One block per (chunk entry, block of rows_per_blk rows of that chunk). Each batch loads its V
+// chunks and K pairs (16 bytes per half) before the angles are formed, so the memory latency
+// overlaps the float64 sin/cos; then V is stored as is and K rotated (bits kept when delta = 0).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int rows_per_blk,
                                                   const T* __restrict__ ks,
                                                   const T* __restrict__ vs, T* __restrict__ kf,
-                                                  T* __restrict__ vf, int64_t L, double base) {
+                                                  T* __restrict__ vf, int64_t L, Theta th) {
   constexpr int H = D / 2;
+  constexpr int VW = Vec<T>::N;
+  constexpr int UPH = H / VW;   // K pair units per head
+  constexpr int UV = 4, UK = 2; // per thread and batch: V chunks, K pair units
   __shared__ float2 cs[H];
   const int e = find_entry(tab, blockIdx.x);
   const int t0 = (blockIdx.x - tab.blk0[e]) * rows_per_blk;
   const int nr = min(rows_per_blk, tab.len[e] - t0);
   const int delta = tab.delta[e];
-  for (int i = threadIdx.x; i < H; i += blockDim.x) cs[i] = rope_cs((double)delta, i, D, base);
-  __syncthreads();
   const int64_t row_elems = (int64_t)Hkv * D;
   const int64_t src0 = ((int64_t)tab.src[e] + t0) * row_elems;
   const int64_t dst0 = ((int64_t)tab.req[e] * L + tab.dst[e] + t0) * row_elems;
-  const int64_t n16 = (int64_t)nr * row_elems * sizeof(T) / 16;
-  copy16(vs + src0, vf + dst0, n16, threadIdx.x, blockDim.x);
-  if (delta == 0) {
-    // rotation by zero is the identity: keep the cached bits
-    copy16(ks + src0, kf + dst0, n16, threadIdx.x, blockDim.x);
-  } else {
-    rotate_rows<T, D>(ks + src0, kf + dst0, nr * Hkv, cs, threadIdx.x, blockDim.x);
+  const int64_t nV = (int64_t)nr * row_elems * (int64_t)sizeof(T) / 16;   // V 16-byte chunks
+  const int64_t nK = (int64_t)nr * Hkv * UPH;                             // K pair units
+  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vs + src0);
+  u32x4* vdst = reinterpret_cast<u32x4*>(vf + dst0);
+  bool first = true;
+  for (int64_t bv = 0, bk = 0; bv < nV || bk < nK; bv += 256 * UV, bk += 256 * UK) {
+    u32x4 v[UV], ka[UK], kb[UK];
+#pragma unroll
+    for (int i = 0; i < UV; ++i) v[i] = vsrc[min(bv + threadIdx.x + 256 * i, nV - 1)];
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int64_t u = min(bk + threadIdx.x + 256 * i, nK - 1);
+      const T* a = ks + src0 + (u / UPH) * D + (u % UPH) * VW;
+      ka[i] = *reinterpret_cast<const u32x4*>(a);
+      kb[i] = *reinterpret_cast<const u32x4*>(a + H);
+    }
+    if (first) {   // uniform: the angles once per block, while the loads are in flight
+      if (delta != 0)
+        for (int i = threadIdx.x; i < H; i += blockDim.x) cs[i] = rope_cs((double)delta, th.v[i]);
+      __syncthreads();
+      first = false;
+    }
+#pragma unroll
+    for (int i = 0; i < UV; ++i)
+      if (bv + threadIdx.x + 256 * i < nV) vdst[bv + threadIdx.x + 256 * i] = v[i];
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int64_t u = bk + threadIdx.x + 256 * i;
+      if (u >= nK) continue;
+      const int i0 = (int)(u % UPH) * VW;
+      T* o = kf + dst0 + (u / UPH) * D + i0;
+      if (delta == 0) {   // rotation by zero is the identity: keep the cached bits
+        *reinterpret_cast<u32x4*>(o) = ka[i];
+        *reinterpret_cast<u32x4*>(o + H) = kb[i];
+      } else {
+        float fa[VW], fb[VW], ra[VW], rb[VW];
+        Vec<T>::unpack(ka[i], fa);
+        Vec<T>::unpack(kb[i], fb);
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+          const float c = cs[i0 + k].x, sn = cs[i0 + k].y;
+          ra[k] = fa[k] * c - fb[k] * sn;
+          rb[k] = fa[k] * sn + fb[k] * c;
+        }
+        *reinterpret_cast<u32x4*>(o) = Vec<T>::pack(ra);
+        *reinterpret_cast<u32x4*>(o + H) = Vec<T>::pack(rb);
+      }
+    }
   }
 }
 
@@ -119,7 +127,7 @@ __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int row
 // K rotated at p, and writes the attention's query operand: every query head rotated at p, scaled
 // by log2(e)/sqrt(d) and split into bf16 hi/lo planes in the matrix-operand order of qop_index.
 // Fresh rows are compact (row r) or position-indexed (row p). Rows outside [0, L) write nothing
-// but zero query operands.
+// but zero query operands. The first batch of every part is loaded before the angles are formed.
 template <typename T, int D>
 __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
                                                  const T* __restrict__ qn, const T* __restrict__ kn,
@@ -127,42 +135,92 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
                                                  int indexed, const int* __restrict__ row_pos,
                                                  T* __restrict__ kf, T* __restrict__ vf,
                                                  float2* __restrict__ cs_out, uint16_t* __restrict__ qop,
-                                                 int qop_blocks, float scale_log2, double base) {
+                                                 int qop_blocks, float scale_log2, Theta th) {
   constexpr int H = D / 2;
   constexpr int NKS = D / 16;
+  constexpr int VW = Vec<T>::N;
+  constexpr int UPH = H / VW;
+  constexpr int NT = 128;
   __shared__ float2 cs[H];
   const int r = blockIdx.x, q = blockIdx.y;
   const int p = row_pos[(int64_t)q * R + r];
   const bool valid = p >= 0 && p < L;  // rows outside the cache are never written
-  const int srow = indexed ? p : r;
+  const int srow = valid ? (indexed ? p : r) : 0;
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t src0 = ((int64_t)q * fresh_rows + srow) * row_elems;
+  const int64_t dst0 = ((int64_t)q * L + (valid ? p : 0)) * row_elems;
+  const int nV = (int)(row_elems * (int64_t)sizeof(T) / 16), nK = Hkv * UPH;
+  const bool do_kv = valid && kn;
+  // first batch: V chunks tid, tid+128; K pair tid; query units tid, tid+128
+  u32x4 v0 = {}, v1 = {}, ka = {}, kb = {};
+  if (kn) {
+    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vn + src0);
+    v0 = vsrc[min((int)threadIdx.x, nV - 1)];
+    v1 = vsrc[min((int)threadIdx.x + NT, nV - 1)];
+    const int u = min((int)threadIdx.x, nK - 1);
+    const T* ap = kn + src0 + (u / UPH) * D + (u % UPH) * VW;
+    ka = *reinterpret_cast<const u32x4*>(ap);
+    kb = *reinterpret_cast<const u32x4*>(ap + H);
+  }
+  const int g = Hq / Hkv;
+  const int nQ = Hq * NKS;   // unit = (head, 16-dim step ks < NKS/2, half hh)
+  auto qsrc = [&](int u) { return qn + (((int64_t)q * fresh_rows + srow) * Hq + u / NKS) * D + 16 * ((u % NKS) >> 1) + 8 * (u & 1); };
+  u32x4 qx[2] = {}, qy[2] = {};
+  if constexpr (sizeof(T) == 2) {
+    if (qop) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const T* src = qsrc(min((int)threadIdx.x + NT * k, nQ - 1));
+        qx[k] = *reinterpret_cast<const u32x4*>(src);
+        qy[k] = *reinterpret_cast<const u32x4*>(src + H);
+      }
+    }
+  }
   if (valid) {
-    for (int i = threadIdx.x; i < H; i += blockDim.x) {
-      const float2 v = rope_cs((double)p, i, D, base);
-      cs[i] = v;
-      if (cs_out) cs_out[((int64_t)q * R + r) * H + i] = v;
+    for (int i = threadIdx.x; i < H; i += NT) {
+      const float2 c = rope_cs((double)p, th.v[i]);
+      cs[i] = c;
+      if (cs_out) cs_out[((int64_t)q * R + r) * H + i] = c;
     }
   }
   __syncthreads();
-  const int64_t row_elems = (int64_t)Hkv * D;
-  if (valid && kn) {
-    const int64_t src0 = ((int64_t)q * fresh_rows + srow) * row_elems;
-    const int64_t dst0 = ((int64_t)q * L + p) * row_elems;
-    copy16(vn + src0, vf + dst0, row_elems * sizeof(T) / 16, threadIdx.x, blockDim.x);
-    rotate_rows<T, D>(kn + src0, kf + dst0, Hkv, cs, threadIdx.x, blockDim.x);
+
+  auto rot_store = [&](int u, u32x4 a, u32x4 b) {   // K pair unit u of the row
+    const int i0 = (u % UPH) * VW;
+    T* o = kf + dst0 + (u / UPH) * D + i0;
+    float fa[VW], fb[VW], ra[VW], rb[VW];
+    Vec<T>::unpack(a, fa);
+    Vec<T>::unpack(b, fb);
+#pragma unroll
+    for (int k = 0; k < VW; ++k) {
+      const float c = cs[i0 + k].x, sn = cs[i0 + k].y;
+      ra[k] = fa[k] * c - fb[k] * sn;
+      rb[k] = fa[k] * sn + fb[k] * c;
+    }
+    *reinterpret_cast<u32x4*>(o) = Vec<T>::pack(ra);
+    *reinterpret_cast<u32x4*>(o + H) = Vec<T>::pack(rb);
+  };
+  if (do_kv) {
+    u32x4* vdst = reinterpret_cast<u32x4*>(vf + dst0);
+    const u32x4* vsrc = reinterpret_cast<const u32x4*>(vn + src0);
+    if ((int)threadIdx.x < nV) vdst[threadIdx.x] = v0;
+    if ((int)threadIdx.x + NT < nV) vdst[threadIdx.x + NT] = v1;
+    for (int u = threadIdx.x + 2 * NT; u < nV; u += NT) vdst[u] = vsrc[u];
+    if ((int)threadIdx.x < nK) rot_store(threadIdx.x, ka, kb);
+    for (int u = threadIdx.x + NT; u < nK; u += NT) {
+      const T* ap = kn + src0 + (u / UPH) * D + (u % UPH) * VW;
+      rot_store(u, *reinterpret_cast<const u32x4*>(ap), *reinterpret_cast<const u32x4*>(ap + H));
+    }
   }
   if constexpr (sizeof(T) == 2) {
     if (qop) {
-      // unit = (head, 16-dim step ks < NKS/2, half hh): dims 16 ks + 8 hh + s pair with + D/2
-      const int g = Hq / Hkv;
-      const int n_units = Hq * NKS;
-      for (int u = threadIdx.x; u < n_units; u += blockDim.x) {
+      auto q_store = [&](int u, u32x4 wx, u32x4 wy) {
         const int h = u / NKS, ks = (u % NKS) >> 1, hh = u & 1;
         const int d0 = 16 * ks + 8 * hh;
         float x[8], y[8];
         if (valid) {
-          const T* src = qn + (((int64_t)q * fresh_rows + srow) * Hq + h) * D + d0;
-          Vec<T>::unpack(*reinterpret_cast<const u32x4*>(src), x);
-          Vec<T>::unpack(*reinterpret_cast<const u32x4*>(src + H), y);
+          Vec<T>::unpack(wx, x);
+          Vec<T>::unpack(wy, y);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float2 c = cs[d0 + k];
@@ -189,6 +247,13 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
           *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 0, v & 31, hh, qop_blocks, NKS)) = wh;
           *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 1, v & 31, hh, qop_blocks, NKS)) = wl;
         }
+      };
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if ((int)threadIdx.x + NT * k < nQ) q_store(threadIdx.x + NT * k, qx[k], qy[k]);
+      for (int u = threadIdx.x + 2 * NT; u < nQ; u += NT) {
+        const T* src = qsrc(u);
+        q_store(u, *reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + H));
       }
     }
   }
@@ -196,12 +261,12 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
 
 template <int D>
 __global__ void k_rope_table(int R, const int* __restrict__ row_pos, float2* __restrict__ cs_out,
-                             double base) {
+                             Theta th) {
   constexpr int H = D / 2;
   const int r = blockIdx.x, q = blockIdx.y;
   const int p = row_pos[(int64_t)q * R + r];
   for (int i = threadIdx.x; i < H; i += blockDim.x)
-    cs_out[((int64_t)q * R + r) * H + i] = rope_cs((double)p, i, D, base);
+    cs_out[((int64_t)q * R + r) * H + i] = rope_cs((double)p, th.v[i]);
 }
 
 __global__ void k_check_rows(const int* __restrict__ row_pos, int n_req, int R, int L,
@@ -223,18 +288,19 @@ hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int r
   const int nblk = tab.blk0[tab.n];
   if (nblk == 0) return hipSuccess;
   dim3 g(nblk), b(256);
+  const Theta th = make_theta(D, base);
   if (dtype == 0 && D == 128)
     k_rerotate<uint16_t, 128><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const uint16_t*)ks,
-                                                (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, base);
+                                                (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, th);
   else if (dtype == 0 && D == 64)
     k_rerotate<uint16_t, 64><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const uint16_t*)ks,
-                                               (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, base);
+                                               (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, th);
   else if (dtype == 1 && D == 128)
     k_rerotate<float, 128><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const float*)ks,
-                                             (const float*)vs, (float*)kf, (float*)vf, L, base);
+                                             (const float*)vs, (float*)kf, (float*)vf, L, th);
   else
     k_rerotate<float, 64><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const float*)ks,
-                                            (const float*)vs, (float*)kf, (float*)vf, L, base);
+                                            (const float*)vs, (float*)kf, (float*)vf, L, th);
   return hipGetLastError();
 }
 
@@ -245,24 +311,25 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
                           hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(128);
+  const Theta th = make_theta(D, base);
   if (dtype == 0 && D == 128)
     k_scatter<uint16_t, 128><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const uint16_t*)qn, (const uint16_t*)kn,
                                                (const uint16_t*)vn, fresh_rows, indexed, row_pos,
                                                (uint16_t*)kf, (uint16_t*)vf, cs_out, qop, qop_blocks,
-                                               scale_log2, base);
+                                               scale_log2, th);
   else if (dtype == 0 && D == 64)
     k_scatter<uint16_t, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const uint16_t*)qn, (const uint16_t*)kn,
                                               (const uint16_t*)vn, fresh_rows, indexed, row_pos,
                                               (uint16_t*)kf, (uint16_t*)vf, cs_out, qop, qop_blocks,
-                                              scale_log2, base);
+                                              scale_log2, th);
   else if (dtype == 1 && D == 128)
     k_scatter<float, 128><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
                                             (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
-                                            (float*)vf, cs_out, nullptr, 0, scale_log2, base);
+                                            (float*)vf, cs_out, nullptr, 0, scale_log2, th);
   else
     k_scatter<float, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
                                            (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
-                                           (float*)vf, cs_out, nullptr, 0, scale_log2, base);
+                                           (float*)vf, cs_out, nullptr, 0, scale_log2, th);
   return hipGetLastError();
 }
 
@@ -270,10 +337,11 @@ hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2
                              double base, hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(64);
+  const Theta th = make_theta(D, base);
   if (D == 128)
-    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
+    k_rope_table<128><<<g, b, 0, st>>>(R, row_pos, cs_out, th);
   else
-    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, base);
+    k_rope_table<64><<<g, b, 0, st>>>(R, row_pos, cs_out, th);
   return hipGetLastError();
 }
 

@@ -33,26 +33,28 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // grid (Lq, entries): one block per (query row i, chunk entry); a thread rotates 8 pairs of one
-// head with 16-byte loads and stores.
+// head with 16-byte loads and stores. The first batch of loads goes out before the angles.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq, int Hkv, int Mpad,
                                                     int Lctx, const uint16_t* __restrict__ qc,
                                                     uint16_t* __restrict__ qrot, int64_t plane,
-                                                    int entry_base, float scale_log2, double base) {
+                                                    int entry_base, float scale_log2, Theta th) {
   constexpr int H = D / 2;
   __shared__ float2 cs[H];
   const int i = blockIdx.x, e = blockIdx.y;
   const int req = tab.req[e];
-  const double pos = (double)Lctx + (double)i - (double)tab.delta[e];
-  for (int j = threadIdx.x; j < H; j += blockDim.x) cs[j] = rope_cs(pos, j, D, base);
-  __syncthreads();
   const int g = Hq / Hkv;
   const int eg = entry_base + e;
   const uint16_t* q = qc + ((int64_t)req * Lq + i) * Hq * D;
-  for (int u = threadIdx.x; u < Hq * (H / 8); u += blockDim.x) {
+  const int nu = Hq * (H / 8);
+  const int u0 = min((int)threadIdx.x, nu - 1);
+  const u32x4 wa0 = *reinterpret_cast<const u32x4*>(q + (u0 / (H / 8)) * D + (u0 % (H / 8)) * 8);
+  const u32x4 wb0 = *reinterpret_cast<const u32x4*>(q + (u0 / (H / 8)) * D + (u0 % (H / 8)) * 8 + H);
+  const double pos = (double)Lctx + (double)i - (double)tab.delta[e];
+  for (int j = threadIdx.x; j < H; j += blockDim.x) cs[j] = rope_cs(pos, th.v[j]);
+  __syncthreads();
+  auto rotate_store = [&](int u, u32x4 wa, u32x4 wb) {
     const int h = u / (H / 8), j0 = (u % (H / 8)) * 8;
-    const u32x4 wa = *reinterpret_cast<const u32x4*>(q + h * D + j0);
-    const u32x4 wb = *reinterpret_cast<const u32x4*>(q + h * D + j0 + H);
     u32x4 hi0, hi1, lo0, lo1;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -79,6 +81,11 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
     *reinterpret_cast<u32x4*>(qrot + o + H) = hi1;
     *reinterpret_cast<u32x4*>(qrot + plane + o) = lo0;
     *reinterpret_cast<u32x4*>(qrot + plane + o + H) = lo1;
+  };
+  if ((int)threadIdx.x < nu) rotate_store(threadIdx.x, wa0, wb0);
+  for (int u = threadIdx.x + blockDim.x; u < nu; u += blockDim.x) {
+    const uint16_t* src = q + (u / (H / 8)) * D + (u % (H / 8)) * 8;
+    rotate_store(u, *reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + H));
   }
   if (i == 0) {  // zero the padding query vectors [Lq*g, Mpad) of every KV head
     const int pad = Mpad - Lq * g;
@@ -333,12 +340,13 @@ hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv
                              int entry_base, float scale_log2, double base, hipStream_t st) {
   if (tab.n == 0 || Lq == 0) return hipSuccess;
   dim3 g(Lq, tab.n), b(256);
+  const Theta th = make_theta(D, base);
   if (D == 128)
     k_score_prep<128><<<g, b, 0, st>>>(tab, Lq, Hq, Hkv, Mpad, Lctx, (const uint16_t*)qc, qrot,
-                                        plane, entry_base, scale_log2, base);
+                                        plane, entry_base, scale_log2, th);
   else
     k_score_prep<64><<<g, b, 0, st>>>(tab, Lq, Hq, Hkv, Mpad, Lctx, (const uint16_t*)qc, qrot,
-                                       plane, entry_base, scale_log2, base);
+                                       plane, entry_base, scale_log2, th);
   return hipGetLastError();
 }
 

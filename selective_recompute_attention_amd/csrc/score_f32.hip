@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ChunkTab tab, int Lq, int Hq,
                                                    const float* __restrict__ qc,
                                                    const float* __restrict__ kc,
                                                    float* __restrict__ prob, float scale_log2,
-                                                   double base) {
+                                                   Theta th) {
   constexpr int H = D / 2;
   __shared__ float qr[D];
   __shared__ float red[256];
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_score_f32(ChunkTab tab, int Lq, int Hq,
     if (tab.req[e] != req) continue;
     const double pos = (double)Lctx + (double)i - (double)tab.delta[e];
     if (threadIdx.x < H) {
-      const float2 c = rope_cs(pos, threadIdx.x, D, base);
+      const float2 c = rope_cs(pos, th.v[threadIdx.x]);
       const float a = q[threadIdx.x], b = q[threadIdx.x + H];
       qr[threadIdx.x] = a * c.x - b * c.y;
       qr[threadIdx.x + H] = a * c.y + b * c.x;
@@ -80,10 +80,11 @@ hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, i
                             int Lctx, const float* qc, const float* kc, float* prob,
                             float scale_log2, double base, hipStream_t st) {
   dim3 g(Hq * Lq, n_req), b(256);
+  const Theta th = make_theta(D, base);
   if (D == 128)
-    k_score_f32<128><<<g, b, 0, st>>>(tab_req, Lq, Hq, Hkv, Lctx, qc, kc, prob, scale_log2, base);
+    k_score_f32<128><<<g, b, 0, st>>>(tab_req, Lq, Hq, Hkv, Lctx, qc, kc, prob, scale_log2, th);
   else
-    k_score_f32<64><<<g, b, 0, st>>>(tab_req, Lq, Hq, Hkv, Lctx, qc, kc, prob, scale_log2, base);
+    k_score_f32<64><<<g, b, 0, st>>>(tab_req, Lq, Hq, Hkv, Lctx, qc, kc, prob, scale_log2, th);
   return hipGetLastError();
 }
 
