@@ -139,7 +139,7 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
     p.qrot = so; so = align256(so + (size_t)p.qrot_plane * 2 * sizeof(uint16_t));
     p.ml_part = so; so = align256(so + (size_t)p.max_blocks * Hkv * p.Mpad * sizeof(float2));
     p.ml_final = so; so = align256(so + (size_t)n_req * Hkv * p.Mpad * sizeof(float2));
-    p.colsum = so; so = align256(so + (size_t)n_req * Hkv * Lctx * sizeof(float));
+    p.colsum = so; so = align256(so + (size_t)n_req * Lctx * sizeof(unsigned long long));  // fixed-point scores
   } else {
     p.prob = so; so = align256(so + (size_t)n_req * Hq * Lq * Lctx * sizeof(float));
     p.parts = so; so = align256(so + (size_t)n_req * Lctx * sizeof(float));
@@ -238,8 +238,8 @@ int do_rerotate(const sra_shape* s, int n_req, const void* ks, const void* vs,
 
 // Selection units and launch.
 int do_select(int n_req, int Lctx, int Lq, int R, int N, const int32_t* quota, const sra_chunk* ch,
-              int n_chunks, int nparts, const float* parts, float* scores, int32_t* row_pos,
-              hipStream_t st) {
+              int n_chunks, const unsigned long long* fx, int nparts, const float* parts, float* scores,
+              int32_t* row_pos, hipStream_t st) {
   struct U { int req, begin, len, quota, off, wq; };
   std::vector<U> units;
   for (int q = 0; q < n_req; ++q) {
@@ -269,7 +269,7 @@ int do_select(int n_req, int Lctx, int Lq, int R, int N, const int32_t* quota, c
       tab.writes_query[tab.n] = u.wq;
       ++tab.n;
     }
-    hipError_t e = sra::launch_select(tab, nparts, Lctx, Lq, R, parts, scores, row_pos, st);
+    hipError_t e = sra::launch_select(tab, fx, nparts, Lctx, Lq, R, parts, scores, row_pos, st);
     if (e != hipSuccess) return hip_fail(e, "selection launch");
   }
   return SRA_OK;
@@ -314,7 +314,7 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
     uint16_t* qrot = reinterpret_cast<uint16_t*>(wsp(ws, p.qrot));
     float2* ml_part = reinterpret_cast<float2*>(wsp(ws, p.ml_part));
     float2* ml_final = reinterpret_cast<float2*>(wsp(ws, p.ml_final));
-    float* colsum = reinterpret_cast<float*>(wsp(ws, p.colsum));
+    unsigned long long* fx = reinterpret_cast<unsigned long long*>(wsp(ws, p.colsum));
     auto ents = chunk_entries(ch, n_req, n_chunks, 128);
     // per-request block ranges in the global block numbering (entries are ordered by request)
     std::vector<int> req_blk0(n_req + 1, 0);
@@ -322,7 +322,7 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
     for (int q = 0; q < n_req; ++q) req_blk0[q + 1] += req_blk0[q];
     e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int) {
       return sra::launch_score_prep(D, tab, Lq, Hq, Hkv, p.Mpad, Lctx, qc, qrot, p.qrot_plane,
-                                    first, scale_log2, s->rope_base, st);
+                                    first, scale_log2, fx, s->rope_base, st);
     });
     if (e != hipSuccess) return hip_fail(e, "score prep launch");
     // Pass 2 merges a request's (max, sum) partials itself when they are few; otherwise a wide
@@ -339,11 +339,11 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
       e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
         return sra::launch_score_pass(pass, D, tab, req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, Lctx, kc,
                                       qrot, p.qrot_plane, first, blk_base, ml_part, ml_final, fuse_merge,
-                                      colsum, st);
+                                      fx, st);
       });
       if (e != hipSuccess) return hip_fail(e, pass == 1 ? "score pass 1 launch" : "score pass 2 launch");
     }
-    return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, Hkv, colsum, sc, row_pos, st);
+    return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, fx, 0, nullptr, sc, row_pos, st);
   }
   // float32 storage: one softmax row per query vector, then fixed-order column sums
   auto ents = chunk_entries(ch, n_req, n_chunks, 1);
@@ -364,7 +364,7 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
   if (e != hipSuccess) return hip_fail(e, "f32 score launch");
   e = sra::launch_colsum_f32(n_req, Hq * Lq, Lctx, prob, parts, st);
   if (e != hipSuccess) return hip_fail(e, "f32 column-sum launch");
-  return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, 1, parts, sc, row_pos, st);
+  return do_select(n_req, Lctx, Lq, R, N, quota, ch, n_chunks, nullptr, 1, parts, sc, row_pos, st);
 }
 
 // S4 on rows whose per-row inputs are ready: the prepared query operand (bf16) or the angle
@@ -548,7 +548,7 @@ int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t
     if (Lctx != ctx_len) return fail(SRA_E_CHUNKS, "chunks cover %d positions, ctx_len is %d", Lctx, ctx_len);
   }
   if ((rc = resolve_count(n_req, n_chunks, chunks, ctx_len, n_select, chunk_quota, &N))) return rc;
-  if ((rc = do_select(n_req, ctx_len, Lq, N + Lq, N, chunk_quota, chunks, n_chunks, 0, nullptr,
+  if ((rc = do_select(n_req, ctx_len, Lq, N + Lq, N, chunk_quota, chunks, n_chunks, nullptr, 0, nullptr,
                       const_cast<float*>(scores), row_pos, stream)))
     return rc;
   return ok();

@@ -141,14 +141,18 @@ hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2
                              double base, hipStream_t st);
 hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
                           double* ss, int32_t* anchors, float* norms, hipStream_t st);
+// Critical-layer scores are accumulated over KV heads as 64-bit fixed point (kScoreFixScale units):
+// integer additions are exact and associative, so the total does not depend on their order.
+constexpr double kScoreFixScale = 1099511627776.0;   // 2^40
 hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv, int Mpad,
                              int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
-                             int entry_base, float scale_log2, double base, hipStream_t st);
+                             int entry_base, float scale_log2, unsigned long long* fx, double base,
+                             hipStream_t st);
 hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
-                             float* colsum, hipStream_t st);
+                             unsigned long long* fx, hipStream_t st);
 hipError_t launch_score_merge(const int* req_blk0, int n_req, int Hkv, int Mpad, int Mvalid,
                               const float2* ml_part, float2* ml_final, hipStream_t st);
 hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,
@@ -156,8 +160,10 @@ hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, i
                             float scale_log2, double base, hipStream_t st);
 hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, float* parts,
                              hipStream_t st);
-hipError_t launch_select(const SelTab& tab, int nparts, int Lctx, int Lq, int R, const float* parts,
-                         float* scores, int* row_pos, hipStream_t st);
+// Scores come from fixed-point totals (fx), from nparts float partials added in order, or (both
+// absent) from `scores` itself.
+hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
+                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st);
 // qop: prepared query operand (qop_blocks blocks of 32 vectors per group); tilecum: [n_req][tiles+1]
 // ints; part_o / part_ml: [n_groups][pieces][2][128] partial results.
 hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,

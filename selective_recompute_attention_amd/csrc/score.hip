@@ -14,9 +14,9 @@
 //   pass 1 : per 128-key block, per query vector, the block's (max, sum of exp2) of the logits.
 //   merge  : per query vector, (max, 1/sum) over all blocks of its request in block order -- inside
 //            pass 2 when a request's partials are small, else as its own wide kernel.
-//   pass 2 : per key, the sum over its KV head's query vectors of exp2(logit - max) / sum, written
-//            per KV head; the selection kernel adds the KV heads in order.
-// Every reduction has a fixed order and there are no float atomics: runs are bit-reproducible.
+//   pass 2 : per key, the sum over its KV head's query vectors of exp2(logit - max) / sum, added
+//            over KV heads as 64-bit fixed point (integer atomics: exact, order-free).
+// Every float reduction has a fixed order and there are no float atomics: runs are bit-reproducible.
 // Cross-block results only meet at kernel boundaries (no device-scope fences, which on this GPU
 // write back the L2).
 #include <float.h>
@@ -38,7 +38,8 @@ template <int D>
 __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq, int Hkv, int Mpad,
                                                     int Lctx, const uint16_t* __restrict__ qc,
                                                     uint16_t* __restrict__ qrot, int64_t plane,
-                                                    int entry_base, float scale_log2, Theta th) {
+                                                    int entry_base, float scale_log2,
+                                                    unsigned long long* __restrict__ fx, Theta th) {
   constexpr int H = D / 2;
   __shared__ float2 cs[H];
   const int i = blockIdx.x, e = blockIdx.y;
@@ -86,6 +87,10 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
   for (int u = threadIdx.x + blockDim.x; u < nu; u += blockDim.x) {
     const uint16_t* src = q + (u / (H / 8)) * D + (u % (H / 8)) * 8;
     rotate_store(u, *reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + H));
+  }
+  if (i == 0 && fx) {  // clear this chunk's score accumulators (pass 2 adds into them)
+    unsigned long long* f = fx + (int64_t)req * Lctx + tab.dst[e];
+    for (int t = threadIdx.x; t < tab.len[e]; t += blockDim.x) f[t] = 0ull;
   }
   if (i == 0) {  // zero the padding query vectors [Lq*g, Mpad) of every KV head
     const int pad = Mpad - Lq * g;
@@ -172,8 +177,8 @@ __device__ __forceinline__ void load_q(const uint16_t* qp, int64_t plane, bf16x8
 // issued before any of them is waited on, so each block pays about one memory latency.
 // PASS 1 writes ml_part[blk][kvh][v] = (max, sum exp2(y - max)) over the block's keys (S^T = K Q^T:
 // one query vector per lane column, its 128 keys across the registers of both half-waves).
-// PASS 2 writes colsum[req][kvh][j] = sum_v exp2(y - M_v) * invS_v (S = Q K^T: one key per lane
-// column), the four waves' sums added in wave order.
+// PASS 2 adds sum_v exp2(y - M_v) * invS_v of its KV head to the key's fixed-point score (S = Q K^T:
+// one key per lane column), the four waves' sums added in wave order first.
 template <int D, int PASS>
 __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, int Hkv, int Mpad,
                                                     int Mvalid, int Lctx,
@@ -182,7 +187,8 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
                                                     int64_t plane, int entry_base, int blk_base,
                                                     float2* __restrict__ ml_part,
                                                     const float2* __restrict__ ml_final,
-                                                    int fuse_merge, float* __restrict__ colsum) {
+                                                    int fuse_merge,
+                                                    unsigned long long* __restrict__ fx) {
   constexpr int NKS = D / 16;
   constexpr int KB = 128;          // keys per block
   constexpr int KST = D + 8;       // LDS row stride (elements)
@@ -328,7 +334,11 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
     if (threadIdx.x < nk) {
       const int j = threadIdx.x;
       const float c = ((colred[0][j] + colred[1][j]) + colred[2][j]) + colred[3][j];
-      colsum[((int64_t)req * Hkv + kvh) * Lctx + tab.dst[e] + t0 + j] = c;
+      // this KV head's share of the score, added in fixed point (c >= 0). System scope: the add is
+      // performed past the per-XCD L2s, where the blocks of every KV head meet.
+      __hip_atomic_fetch_add(fx + (int64_t)req * Lctx + tab.dst[e] + t0 + j,
+                             (unsigned long long)__double2ll_rn((double)c * kScoreFixScale),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }
@@ -337,16 +347,17 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
 
 hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv, int Mpad,
                              int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
-                             int entry_base, float scale_log2, double base, hipStream_t st) {
+                             int entry_base, float scale_log2, unsigned long long* fx, double base,
+                             hipStream_t st) {
   if (tab.n == 0 || Lq == 0) return hipSuccess;
   dim3 g(Lq, tab.n), b(256);
   const Theta th = make_theta(D, base);
   if (D == 128)
     k_score_prep<128><<<g, b, 0, st>>>(tab, Lq, Hq, Hkv, Mpad, Lctx, (const uint16_t*)qc, qrot,
-                                        plane, entry_base, scale_log2, th);
+                                        plane, entry_base, scale_log2, fx, th);
   else
     k_score_prep<64><<<g, b, 0, st>>>(tab, Lq, Hq, Hkv, Mpad, Lctx, (const uint16_t*)qc, qrot,
-                                       plane, entry_base, scale_log2, th);
+                                       plane, entry_base, scale_log2, fx, th);
   return hipGetLastError();
 }
 
@@ -354,7 +365,7 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
-                             float* colsum, hipStream_t st) {
+                             unsigned long long* fx, hipStream_t st) {
   const int nblk = tab.blk0[tab.n];
   if (nblk == 0) return hipSuccess;
   ReqBlocks rb;
@@ -364,7 +375,7 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
 #define SRA_PASS(DD, PP)                                                                        \
   k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
                                           entry_base, blk_base, ml_part, ml_final, fuse_merge,  \
-                                          colsum)
+                                          fx)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);
   else if (D == 128) SRA_PASS(128, 2);
   else if (pass == 1) SRA_PASS(64, 1);

@@ -3,8 +3,8 @@
 // sort by descending score, Cache-Craft CSDN article §2.2.2, so the lower index wins).
 //
 // One block of 256 threads per selection unit (a whole request, or one chunk of a request when
-// per-chunk quotas are given). The block first sums the per-KV-head partial column sums in a fixed
-// order (the scores), then finds the score of the N-th best token exactly with an 8-bit radix
+// per-chunk quotas are given). The block first forms the scores (fixed-point totals over KV heads,
+// or per-head float partials added in a fixed order), then finds the score of the N-th best token exactly with an 8-bit radix
 // select over order-preserving 32-bit keys (leading bytes shared by every key are skipped), and
 // finally writes, in ascending position order, every token above that score plus the lowest-index
 // tokens equal to it. All decisions are integer comparisons of the same float32 bits, so the result
@@ -45,7 +45,8 @@ __device__ __forceinline__ int block_excl_sum(int x, int* wsum, int& total) {
   return before + incl - x;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, int nparts, int Lctx, int Lq, int R,
+__global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsigned long long* __restrict__ fx,
+                                                        int nparts, int Lctx, int Lq, int R,
                                                         const float* __restrict__ parts,
                                                         float* __restrict__ scores,
                                                         int* __restrict__ row_pos) {
@@ -78,7 +79,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, int nparts, 
   uint32_t kand = ~0u, kor = 0u;
   if (in_regs) {
     float sv[KREG];
-    if (nparts > 0) {
+    if (fx) {
+      const unsigned long long* frow = fx + (int64_t)req * Lctx + begin;
+      unsigned long long fv[KREG];   // one batch of independent loads
+#pragma unroll
+      for (int i = 0; i < KREG; ++i) fv[i] = frow[min((int)threadIdx.x + kSelThreads * i, len - 1)];
+#pragma unroll
+      for (int i = 0; i < KREG; ++i) sv[i] = (float)((double)fv[i] * (1.0 / kScoreFixScale));
+    } else if (nparts > 0) {
 #pragma unroll
       for (int i = 0; i < KREG; ++i) sv[i] = 0.f;
       for (int p0 = 0; p0 < nparts; p0 += 8) {
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, int nparts, 
     for (int i = 0; i < KREG; ++i) {
       const int j = threadIdx.x + kSelThreads * i;
       if (i < per && j < len) {
-        if (nparts > 0) srow[j] = sv[i];
+        if (fx || nparts > 0) srow[j] = sv[i];
         kl[j] = order_key(sv[i]);
       }
     }
@@ -122,7 +130,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, int nparts, 
       const int j = threadIdx.x + kSelThreads * i;
       if (j >= len) break;
       float sv = 0.f;
-      if (nparts > 0) {
+      if (fx) {
+        sv = (float)((double)fx[(int64_t)req * Lctx + begin + j] * (1.0 / kScoreFixScale));
+        srow[j] = sv;
+      } else if (nparts > 0) {
         for (int p0 = 0; p0 < nparts; p0 += 8) {
           float v[8];
 #pragma unroll
@@ -281,10 +292,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, int nparts, 
 
 }  // namespace
 
-hipError_t launch_select(const SelTab& tab, int nparts, int Lctx, int Lq, int R, const float* parts,
-                         float* scores, int* row_pos, hipStream_t st) {
+hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
+                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st) {
   if (tab.n == 0) return hipSuccess;
-  k_select<<<dim3(tab.n), dim3(kSelThreads), 0, st>>>(tab, nparts, Lctx, Lq, R, parts, scores, row_pos);
+  k_select<<<dim3(tab.n), dim3(kSelThreads), 0, st>>>(tab, fx, nparts, Lctx, Lq, R, parts, scores, row_pos);
   return hipGetLastError();
 }
 
