@@ -1,9 +1,8 @@
 """Benchmark of the per-layer KV-cache fusion step on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input: key-norm anchors of
-the critical layer's chunks, then the fused layer call (re-rotation, critical-layer scoring and
-top-N selection, scatter of fresh K/V, sparse causal attention), eager calls on one stream. The
-workload is the Mistral-7B-shaped layer (32 Q / 8 KV heads, head_dim 128, 5 chunks x 512 tokens + 32-token query,
+One step = one pass of the whole hot path over one batch of synthetic input: one fused layer call
+(re-rotation, critical-layer scoring with the chunks' key-norm anchors and top-N selection, scatter
+of fresh K/V, sparse causal attention) on one stream. The workload is the Mistral-7B-shaped layer (32 Q / 8 KV heads, head_dim 128, 5 chunks x 512 tokens + 32-token query,
 15% of the context recomputed), seeded synthetic data.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu]
@@ -171,27 +170,22 @@ def main():
             "lse": torch.empty((1, R, Hq), dtype=torch.float32, device="cuda"),
             "row_pos": torch.empty((1, R), dtype=torch.int32, device="cuda"),
             "scores": torch.empty((1, Lctx), dtype=torch.float32, device="cuda"),
-            "anchors": torch.empty((n_chunks, cfg.anchors_k), dtype=torch.int32, device="cuda"),
+            "anchors": torch.empty((1, n_chunks, cfg.anchors_k), dtype=torch.int32, device="cuda"),
         }
         reps.append((ins, outs))
     ws = torch.empty(sra.workspace_size(shape, 1, n_chunks, L, R, Lq), dtype=torch.uint8, device="cuda")
-    anchor_ws = torch.empty(sra.anchor_workspace_size(w.chunks[0]), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     hip = Hip()
     sp = ctypes.c_void_p(stream.cuda_stream)
 
-    def step(i, events=None, anchor_ev=None):
+    def step(i, events=None):
         ins, outs = reps[i % len(reps)]
-        if anchor_ev is not None:
-            hip.record(anchor_ev[0], sp)
-        sra.extract_anchors(shape, ins["k_crit"], w.chunks[0], cfg.anchors_k, outs["anchors"], anchor_ws)
-        if anchor_ev is not None:
-            hip.record(anchor_ev[1], sp)
         sra.fused_layer(shape, chunks=w.chunks, k_store=ins["k_store"], v_store=ins["v_store"],
                         q_fresh=ins["q_new"], k_fresh=ins["k_new"], v_fresh=ins["v_new"],
                         row_pos=outs["row_pos"], k_fused=outs["k_fused"], v_fused=outs["v_fused"],
                         out=outs["out"], lse=outs["lse"], ws=ws, q_crit=ins["q_crit"],
-                        k_crit_store=ins["k_crit"], n_select=N, scores=outs["scores"], stage_events=events)
+                        k_crit_store=ins["k_crit"], n_select=N, scores=outs["scores"],
+                        anchors_k=cfg.anchors_k, anchor_rows=outs["anchors"], stage_events=events)
 
     for i in range(args.warmup):
         step(i)
@@ -205,17 +199,15 @@ def main():
     # Per-stage durations from HIP events recorded by the library on this stream (separate pass).
     n_ev = args.steps
     ev = [(ctypes.c_void_p * 8)(*[hip.event() for _ in range(8)]) for _ in range(n_ev)]
-    aev = [(hip.event(), hip.event()) for _ in range(n_ev)]
     # a spin kernel first, so that every step of this pass is queued before the GPU reaches it and
     # no stage waits for the host between its kernels
     torch.cuda._sleep(int(4e7))
     for i in range(n_ev):
-        step(i, ev[i], aev[i])
+        step(i, ev[i])
     torch.cuda.synchronize()
     names = ["rerotate", "score_select", "scatter", "attention"]
     stage_ms = {n: float(np.mean([hip.elapsed_ms(ctypes.c_void_p(ev[i][2 * s]), ctypes.c_void_p(ev[i][2 * s + 1]))
                                   for i in range(n_ev)])) for s, n in enumerate(names)}
-    stage_ms["anchors"] = float(np.mean([hip.elapsed_ms(a, b) for a, b in aev]))
 
     # algorithmic work (realised row positions)
     rp = reps[0][1]["row_pos"].cpu().numpy()[0].astype(np.int64)
@@ -225,7 +217,6 @@ def main():
     s2_bytes = kv_row_bytes * Lctx                      # critical layer's K once
     s2_flops = 2.0 * Lq * Hq * D * Lctx
     s3_bytes = 4 * kv_row_bytes * R
-    anchors_bytes = kv_row_bytes * Lctx
     t_attn = stage_ms["attention"] * 1e-3
     achieved = attn_flops / t_attn / 1e12
     rs_t = (stage_ms["rerotate"] + stage_ms["score_select"]) * 1e-3
@@ -254,7 +245,6 @@ def main():
         "rerotate_score_hbm_gbs": (s1_bytes + s2_bytes) / rs_t / 1e9,
         "rerotate_hbm_gbs": s1_bytes / (stage_ms["rerotate"] * 1e-3) / 1e9,
         "scatter_hbm_gbs": s3_bytes / (stage_ms["scatter"] * 1e-3) / 1e9,
-        "anchors_hbm_gbs": anchors_bytes / (stage_ms["anchors"] * 1e-3) / 1e9,
         "score_flops_tflops": s2_flops / (stage_ms["score_select"] * 1e-3) / 1e12,
     }
     if not args.no_cpu:

@@ -109,6 +109,12 @@ typedef struct {
     int32_t n_select;              /* N per request (ignored when chunk_quota is given)      */
     const int32_t* chunk_quota;    /* host [n_req][n_chunks] per-chunk N_c, or NULL          */
     float* scores;                 /* out [n_req][L_ctx] (may be NULL)                       */
+    /* S2a (optional, needs q_crit): key-norm anchors of every (request, chunk), taken from the
+     * same critical-layer K rows as the scoring; same order and results as sra_extract_anchors
+     * (chunks of one request: anchor_rows[q][c]). 0 < anchors_k <= n_tokens of every chunk. */
+    int32_t anchors_k;             /* anchors per chunk, 0 = none                            */
+    int32_t* anchor_rows;          /* out [n_req][n_chunks][anchors_k] token offsets         */
+    float* anchor_norms;           /* out [crit_store_rows] key norms at the chunks' rows, or NULL */
     /* fresh projections of every position (position-indexed, before rotary embedding) */
     const void* q_fresh;           /* [n_req][L][Hq][d]                                      */
     const void* k_fresh;           /* [n_req][L][Hkv][d]                                     */

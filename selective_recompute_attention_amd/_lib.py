@@ -41,6 +41,7 @@ class LayerArgs(ctypes.Structure):
         ("q_crit", ctypes.c_void_p), ("k_crit_store", ctypes.c_void_p), ("crit_store_rows", ctypes.c_int64),
         ("n_select", ctypes.c_int32), ("chunk_quota", ctypes.POINTER(ctypes.c_int32)),
         ("scores", ctypes.c_void_p),
+        ("anchors_k", ctypes.c_int32), ("anchor_rows", ctypes.c_void_p), ("anchor_norms", ctypes.c_void_p),
         ("q_fresh", ctypes.c_void_p), ("k_fresh", ctypes.c_void_p), ("v_fresh", ctypes.c_void_p),
         ("row_pos", ctypes.c_void_p), ("n_rows", ctypes.c_int32),
         ("k_fused", ctypes.c_void_p), ("v_fused", ctypes.c_void_p),

@@ -126,8 +126,10 @@ def sparse_causal_attn(shape, q_new, row_pos, k_fused, v_fused, out, lse, ws, st
 
 def fused_layer(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, row_pos, k_fused, v_fused,
                 out, ws, lse=None, q_crit=None, k_crit_store=None, n_select=None, quotas=None, scores=None,
-                stage_events=None, stream=None):
-    """stage_events: optional ctypes array of 8 hipEvent_t handles (see sra_layer_args)."""
+                anchors_k=0, anchor_rows=None, anchor_norms=None, stage_events=None, stream=None):
+    """stage_events: optional ctypes array of 8 hipEvent_t handles (see sra_layer_args).
+    anchors_k > 0 also extracts key-norm anchors of every (request, chunk) into anchor_rows
+    [n_req][n_chunks][anchors_k] (int32) and, when given, anchor_norms [crit_store_rows] (float32)."""
     ch = np.asarray(chunks, dtype=np.int32)
     n_req, n_chunks = ch.shape[0], ch.shape[1]
     carr = chunk_array(ch)
@@ -145,6 +147,7 @@ def fused_layer(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, r
     a.n_select = -1 if n_select is None else int(n_select)
     a.chunk_quota = qp
     a.scores = _ptr(scores)
+    a.anchors_k, a.anchor_rows, a.anchor_norms = int(anchors_k), _ptr(anchor_rows), _ptr(anchor_norms)
     a.q_fresh, a.k_fresh, a.v_fresh = _ptr(q_fresh), _ptr(k_fresh), _ptr(v_fresh)
     a.row_pos, a.n_rows = _ptr(row_pos), row_pos.shape[1]
     a.k_fused, a.v_fused, a.out, a.lse = _ptr(k_fused), _ptr(v_fused), _ptr(out), _ptr(lse)

@@ -2,10 +2,9 @@
 // lightweight query probing: offline, each chunk keeps the few tokens with the largest key norm
 // as a compressed semantic summary).
 //
-// Two launches, both wide: (1) one wave per token row reduces the squares of its key (all KV heads
-// and dims) in float64 -- squares of bf16/f32 values are exact there, so the ranking matches an
-// exact computation up to the last float64 bit -- into the workspace; (2) one wave per chunk picks
-// the k largest in the order (larger norm first, lower token offset on a tie).
+// Two launches, both wide: (1) the squares of every token's key (all KV heads and dims) summed in
+// float64 -- squares of bf16/f32 values are exact there -- into the workspace; (2) one wave per chunk
+// picks the k largest in the order (larger norm first, lower token offset on a tie).
 #include <float.h>
 
 #include "common.h"
@@ -15,50 +14,42 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
-__device__ __forceinline__ double sumsq16(u32x4 v);
-template <>
-__device__ __forceinline__ double sumsq16<uint16_t>(u32x4 v) {
-  double acc = 0.0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const double a = __uint_as_float(v[k] << 16), b = __uint_as_float(v[k] & 0xffff0000u);
-    acc += a * a;
-    acc += b * b;
-  }
-  return acc;
-}
-template <>
-__device__ __forceinline__ double sumsq16<float>(u32x4 v) {
-  double acc = 0.0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const double a = __uint_as_float(v[k]);
-    acc += a * a;
-  }
-  return acc;
-}
-
-// Table use: entry e = one chunk; src/len its store rows; dst its output slot; delta its offset in
-// the sum-of-squares workspace. blk0 counts blocks of 4 rows (one wave per row).
-template <typename T>
-__global__ __launch_bounds__(256) void k_row_sumsq(ChunkTab tab, int row_elems,
+// Table use: entry e = one chunk; src/len its store rows; dst its output slot; delta the offset of
+// its sums of squares in the workspace. One thread per (row, KV head) sums that head's d squares in
+// order (float64); the row's thread then adds the heads in order. The scoring pass forms the same
+// per-head sums from its LDS tile, so fused and standalone anchors agree bit for bit.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_row_sumsq(ChunkTab tab, int Hkv,
                                                    const T* __restrict__ ks,
                                                    double* __restrict__ ss,
                                                    float* __restrict__ norms) {
+  constexpr int NC = D * (int)sizeof(T) / 16;   // 16-byte pieces of one head
+  __shared__ double part[256];
   const int e = find_entry(tab, blockIdx.x);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = (blockIdx.x - tab.blk0[e]) * 4 + wave;
-  if (t >= tab.len[e]) return;
-  const int64_t row = (int64_t)tab.src[e] + t;
-  const u32x4* p = reinterpret_cast<const u32x4*>(ks + row * row_elems);
-  const int n16 = row_elems * (int)sizeof(T) / 16;
+  const int rpb = anchor_rows_per_block(Hkv);
+  const int rl = threadIdx.x / Hkv, h = threadIdx.x % Hkv;
+  const int t0 = (blockIdx.x - tab.blk0[e]) * rpb;
+  const int t = t0 + rl;
+  const bool active = rl < rpb && t < tab.len[e];
+  const u32x4* p = reinterpret_cast<const u32x4*>(
+      ks + (((int64_t)tab.src[e] + (active ? t : 0)) * Hkv + (active ? h : 0)) * D);
+  u32x4 w[NC];   // one batch of loads
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = p[c];
   double acc = 0.0;
-  for (int u = lane; u < n16; u += 64) acc += sumsq16<T>(p[u]);
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, 64);  // fixed-order tree
-  if (lane == 0) {
-    ss[tab.delta[e] + t] = acc;
-    if (norms) norms[row] = (float)sqrt(acc);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t x[4] = {w[c][0], w[c][1], w[c][2], w[c][3]};
+    acc = sumsq16<T>(acc, x);
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  if ((int)threadIdx.x < rpb && t0 + (int)threadIdx.x < tab.len[e]) {
+    double tot = 0.0;
+    for (int hh = 0; hh < Hkv; ++hh) tot += part[threadIdx.x * Hkv + hh];
+    const int tt = t0 + threadIdx.x;
+    ss[tab.delta[e] + tt] = tot;
+    if (norms) norms[(int64_t)tab.src[e] + tt] = (float)sqrt(tot);
   }
 }
 
@@ -116,15 +107,15 @@ __global__ __launch_bounds__(256) void k_anchor_topk(ChunkTab tab, int k, const 
 
 }  // namespace
 
-hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
+hipError_t launch_anchors(int dtype, int Hkv, int D, const ChunkTab& tab, int k, const void* ks,
                           double* ss, int32_t* anchors, float* norms, hipStream_t st) {
-  // tab.blk0 counts blocks of 4 rows per chunk
   if (tab.n == 0) return hipSuccess;
   const int nblk = tab.blk0[tab.n];
-  if (dtype == 0)
-    k_row_sumsq<uint16_t><<<dim3(nblk), dim3(256), 0, st>>>(tab, row_elems, (const uint16_t*)ks, ss, norms);
-  else
-    k_row_sumsq<float><<<dim3(nblk), dim3(256), 0, st>>>(tab, row_elems, (const float*)ks, ss, norms);
+  const dim3 g(nblk), b(256);
+  if (dtype == 0 && D == 128) k_row_sumsq<uint16_t, 128><<<g, b, 0, st>>>(tab, Hkv, (const uint16_t*)ks, ss, norms);
+  else if (dtype == 0) k_row_sumsq<uint16_t, 64><<<g, b, 0, st>>>(tab, Hkv, (const uint16_t*)ks, ss, norms);
+  else if (D == 128) k_row_sumsq<float, 128><<<g, b, 0, st>>>(tab, Hkv, (const float*)ks, ss, norms);
+  else k_row_sumsq<float, 64><<<g, b, 0, st>>>(tab, Hkv, (const float*)ks, ss, norms);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   k_anchor_topk<<<dim3((tab.n + 3) / 4), dim3(256), 0, st>>>(tab, k, ss, anchors);

@@ -112,7 +112,7 @@ struct Plan {
   // score (bf16)
   int Mpad = 0;
   int64_t max_blocks = 0;
-  size_t qrot = 0, ml_part = 0, ml_final = 0, colsum = 0, scores_tmp = 0;
+  size_t qrot = 0, ml_part = 0, ml_final = 0, colsum = 0, scores_tmp = 0, ssp = 0;
   int64_t qrot_plane = 0;  // elements per hi/lo plane
   // score (f32)
   size_t prob = 0, parts = 0;
@@ -145,6 +145,8 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
     p.parts = so; so = align256(so + (size_t)n_req * Lctx * sizeof(float));
   }
   p.scores_tmp = so; so = align256(so + (size_t)n_req * Lctx * sizeof(float));
+  // anchors: per-head float64 sums of squares of the critical layer's keys
+  p.ssp = so; so = align256(so + (size_t)Hkv * n_req * Lctx * sizeof(double));
   p.score_end = so;
   // attention region (same start: scoring is finished before the scatter writes it)
   size_t ao = off;
@@ -178,6 +180,7 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 // ------------------------------------------------------------------------------ table packing
 struct Entry {
   int req, src, len, dst, delta, blocks;
+  int c = 0;   // chunk index within the request
 };
 
 // Pack entries into launch-sized tables; calls fn(tab, first_entry_index, first_block_index).
@@ -197,6 +200,7 @@ hipError_t for_each_tab(const std::vector<Entry>& ents, Fn fn) {
       tab.len[tab.n] = e.len;
       tab.dst[tab.n] = e.dst;
       tab.delta[tab.n] = e.delta;
+      tab.aux[tab.n] = e.c;
       tab.blk0[tab.n] = blk;
       blk += e.blocks;
       ++tab.n;
@@ -217,7 +221,7 @@ std::vector<Entry> chunk_entries(const sra_chunk* ch, int n_req, int n_chunks, i
       const sra_chunk& k = ch[(int64_t)q * n_chunks + c];
       if (k.n_tokens == 0) continue;
       v.push_back({q, k.src_row, k.n_tokens, k.dst_row, k.dst_row - k.orig_pos,
-                   (int)ceil_div(k.n_tokens, rows_per_blk)});
+                   (int)ceil_div(k.n_tokens, rows_per_blk), c});
     }
   return v;
 }
@@ -304,7 +308,8 @@ int resolve_count(int n_req, int n_chunks, const sra_chunk* ch, int Lctx, int n_
 
 int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const void* kc,
                     const sra_chunk* ch, int n_chunks, int Lctx, int N, const int32_t* quota,
-                    float* scores, int32_t* row_pos, void* ws, const Plan& p, hipStream_t st) {
+                    float* scores, int32_t* row_pos, void* ws, const Plan& p, hipStream_t st,
+                    const sra::AnchorOut& anc = sra::AnchorOut()) {
   const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads, g = Hq / Hkv;
   const int R = N + Lq;
   float* sc = scores ? scores : reinterpret_cast<float*>(wsp(ws, p.scores_tmp));
@@ -339,7 +344,7 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
       e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
         return sra::launch_score_pass(pass, D, tab, req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, Lctx, kc,
                                       qrot, p.qrot_plane, first, blk_base, ml_part, ml_final, fuse_merge,
-                                      fx, st);
+                                      fx, anc, st);
       });
       if (e != hipSuccess) return hip_fail(e, pass == 1 ? "score pass 1 launch" : "score pass 2 launch");
     }
@@ -398,7 +403,11 @@ int check_attn_limits(const sra_shape* s, int R, int L) {
       ceil_div((int64_t)R * (s->n_q_heads / s->n_kv_heads), 128) > sra::kAttnMaxTiles)
     return fail(SRA_E_LIMIT, "bf16 attention supports at most %d query vectors per KV head and request",
                 sra::kAttnMaxTiles * 128);
-  (void)L;
+  // the bf16 kernel addresses one request's K/V rows and output rows with 32-bit offsets
+  if (s->dtype == SRA_DTYPE_BF16 && (int64_t)L * s->n_kv_heads * s->head_dim * 2 > (int64_t)UINT32_MAX)
+    return fail(SRA_E_LIMIT, "bf16 attention: one request's fused K or V exceeds 4 GiB");
+  if (s->dtype == SRA_DTYPE_BF16 && (int64_t)R * s->n_q_heads * s->head_dim > (int64_t)INT32_MAX)
+    return fail(SRA_E_LIMIT, "bf16 attention: one request's output exceeds 2^31 elements");
   return SRA_OK;
 }
 
@@ -490,6 +499,8 @@ int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t sto
   if (n_chunks <= 0) return fail(SRA_E_SHAPE, "n_chunks must be positive");
   if (k < 1) return fail(SRA_E_SHAPE, "k must be >= 1");
   if (k > SRA_MAX_ANCHOR_K) return fail(SRA_E_LIMIT, "k = %d exceeds %d", k, SRA_MAX_ANCHOR_K);
+  if (shape->n_kv_heads > 256) return fail(SRA_E_LIMIT, "anchors support at most 256 KV heads");
+  const int rpb = sra::anchor_rows_per_block(shape->n_kv_heads);
   std::vector<Entry> ents;
   int64_t total = 0;
   for (int c = 0; c < n_chunks; ++c) {
@@ -498,15 +509,15 @@ int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t sto
       return fail(SRA_E_CHUNKS, "chunk %d reads outside the store", c);
     if (ch.n_tokens < k) return fail(SRA_E_SHAPE, "chunk %d has %d tokens < k = %d", c, ch.n_tokens, k);
     // dst: output slot; delta: offset of the chunk's sums of squares in the workspace
-    ents.push_back({0, ch.src_row, ch.n_tokens, c, (int)total, (int)ceil_div(ch.n_tokens, 4)});
+    ents.push_back({0, ch.src_row, ch.n_tokens, c, (int)total, (int)ceil_div(ch.n_tokens, rpb), c});
     total += ch.n_tokens;
   }
   if (total > std::numeric_limits<int32_t>::max()) return fail(SRA_E_LIMIT, "too many chunk tokens");
   if ((rc = check_ws(ws, ws_bytes, (size_t)total * sizeof(double)))) return rc;
-  const int row_elems = shape->n_kv_heads * shape->head_dim;
   double* ss = static_cast<double*>(ws);
   hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
-    return sra::launch_anchors(shape->dtype, row_elems, tab, k, k_store, ss, anchor_rows, norms, stream);
+    return sra::launch_anchors(shape->dtype, shape->n_kv_heads, shape->head_dim, tab, k, k_store, ss,
+                               anchor_rows, norms, stream);
   });
   if (e != hipSuccess) return hip_fail(e, "anchor launch");
   return ok();
@@ -649,6 +660,21 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
     if ((rc = resolve_count(n_req, a->n_chunks, a->chunks, Lctx, a->n_select, a->chunk_quota, &N))) return rc;
     if (N + Lq != R) return fail(SRA_E_SHAPE, "n_rows %d != selected %d + query %d", R, N, Lq);
   }
+  const int ak = a->anchors_k;
+  bool anchors_fused = false;
+  if (ak != 0) {
+    if (!a->q_crit) return fail(SRA_E_SHAPE, "anchors are taken with the scoring: q_crit is NULL");
+    if (ak < 1) return fail(SRA_E_SHAPE, "anchors_k must be >= 0");
+    if (ak > SRA_MAX_ANCHOR_K) return fail(SRA_E_LIMIT, "anchors_k = %d exceeds %d", ak, SRA_MAX_ANCHOR_K);
+    if (!a->anchor_rows) return fail(SRA_E_NULL, "anchor_rows is NULL");
+    if (s->n_kv_heads > 256) return fail(SRA_E_LIMIT, "anchors support at most 256 KV heads");
+    anchors_fused = s->dtype == SRA_DTYPE_BF16;
+    for (int64_t i = 0; i < (int64_t)n_req * a->n_chunks; ++i) {
+      const int nt = a->chunks[i].n_tokens;
+      if (nt < ak) return fail(SRA_E_SHAPE, "chunk %lld has %d tokens < anchors_k = %d", (long long)i, nt, ak);
+      if (nt > sra::kAnchorFusedMaxLen) anchors_fused = false;
+    }
+  }
   const Plan p = make_plan(s, n_req, a->n_chunks, L, R, Lq);
   const size_t need = a->q_crit ? p.total : p.attn_end;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
@@ -666,9 +692,34 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
     return rc;
   if ((rc = mark(1)) || (rc = mark(2))) return rc;
   if (a->q_crit) {
+    sra::AnchorOut anc;
+    if (anchors_fused) {   // the scoring passes take the anchors from their own K loads
+      anc.k = ak;
+      anc.ssp = reinterpret_cast<double*>(wsp(ws, p.ssp));
+      anc.stride = (int64_t)n_req * Lctx;
+      anc.rows = a->anchor_rows;
+      anc.norms = a->anchor_norms;
+      anc.n_chunks = a->n_chunks;
+    }
     if ((rc = do_score_select(s, n_req, a->q_crit, Lq, a->k_crit_store, a->chunks, a->n_chunks, Lctx,
-                              N, a->chunk_quota, a->scores, a->row_pos, ws, p, stream)))
+                              N, a->chunk_quota, a->scores, a->row_pos, ws, p, stream, anc)))
       return rc;
+    if (ak > 0 && !anchors_fused) {   // the standalone kernels, over every (request, chunk)
+      std::vector<Entry> ents;
+      const int rpb = sra::anchor_rows_per_block(s->n_kv_heads);
+      for (int q = 0; q < n_req; ++q)
+        for (int c = 0; c < a->n_chunks; ++c) {
+          const sra_chunk& k = a->chunks[(int64_t)q * a->n_chunks + c];
+          ents.push_back({0, k.src_row, k.n_tokens, q * a->n_chunks + c, q * Lctx + k.dst_row,
+                          (int)ceil_div(k.n_tokens, rpb), c});
+        }
+      double* ss = reinterpret_cast<double*>(wsp(ws, p.ssp));
+      hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
+        return sra::launch_anchors(s->dtype, s->n_kv_heads, s->head_dim, tab, ak, a->k_crit_store, ss,
+                                   a->anchor_rows, a->anchor_norms, stream);
+      });
+      if (e != hipSuccess) return hip_fail(e, "anchor launch");
+    }
   }
   if ((rc = mark(3)) || (rc = mark(4))) return rc;
   // the scatter kernel also writes the attention's per-row inputs (query operand or angle table)

@@ -95,12 +95,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       cum[t + 1] = n;
       local += n;
     }
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
+    const int incl = (int)wave_incl_sum((uint32_t)local);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int run = incl - local;
@@ -128,8 +123,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
   }
 
-  const int64_t kv_base = ((int64_t)req * a.L * a.Hkv + kvh) * D;
-  const int64_t kv_row = (int64_t)a.Hkv * D;
+  // uniform base of this (request, KV head); per-thread byte offsets fit 32 bits (checked by the host)
+  const char* kbase = reinterpret_cast<const char*>(a.kf + ((int64_t)req * a.L * a.Hkv + kvh) * D);
+  const char* vbase = reinterpret_cast<const char*>(a.vf + ((int64_t)req * a.L * a.Hkv + kvh) * D);
+  const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
   // Tile loads. K: 16-byte chunks, dims fastest (coalesced rows). V: each task holds 4 keys x 8
   // dims and writes them transposed; key quads vary fastest across lanes, so the 16 lanes an LDS
   // write serves together hit 16 distinct bank pairs. The next tile's loads are issued into
@@ -144,13 +141,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
       const int u = threadIdx.x + 256 * i;
-      const int j = min(kt0 + u / (D / 8), kend - 1);
-      kr[i] = *reinterpret_cast<const u32x4*>(a.kf + kv_base + j * kv_row + 8 * (u % (D / 8)));
+      const uint32_t j = (uint32_t)min(kt0 + u / (D / 8), kend - 1);
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (j * row_bytes + 16u * (uint32_t)(u % (D / 8))));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = min(kt0 + 4 * vkq + i, kend - 1);
-      vr[i] = *reinterpret_cast<const u32x4*>(a.vf + kv_base + j * kv_row + 8 * (vtask ? vc : 0));
+      const uint32_t j = (uint32_t)min(kt0 + 4 * vkq + i, kend - 1);
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + (j * row_bytes + 16u * (uint32_t)(vtask ? vc : 0)));
     }
 #pragma unroll
     for (int i = 0; i < NKL; ++i)
@@ -174,11 +171,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const int v = t * 128 + wave * 32 + l32;
     bf16x8 qhi[NKS], qlo[NKS];
     {
-      const int b = t * 4 + wave;
+      // the wave's 32-vector block: a uniform base and 32-bit lane offsets (layout of qop_index)
+      const char* qb = reinterpret_cast<const char*>(a.qop + qop_index(group, t * 4 + wave, 0, 0, 0, 0, a.qop_blocks, NKS));
+      const uint32_t lo = (uint32_t)(l32 * 16 + hh * 8) * 2u;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        qhi[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.qop + qop_index(group, b, ks, 0, l32, hh, a.qop_blocks, NKS)));
-        qlo[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(a.qop + qop_index(group, b, ks, 1, l32, hh, a.qop_blocks, NKS)));
+        qhi[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + ((uint32_t)(ks * 2 + 0) * 1024u + lo)));
+        qlo[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + ((uint32_t)(ks * 2 + 1) * 1024u + lo)));
       }
     }
     prefetch(kbeg, kend);
@@ -192,9 +191,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       for (int ks = 0; ks < NKS; ++ks) qhi[ks] = qlo[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
     // smallest position among this wave's query vectors: tiles entirely at or below it need no mask
-    int pmin = qvalid ? pq : INT_MAX;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) pmin = min(pmin, __shfl_xor(pmin, off, 64));
+    const int pmin = (int)wave_reduce(qvalid ? (uint32_t)pq : (uint32_t)INT_MAX,
+                                      [](uint32_t x, uint32_t y) { return x < y ? x : y; });
 
     f32x16 o[NDT];
 #pragma unroll
@@ -313,11 +311,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
 
     const float l_tot = half_sum(l_run);
+    // the lane's store offsets are formed here from an opaque copy of the lane index, so that the
+    // compiler does not hold 64-bit lane addresses across the key loop (they would spill)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int e32 = ln & 31, ehh = ln >> 5;
     // o[dt][rr] holds dim 32*dt + 8*(rr/4) + 4*hh + rr%4 of query vector v
     if (direct) {
       if (qvalid) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* op = a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 4 * hh;
+        // uniform request base and a 32-bit lane offset (the host bounds R*Hq*D)
+        uint16_t* ob = a.out + (int64_t)req * a.R * a.Hq * D;
+        const uint32_t lo = (uint32_t)((r * a.Hq + hq) * D + 4 * ehh);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -325,23 +330,25 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             u32x2 w;
             w[0] = pack_bf2(o[dt][4 * b4] * inv, o[dt][4 * b4 + 1] * inv);
             w[1] = pack_bf2(o[dt][4 * b4 + 2] * inv, o[dt][4 * b4 + 3] * inv);
-            *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * b4) = w;
+            *reinterpret_cast<u32x2*>(ob + (lo + (uint32_t)(32 * dt + 8 * b4))) = w;
           }
         if (hh == 0 && a.lse)
           a.lse[((int64_t)req * a.R + r) * a.Hq + hq] =
               l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else {
-      const int64_t pi = part_index(a, group, piece, slot) + wave * 32 + l32;
-      float* po = a.part_o + pi * D + 4 * hh;
+      // the wave's 32 vectors of the slot: a uniform base and 32-bit lane offsets
+      const int64_t pw = part_index(a, group, piece, slot) + __builtin_amdgcn_readfirstlane(wave) * 32;
+      float* pob = a.part_o + pw * D;
+      const uint32_t lo = (uint32_t)(e32 * D + 4 * ehh);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
           const f32x4 w = {o[dt][4 * b4], o[dt][4 * b4 + 1], o[dt][4 * b4 + 2], o[dt][4 * b4 + 3]};
-          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * b4) = w;
+          *reinterpret_cast<f32x4*>(pob + (lo + (uint32_t)(32 * dt + 8 * b4))) = w;
         }
-      if (hh == 0) a.part_ml[pi] = make_float2(m_run, l_tot);
+      if (ehh == 0) a.part_ml[pw + e32] = make_float2(m_run, l_tot);
     }
     slot = 1;
     u = se;

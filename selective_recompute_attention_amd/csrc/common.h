@@ -20,6 +20,7 @@ struct ChunkTab {
   int len[kMaxEntries];
   int dst[kMaxEntries];
   int delta[kMaxEntries];
+  int aux[kMaxEntries];      // the entry's chunk index within its request
   int blk0[kMaxEntries + 1];
 };
 
@@ -74,6 +75,64 @@ __device__ __forceinline__ float half_sum(float x) {
 __device__ __forceinline__ float half_partner(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Sum of squares of the 16 bytes of one key in float64, element by element in order. A square of a
+// bf16 or float32 value is exact in float64, so this sequence gives the same bits wherever it runs.
+template <typename T>
+__device__ __forceinline__ double sumsq16(double acc, const uint32_t* w);
+template <>
+__device__ __forceinline__ double sumsq16<uint16_t>(double acc, const uint32_t* w) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double a = __uint_as_float(w[k] << 16), b = __uint_as_float(w[k] & 0xffff0000u);
+    acc += a * a;
+    acc += b * b;
+  }
+  return acc;
+}
+template <>
+__device__ __forceinline__ double sumsq16<float>(double acc, const uint32_t* w) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double a = __uint_as_float(w[k]);
+    acc += a * a;
+  }
+  return acc;
+}
+// Key-norm sums: one float64 sum per (token, KV head) over its d values in order, then the heads in
+// order. Rows of one block of the row-sum kernel: one thread per (row, head).
+__host__ __device__ __forceinline__ int anchor_rows_per_block(int Hkv) { return Hkv >= 256 ? 1 : 256 / Hkv; }
+// Longest chunk whose anchors the scoring pass picks itself (its sums fit the pass's LDS tile).
+constexpr int kAnchorFusedMaxLen = 4352;
+
+// Whole-wave scans and reductions on DPP lane moves (row shifts inside 16-lane rows, then the
+// row broadcasts of lanes 15 and 31), all plain VALU instructions.
+template <int CTRL, int ROW_MASK, bool BC>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, BC);
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += dpp_mov<0x111, 0xf, true>(0u, v);    // row_shr:1
+  v += dpp_mov<0x112, 0xf, true>(0u, v);    // row_shr:2
+  v += dpp_mov<0x114, 0xf, true>(0u, v);    // row_shr:4
+  v += dpp_mov<0x118, 0xf, true>(0u, v);    // row_shr:8
+  v += dpp_mov<0x142, 0xa, false>(0u, v);   // row_bcast:15 -> rows 1 and 3
+  v += dpp_mov<0x143, 0xc, false>(0u, v);   // row_bcast:31 -> rows 2 and 3
+  return v;
+}
+// Reduction with an idempotent operation (lanes without a source keep their own value); the
+// result of the whole wave, returned in every lane.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, dpp_mov<0x111, 0xf, false>(v, v));
+  v = op(v, dpp_mov<0x112, 0xf, false>(v, v));
+  v = op(v, dpp_mov<0x114, 0xf, false>(v, v));
+  v = op(v, dpp_mov<0x118, 0xf, false>(v, v));
+  v = op(v, dpp_mov<0x142, 0xa, false>(v, v));
+  v = op(v, dpp_mov<0x143, 0xc, false>(v, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Rotary frequencies theta_i = base^(-2i/d), i < d/2, formed once on the host in float64 and passed
@@ -139,8 +198,21 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
                           hipStream_t st);
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
                              double base, hipStream_t st);
-hipError_t launch_anchors(int dtype, int row_elems, const ChunkTab& tab, int k, const void* ks,
+// tab: entries = chunks (src, len), dst = output slot, delta = offset of the chunk's sums in ss,
+// blk0 in blocks of anchor_rows_per_block(Hkv) rows.
+hipError_t launch_anchors(int dtype, int Hkv, int D, const ChunkTab& tab, int k, const void* ks,
                           double* ss, int32_t* anchors, float* norms, hipStream_t st);
+// Anchors taken inside the scoring passes: pass 1 writes per-head sums of squares (ssp
+// [Hkv][stride], stride = n_req * L_ctx, at the token's context position), pass 2 adds one block per
+// chunk entry that picks the k largest totals (k == 0: none).
+struct AnchorOut {
+  int k = 0;
+  double* ssp = nullptr;
+  int64_t stride = 0;
+  int32_t* rows = nullptr;   // [n_req][n_chunks][k]
+  float* norms = nullptr;    // [store rows] or NULL
+  int n_chunks = 0;
+};
 // Critical-layer scores are accumulated over KV heads as 64-bit fixed point (kScoreFixScale units):
 // integer additions are exact and associative, so the total does not depend on their order.
 constexpr double kScoreFixScale = 1099511627776.0;   // 2^40
@@ -152,7 +224,7 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
-                             unsigned long long* fx, hipStream_t st);
+                             unsigned long long* fx, const AnchorOut& anc, hipStream_t st);
 hipError_t launch_score_merge(const int* req_blk0, int n_req, int Hkv, int Mpad, int Mvalid,
                               const float2* ml_part, float2* ml_final, hipStream_t st);
 hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,

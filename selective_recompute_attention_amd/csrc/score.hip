@@ -171,6 +171,59 @@ __device__ __forceinline__ void load_q(const uint16_t* qp, int64_t plane, bf16x8
   }
 }
 
+// Anchors of chunk entry e (one block): the key-norm totals (per-head sums added in head order) go
+// to LDS, then wave 0 takes k rounds, each picking the best token ranked after the previous pick
+// (larger sum first, lower offset on a tie; float64 sums of squares order like their bit patterns).
+// (Scalar arguments only: a reference to the kernel-argument table would copy it to scratch.)
+__device__ __forceinline__ void anchor_block(int len, int64_t base, int src, int64_t out_slot, int Hkv,
+                                             const AnchorOut& anc, unsigned long long* tot) {
+  // len <= kAnchorFusedMaxLen (checked by the host); base = the chunk's first context position
+  for (int t = threadIdx.x; t < len; t += blockDim.x) {
+    double sum = 0.0;
+    for (int h0 = 0; h0 < Hkv; h0 += 8) {
+      double v[8];   // eight heads' loads at once, added in head order
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = anc.ssp[(int64_t)min(h0 + u, Hkv - 1) * anc.stride + base + t];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (h0 + u < Hkv) sum += v[u];
+    }
+    tot[t] = __double_as_longlong(sum);
+    if (anc.norms) anc.norms[(int64_t)src + t] = (float)sqrt(sum);
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  unsigned long long pv = ~0ull;   // previous pick (value, offset); starts above everything
+  int pt = -1;
+  for (int round = 0; round < anc.k; ++round) {
+    bool have = false;
+    unsigned long long bv = 0;
+    int bt = INT_MAX;
+    for (int t = lane; t < len; t += 64) {
+      const unsigned long long v = tot[t];
+      const bool after = v < pv || (v == pv && t > pt);
+      const bool better = after && (!have || v > bv || (v == bv && t < bt));
+      bv = better ? v : bv;
+      bt = better ? t : bt;
+      have = have || better;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const unsigned long long ov = __shfl_xor(bv, off, 64);
+      const int ot = __shfl_xor(bt, off, 64);
+      const bool oh = __shfl_xor((int)have, off, 64) != 0;
+      const bool better = oh && (!have || ov > bv || (ov == bv && ot < bt));
+      bv = better ? ov : bv;
+      bt = better ? ot : bt;
+      have = have || oh;
+    }
+    if (lane == 0) anc.rows[out_slot * anc.k + round] = bt;
+    pv = bv;
+    pt = bt;
+  }
+}
+
 // grid (key blocks, Hkv). A block owns 128 keys of one chunk (staged once in LDS, rows padded for
 // conflict-free 16-byte reads); wave w owns the 32-vector query tiles w, w+4, ... with their
 // operands in registers. Every global load of a tile (K, Q and, in pass 2, the merge inputs) is
@@ -188,7 +241,8 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
                                                     float2* __restrict__ ml_part,
                                                     const float2* __restrict__ ml_final,
                                                     int fuse_merge,
-                                                    unsigned long long* __restrict__ fx) {
+                                                    unsigned long long* __restrict__ fx,
+                                                    AnchorOut anc) {
   constexpr int NKS = D / 16;
   constexpr int KB = 128;          // keys per block
   constexpr int KST = D + 8;       // LDS row stride (elements)
@@ -198,6 +252,16 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
   __shared__ float colred[4][KB];
   __shared__ float2 mlw[4][32];
   const int blk = blockIdx.x, kvh = blockIdx.y;
+  if (blk >= tab.blk0[tab.n]) {   // pass 2's extra blocks: one per chunk entry picks its anchors
+    if constexpr (PASS == 2) {
+      const int e = blk - tab.blk0[tab.n];
+      if (kvh == 0)
+        anchor_block(tab.len[e], (int64_t)tab.req[e] * Lctx + tab.dst[e], tab.src[e],
+                     (int64_t)tab.req[e] * anc.n_chunks + tab.aux[e], Hkv, anc,
+                     reinterpret_cast<unsigned long long*>(Ks));
+    }
+    return;
+  }
   const int e = find_entry(tab, blk);
   const int t0 = (blk - tab.blk0[e]) * KB;
   const int req = tab.req[e];
@@ -258,6 +322,15 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
     *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) = kr[i];
   }
   __syncthreads();
+  if constexpr (PASS == 1) {
+    if (anc.k > 0 && (int)threadIdx.x < nk) {   // this KV head's share of the key norms
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(Ks + threadIdx.x * KST);
+      double acc = 0.0;
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) acc = sumsq16<uint16_t>(acc, row + 4 * c);
+      anc.ssp[kvh * anc.stride + (int64_t)req * Lctx + tab.dst[e] + t0 + threadIdx.x] = acc;
+    }
+  }
 
   float col[4] = {0.f, 0.f, 0.f, 0.f};   // pass 2: keys 32 st + l32
   for (int qt = wave; qt < nqt; qt += 4) {
@@ -365,17 +438,18 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
-                             unsigned long long* fx, hipStream_t st) {
+                             unsigned long long* fx, const AnchorOut& anc, hipStream_t st) {
   const int nblk = tab.blk0[tab.n];
   if (nblk == 0) return hipSuccess;
   ReqBlocks rb;
   for (int r = 0; r <= n_req; ++r) rb.blk0[r] = req_blk0[r];
-  dim3 g(nblk, Hkv), b(256);
+  // pass 2 carries one extra block per entry for the anchors
+  dim3 g(nblk + (pass == 2 && anc.k > 0 ? tab.n : 0), Hkv), b(256);
   const uint16_t* k = (const uint16_t*)kc;
 #define SRA_PASS(DD, PP)                                                                        \
   k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
                                           entry_base, blk_base, ml_part, ml_final, fuse_merge,  \
-                                          fx)
+                                          fx, anc)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);
   else if (D == 128) SRA_PASS(128, 2);
   else if (pass == 1) SRA_PASS(64, 1);

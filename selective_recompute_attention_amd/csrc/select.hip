@@ -25,12 +25,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Exclusive prefix sum of x over the block (4 waves, in thread order); also the total.
 __device__ __forceinline__ int block_excl_sum(int x, int* wsum, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const int incl = (int)wave_incl_sum((uint32_t)x);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int before = 0, tot = 0;
@@ -52,7 +47,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
                                                         int* __restrict__ row_pos) {
   constexpr int NW = kSelThreads / 64;
   constexpr int KREG = 16;   // keys per thread held in registers (units up to 4096 keys)
-  __shared__ unsigned hist[4][NW][256];   // one histogram per radix pass and wave
+  constexpr int kSub = 4;
+  __shared__ unsigned hist[4][NW][256 * kSub];   // per radix pass and wave: kSub copies of each bin
   __shared__ uint32_t sh_prefix, sh_remaining;
   __shared__ uint32_t sh_and[NW], sh_or[NW];
   __shared__ int wsum[NW];
@@ -69,7 +65,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
   const int jlo = min((int)threadIdx.x * per, len), jhi = min(jlo + per, len), cnt = jhi - jlo;
   const bool in_regs = len > 0 && per <= KREG;
   const bool in_lds = len <= kSelLdsKeys;
-  for (int i = threadIdx.x; i < 4 * NW * 256; i += kSelThreads) (&hist[0][0][0])[i] = 0;
+  for (int i = threadIdx.x; i < 4 * NW * 256 * kSub; i += kSelThreads) (&hist[0][0][0])[i] = 0;
 
   // scores: per-KV-head partial column sums added in head order, then order-preserving keys. The
   // loads are coalesced (position j = tid + 256 i); small units then pass their keys through LDS
@@ -153,11 +149,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
     }
   }
   // bits shared by every key of the unit
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kand &= __shfl_xor(kand, o, 64);
-    kor |= __shfl_xor(kor, o, 64);
-  }
+  kand = wave_reduce(kand, [](uint32_t a, uint32_t b) { return a & b; });
+  kor = wave_reduce(kor, [](uint32_t a, uint32_t b) { return a | b; });
   if (lane == 0) { sh_and[wave] = kand; sh_or[wave] = kor; }
   __syncthreads();
 #pragma unroll
@@ -177,20 +170,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
       }
       for (; shift >= 0; shift -= 8) {
         unsigned* h = &hist[shift >> 3][wave][0];
+        // each bin has kSub copies, chosen by lane: lanes of one wave that hit the same bin (the
+        // leading bytes of the scores take few values) spread over kSub addresses
         auto count = [&](uint32_t u, bool valid) {
-          const bool match = valid && (u & mask) == prefix;
-          const uint32_t digit = (u >> shift) & 255u;
-          const unsigned long long act = __ballot(match);
-          if (act) {
-            const int leader = __ffsll(act) - 1;
-            const uint32_t d0 = __builtin_amdgcn_readlane(digit, leader);
-            if (__ballot(match && digit == d0) == act) {
-              // the whole wave agrees: one atomic instead of a queue of same-address ones
-              if (lane == leader) atomicAdd(&h[d0], (unsigned)__popcll(act));
-            } else if (match) {
-              atomicAdd(&h[digit], 1u);
-            }
-          }
+          if (valid && (u & mask) == prefix) atomicAdd(&h[((u >> shift) & 255u) * kSub + (lane & (kSub - 1))], 1u);
         };
         if (in_regs) {
 #pragma unroll
@@ -208,16 +191,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
             const int bin = 255 - 4 * lane - i;
             uint32_t cc = 0;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) cc += hist[shift >> 3][w][bin];
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+              for (int sb = 0; sb < kSub; ++sb) cc += hist[shift >> 3][w][bin * kSub + sb];
             c[i] = cc;
             tot += cc;
           }
-          uint32_t incl = tot;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-          }
+          const uint32_t incl = wave_incl_sum(tot);
           uint32_t cum = incl - tot, before = 0;
           int found = -1;
 #pragma unroll

@@ -274,6 +274,64 @@ def test_anchors_match_oracle(idx):
                 assert set(anchors.cpu().numpy()[c].tolist()) <= set(outl.tolist())
 
 
+
+FUSED_ANCHOR_CASES = {
+    # name: (workload builder, anchors k)
+    "mistral7b_layer": (lambda: make_workload(1), 4),                       # bf16: in the scoring passes
+    "tiny_f32": (lambda: make_workload(0), 4),                              # float32: standalone kernels
+    "two_requests_ragged_bf16": (lambda: make_custom(dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                                     chunk_lens=(200, 37, 301), orig_pos=(0, 5, 0), query_len=7,
+                                                     n_req=2, seed=11), 6),
+    "chunk_longer_than_lds_bf16": (lambda: make_custom(dtype="bf16", n_q_heads=2, n_kv_heads=1, head_dim=64,
+                                                       chunk_lens=(4500, 100), query_len=3, seed=12), 5),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_ANCHOR_CASES))
+def test_fused_anchors_match_standalone_and_oracle(name):
+    build, k = FUSED_ANCHOR_CASES[name]
+    w = build()
+    cfg = w.cfg
+    shape = shape_of(cfg)
+    n_req, n_chunks = w.chunks.shape[0], w.chunks.shape[1]
+    lay = w.layer(0)
+    Lctx = int(w.chunks[0, :, 1].sum())
+    Lq = cfg.query_len
+    L = Lctx + Lq
+    N = sra.select_count(15, 100, Lctx)
+    R = N + Lq
+    dt = cfg.dtype
+    say(f"case fused anchors {name}: n_req {n_req}, chunks {n_chunks}, k {k}")
+    t = {kk: dev(v, dt) for kk, v in lay.items()}
+    kc = dev(w.k_crit, dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    kf = torch.empty((n_req, L, cfg.n_kv_heads, cfg.head_dim), dtype=tdt, device="cuda")
+    vf = torch.empty_like(kf)
+    out = torch.empty((n_req, R, cfg.n_q_heads, cfg.head_dim), dtype=tdt, device="cuda")
+    rp = torch.empty((n_req, R), dtype=torch.int32, device="cuda")
+    anchors = torch.full((n_req, n_chunks, k), -7, dtype=torch.int32, device="cuda")
+    norms = torch.zeros((w.k_crit.shape[0],), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sra.workspace_size(shape, n_req, n_chunks, L, R, Lq), dtype=torch.uint8, device="cuda")
+    sra.fused_layer(shape, chunks=w.chunks, k_store=t["k_store"], v_store=t["v_store"], q_fresh=t["q_new"],
+                    k_fresh=t["k_new"], v_fresh=t["v_new"], row_pos=rp, k_fused=kf, v_fused=vf, out=out, ws=ws,
+                    q_crit=dev(w.q_crit, dt), k_crit_store=kc, n_select=N, anchors_k=k, anchor_rows=anchors,
+                    anchor_norms=norms)
+    torch.cuda.synchronize()
+    got = anchors.cpu().numpy()
+    for q in range(n_req):
+        ch = w.chunks[q]
+        a1 = torch.empty((n_chunks, k), dtype=torch.int32, device="cuda")
+        n1 = torch.zeros_like(norms)
+        aws = torch.empty(sra.anchor_workspace_size(ch), dtype=torch.uint8, device="cuda")
+        sra.extract_anchors(shape, kc, ch, k, a1, aws, n1)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got[q], a1.cpu().numpy())           # same bits as the standalone call
+        np.testing.assert_array_equal(got[q], O.extract_anchors(w.k_crit, ch, k, dt))
+        rows = np.concatenate([np.arange(s0, s0 + T) for s0, T, _d, _o in ch.tolist()])
+        np.testing.assert_array_equal(norms.cpu().numpy()[rows], n1.cpu().numpy()[rows])
+    np.testing.assert_allclose(norms.cpu().numpy()[rows], O.key_norms(w.k_crit, dt)[rows], rtol=1e-6)
+
+
 # ------------------------------------------------------------------------------ invariants on the GPU
 
 def test_zero_selection_zero_delta_keeps_cache_bits():
