@@ -136,8 +136,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int vkq = threadIdx.x % (KT / 4), vc = threadIdx.x / (KT / 4);
   u32x4 kr[NKL], vr[4];
   auto prefetch = [&](int kt0, int kend) {
-    // unconditional loads of clamped rows (kt0 < kend), zeroed past the range afterwards, so that
-    // no load waits for another
+    // unconditional loads of clamped rows (kt0 < kend): rows past the range repeat row kend - 1,
+    // whose keys the mask removes (probability 0 on finite values). Nothing reads the registers
+    // until the tile is stored, so no load waits for another.
 #pragma unroll
     for (int i = 0; i < NKL; ++i) {
       const int u = threadIdx.x + 256 * i;
@@ -149,12 +150,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const uint32_t j = (uint32_t)min(kt0 + 4 * vkq + i, kend - 1);
       vr[i] = *reinterpret_cast<const u32x4*>(vbase + (j * row_bytes + 16u * (uint32_t)(vtask ? vc : 0)));
     }
-#pragma unroll
-    for (int i = 0; i < NKL; ++i)
-      if (kt0 + (threadIdx.x + 256 * i) / (D / 8) >= kend) kr[i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (!vtask || kt0 + 4 * vkq + i >= kend) vr[i] = u32x4{0u, 0u, 0u, 0u};
   };
 
   int slot = 0;
@@ -231,7 +226,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const uint16_t* Kc = Ks[cur];
       const uint16_t* Vc = Vt[cur];
 
-      // S^T[key][q] for two 32-key sub-tiles
+      // S^T[key][q] for the two 32-key halves. The halves then go through softmax and P V one
+      // after the other (an online-softmax step each), so the second half's products are still
+      // running while the first half's softmax is formed.
       f32x16 sc[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -244,53 +241,49 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qlo[ks], sc[st], 0, 0, 0);
         }
       }
-      // causal mask by absolute position (only on tiles that reach past the wave's smallest
-      // position or the range's end), online softmax in the log2 domain
-      float mt = -INFINITY;
-      if (kt0 + KT <= kend && kt0 + KT - 1 <= pmin) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st) {
+        f32x16 x = sc[st];
+        // causal mask by absolute position (only where the half reaches past the wave's smallest
+        // position or the range's end), online softmax in the log2 domain
+        const int klast = kt0 + 32 * st + 31;
+        float mt = -INFINITY;
+        if (klast < kend && klast <= pmin) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, sc[st][rr]);
-      } else {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
+          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
+        } else {
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int key = kt0 + 32 * st + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            if (!(key < kend && key <= pq)) sc[st][rr] = -INFINITY;
-            mt = fmaxf(mt, sc[st][rr]);
+            if (!(key < kend && key <= pq)) x[rr] = -INFINITY;
+            mt = fmaxf(mt, x[rr]);
           }
-      }
-      mt = half_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all masked so far: every p is 0
-      const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
+        }
+        mt = half_max(mt);
+        const float m_new = fmaxf(m_run, mt);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all masked so far: every p is 0
+        const float alpha = fast_exp2(m_run - m_use);
+        float lsum = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const float pr = fast_exp2(sc[st][rr] - m_use);
-          sc[st][rr] = pr;
+          const float pr = fast_exp2(x[rr] - m_use);
+          x[rr] = pr;
           lsum += pr;
         }
-      l_run = l_run * alpha + lsum;
-      // rescale the accumulator only when some lane's running max grew (alpha is 1 elsewhere)
-      if (__any(m_new > m_run)) {
+        l_run = l_run * alpha + lsum;
+        // rescale the accumulator only when some lane's running max grew (alpha is 1 elsewhere)
+        if (__any(m_new > m_run)) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-      }
-      m_run = m_new;
+          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
+        m_run = m_new;
 
-      // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
+        // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
           u32x4 pw;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) pw[k] = pack_bf2(sc[st][8 * mp + 2 * k], sc[st][8 * mp + 2 * k + 1]);
+          for (int k = 0; k < 4; ++k) pw[k] = pack_bf2(x[8 * mp + 2 * k], x[8 * mp + 2 * k + 1]);
           const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
@@ -301,6 +294,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pb, o[dt], 0, 0, 0);
           }
         }
+      }
 
       if (kt0 + KT < kend) {
         store_tile(cur ^ 1);   // its previous tile was retired by the last barrier
