@@ -41,6 +41,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLazyMax = 8.f;   // log2 headroom of the attention softmax reference
 
 struct AttnArgs {
   const uint16_t* qop;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     f32x16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, m_ref = 0.f, l_run = 0.f;  // running max, softmax reference, sum
 
     // K row-major; V transposed on the way in (word pp of a task: dims 8c+2pp in the low half
     // and 8c+2pp+1 in the high half, four keys each)
@@ -244,46 +245,48 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x16 x = sc[st];
-        // causal mask by absolute position (only where the half reaches past the wave's smallest
-        // position or the range's end), online softmax in the log2 domain
+        // causal mask by absolute position where the half reaches past the wave's smallest position
+        // or the range's end: element rr holds key kt0 + 32 st + 4 hh + (8 (rr / 4) + rr % 4)
         const int klast = kt0 + 32 * st + 31;
+        if (!(klast < kend && klast <= pmin)) {
+          const int lim = min(kend - 1, pq) - (kt0 + 32 * st + 4 * hh);
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (8 * (rr >> 2) + (rr & 3) > lim) x[rr] = -INFINITY;
+        }
+        // online softmax in the log2 domain against a lazily moved reference m_ref (0 before any
+        // key): the reference follows a lane's maximum only once a logit exceeds it by more than
+        // kLazyMax, so probabilities stay below 2^kLazyMax and the accumulator is rescaled rarely
         float mt = -INFINITY;
-        if (klast < kend && klast <= pmin) {
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
-        } else {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int key = kt0 + 32 * st + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-            if (!(key < kend && key <= pq)) x[rr] = -INFINITY;
-            mt = fmaxf(mt, x[rr]);
-          }
-        }
+        for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
         mt = half_max(mt);
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // all masked so far: every p is 0
-        const float alpha = fast_exp2(m_run - m_use);
-        float lsum = 0.f;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float pr = fast_exp2(x[rr] - m_use);
-          x[rr] = pr;
-          lsum += pr;
-        }
-        l_run = l_run * alpha + lsum;
-        // rescale the accumulator only when some lane's running max grew (alpha is 1 elsewhere)
-        if (__any(m_new > m_run)) {
+        const bool upd = mt - m_ref > (m_run == -INFINITY ? -INFINITY : kLazyMax);
+        if (__any(upd)) {
+          const float m_new = upd ? mt : m_run;
+          const float r_new = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_ref - r_new);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+          m_ref = r_new;
         }
-        m_run = m_new;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) x[rr] = fast_exp2(x[rr] - m_ref);
 
         // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4
+        // the sum takes the same bf16-rounded probabilities the products use, so the output
+        // weights stay a convex combination
+        float lsum = 0.f;
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
           u32x4 pw;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) pw[k] = pack_bf2(x[8 * mp + 2 * k], x[8 * mp + 2 * k + 1]);
+          for (int k = 0; k < 4; ++k) {
+            pw[k] = pack_bf2(x[8 * mp + 2 * k], x[8 * mp + 2 * k + 1]);
+            lsum += __uint_as_float(pw[k] << 16) + __uint_as_float(pw[k] & 0xffff0000u);
+          }
           const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
@@ -294,6 +297,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pb, o[dt], 0, 0, 0);
           }
         }
+        l_run += lsum;
       }
 
       if (kt0 + KT < kend) {
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           }
         if (hh == 0 && a.lse)
           a.lse[((int64_t)req * a.R + r) * a.Hq + hq] =
-              l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+              l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else {
       // the wave's 32 vectors of the slot: a uniform base and 32-bit lane offsets
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           const f32x4 w = {o[dt][4 * b4], o[dt][4 * b4 + 1], o[dt][4 * b4 + 2], o[dt][4 * b4 + 3]};
           *reinterpret_cast<f32x4*>(pob + (lo + (uint32_t)(32 * dt + 8 * b4))) = w;
         }
-      if (ehh == 0) a.part_ml[pw + e32] = make_float2(m_run, l_tot);
+      if (ehh == 0) a.part_ml[pw + e32] = make_float2(l_tot > 0.f ? m_ref : -INFINITY, l_tot);
     }
     slot = 1;
     u = se;
