@@ -42,7 +42,7 @@ __all__ = [
     "to_f64", "round_to_storage", "bf16_round", "storage_bits", "rope_theta", "rope",
     "chunk_layout", "fuse_rerotate", "key_norms", "extract_anchors", "critical_scores",
     "select_count", "select_topn", "select_topn_quota", "row_positions", "scatter_kv",
-    "sparse_causal_attn", "fused_layer",
+    "sparse_causal_attn", "fused_layer", "kv_deviation", "hkvd_filter", "gradual_filter_layers",
 ]
 
 
@@ -247,6 +247,44 @@ def scatter_kv(k_fused, v_fused, k_new, v_new, row_pos, dtype: str, base: float)
     return kf, vf
 
 
+# ----------------------------------------------------------------------------- CacheBlend gradual filtering
+
+def kv_deviation(k_fused, v_fused, k_new, v_new, row_pos, n_rows: int, dtype: str, base: float):
+    """KV deviation of recomputed tokens (KVCache reuse 01, §1.3.2: the absolute difference between
+    a token's reused KV and its recomputed KV; §1.3.3 ranks tokens by it).
+
+    Reading: for each of the first n_rows recomputed rows r, at absolute position p = row_pos[r],
+    the Euclidean norm, over every KV head and dimension, of (recomputed K - reused K) together
+    with (recomputed V - reused V). The recomputed K is the value the cache would store,
+    round(R(p) K_new[r]); the reused K/V are the cache's rows at p after re-rotation and before the
+    scatter. k_fused, v_fused: float64 [L, Hkv, d]; k_new, v_new: stored values [>= n_rows, Hkv, d]
+    (compact, K before rotation). Returns float64 [n_rows].
+    """
+    n = int(n_rows)
+    rp = np.asarray(row_pos, dtype=np.int64)[:n]
+    kf, vf = np.asarray(k_fused, dtype=np.float64), np.asarray(v_fused, dtype=np.float64)
+    kn = round_to_storage(rope(to_f64(np.asarray(k_new)[:n], dtype), rp[:, None], base), dtype)
+    vn = to_f64(np.asarray(v_new)[:n], dtype)
+    dk = kn - kf[rp]
+    dv = vn - vf[rp]
+    return np.sqrt((dk * dk).sum(axis=(1, 2)) + (dv * dv).sum(axis=(1, 2)))
+
+
+def hkvd_filter(dev, row_pos, n_prev: int, n_keep: int) -> np.ndarray:
+    """Next layer's recomputed rows under gradual filtering (KVCache reuse 01, §1.3.3: layer i keeps,
+    among the tokens layer i-1 selected, the given share with the highest KV deviation).
+
+    row_pos holds the previous selection (n_prev context positions, ascending) followed by the query
+    rows. The n_keep context rows of highest deviation are kept -- ranked on float32 deviations,
+    the precision the device decides in, ties to the lower row -- in ascending order, followed by
+    the same query rows.
+    """
+    rp = np.asarray(row_pos, dtype=np.int64)
+    d32 = np.asarray(dev, dtype=np.float64)[:n_prev].astype(np.float32).astype(np.float64)
+    keep = select_topn(d32, int(n_keep))
+    return np.concatenate([rp[:n_prev][keep], rp[n_prev:]]).astype(np.int32)
+
+
 # ----------------------------------------------------------------------------- S4: attention
 
 def sparse_causal_attn(q_new, row_pos, k_fused, v_fused, dtype: str, base: float,
@@ -286,18 +324,27 @@ def sparse_causal_attn(q_new, row_pos, k_fused, v_fused, dtype: str, base: float
 
 def fused_layer(*, k_store, v_store, chunks, L: int, q_new, k_new, v_new, dtype: str, base: float,
                 n_kv_heads: int, q_crit=None, k_crit_store=None, n_select: Optional[int] = None,
-                quotas=None, row_pos=None, attn_rows=None):
+                quotas=None, row_pos=None, attn_rows=None, hkvd_prev=None, hkvd_n_prev=None):
     """One layer of the fusion step: S1, then (S2 when a critical-layer query is given), S3, S4.
 
     q_new, k_new, v_new are position-indexed fresh projections [L, H, d]; the recomputed
-    rows are gathered from them at row_pos. Without q_crit, row_pos must be given.
-    Returns a dict with k_fused, v_fused, row_pos, scores (or None), out, lse.
+    rows are gathered from them at row_pos. Without q_crit, row_pos must be given -- or, for
+    gradual filtering, the previous layer's rows hkvd_prev (hkvd_n_prev context rows first): then
+    the n_select of them with the highest KV deviation at this layer are recomputed.
+    Returns a dict with k_fused, v_fused, row_pos, scores (or None), dev (or None), out, lse.
     """
     L_ctx, _ = chunk_layout(chunks)
     Lq = L - L_ctx
     kf, vf = fuse_rerotate(k_store, v_store, chunks, L, dtype, base)
     scores = None
-    if q_crit is not None:
+    dev = None
+    if hkvd_prev is not None:
+        prev = np.asarray(hkvd_prev, dtype=np.int64)
+        npv = int(hkvd_n_prev)
+        dev = kv_deviation(kf, vf, np.asarray(k_new)[prev[:npv]], np.asarray(v_new)[prev[:npv]],
+                           prev, npv, dtype, base)
+        row_pos = hkvd_filter(dev, prev, npv, int(n_select))
+    elif q_crit is not None:
         scores = critical_scores(q_crit, k_crit_store, chunks, n_kv_heads, dtype, base)
         if quotas is not None:
             sel = select_topn_quota(scores, chunks, quotas)
@@ -308,4 +355,37 @@ def fused_layer(*, k_store, v_store, chunks, L: int, q_new, k_new, v_new, dtype:
     kf, vf = scatter_kv(kf, vf, np.asarray(k_new)[rp], np.asarray(v_new)[rp], rp, dtype, base)
     out, lse = sparse_causal_attn(np.asarray(q_new)[rp], rp, kf, vf, dtype, base, rows=attn_rows)
     return {"k_fused": kf, "v_fused": vf, "row_pos": rp.astype(np.int32), "scores": scores,
-            "out": out, "lse": lse}
+            "dev": dev, "out": out, "lse": lse}
+
+
+def gradual_filter_layers(*, layers, chunks, L: int, dtype: str, base: float, n_kv_heads: int,
+                          counts: Sequence[int], q_crit=None, k_crit_store=None, row_pos0=None,
+                          attn_rows=None):
+    """Layer-by-layer recompute with gradual filtering (KVCache reuse 01, §1.3.3 and §1.3.4).
+
+    layers[l] holds layer l's k_store, v_store, q_new, k_new, v_new. Layer 0 recomputes counts[0]
+    tokens chosen by the critical-layer score (or the given row_pos0): the first-layer attention
+    deviation of the page needs a full prefill of that layer, so the query-centric score stands in
+    for it (a reading). Layer l > 0 keeps the counts[l] tokens of layer l-1's selection with the
+    highest KV deviation at layer l (counts must not increase). Returns one fused_layer result
+    per layer.
+    """
+    res = []
+    prev, npv = None, None
+    for l, lay in enumerate(layers):
+        kw = dict(k_store=lay["k_store"], v_store=lay["v_store"], chunks=chunks, L=L,
+                  q_new=lay["q_new"], k_new=lay["k_new"], v_new=lay["v_new"], dtype=dtype, base=base,
+                  n_kv_heads=n_kv_heads, n_select=int(counts[l]), attn_rows=attn_rows)
+        if l == 0:
+            if row_pos0 is not None:
+                r = fused_layer(row_pos=row_pos0, **kw)
+            else:
+                r = fused_layer(q_crit=q_crit, k_crit_store=k_crit_store, **kw)
+        else:
+            if counts[l] > npv:
+                raise ValueError("gradual filtering keeps a subset: counts must not increase")
+            r = fused_layer(hkvd_prev=prev, hkvd_n_prev=npv, **kw)
+        res.append(r)
+        prev = r["row_pos"]
+        npv = len(prev) - (L - chunk_layout(chunks)[0])
+    return res
