@@ -115,6 +115,14 @@ typedef struct {
     int32_t anchors_k;             /* anchors per chunk, 0 = none                            */
     int32_t* anchor_rows;          /* out [n_req][n_chunks][anchors_k] token offsets         */
     float* anchor_norms;           /* out [crit_store_rows] key norms at the chunks' rows, or NULL */
+    /* Gradual filtering (optional, q_crit must be NULL; KVCache reuse 01 §1.3.3): the previous
+     * layer's recomputed rows. This layer keeps the n_select of their hkvd_prev_ctx context rows
+     * with the highest KV deviation at this layer (as sra_hkvd_select, fresh rows taken from
+     * k_fresh/v_fresh at their positions) and writes them, then the query rows, to row_pos. */
+    const int32_t* hkvd_prev;      /* [n_req][hkvd_prev_rows]: ascending context rows, then Lq query rows */
+    int32_t hkvd_prev_rows;        /* hkvd_prev_ctx + Lq                                     */
+    int32_t hkvd_prev_ctx;         /* context rows of hkvd_prev                              */
+    float* hkvd_dev;               /* out [n_req][hkvd_prev_ctx] deviation of each previous row */
     /* fresh projections of every position (position-indexed, before rotary embedding) */
     const void* q_fresh;           /* [n_req][L][Hq][d]                                      */
     const void* k_fresh;           /* [n_req][L][Hkv][d]                                     */
@@ -234,6 +242,25 @@ int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, con
                    const int32_t* row_pos, int32_t R, void* k_fused, void* v_fused, int32_t L,
                    hipStream_t stream);
 
+/* KV deviation and the next layer's rows under gradual filtering (KVCache reuse 01 §1.3.2:
+ * the KV deviation of a token is the difference between its reused and its recomputed KV;
+ * §1.3.3: each layer keeps, among the tokens the previous layer selected, those of highest
+ * deviation). For each of the n_prev context rows r of row_pos_prev, at p = row_pos_prev[q][r]:
+ *   dev[q][r] = || (round(R(p) k_new[q][r]) - k_fused[q][p],  v_new[q][r] - v_fused[q][p]) ||_2
+ * over every KV head and dimension (float64 sums, rounded to float32 once). Then row_pos_next[q]
+ * = the n_keep context rows of highest dev (float32 comparison, lower row on a tie) in ascending
+ * order, followed by the R_prev - n_prev query rows of row_pos_prev unchanged.
+ * k_fused, v_fused: [n_req][L][Hkv][d] reused cache (re-rotated, before this layer's scatter).
+ * k_new, v_new: [n_req][R_prev][Hkv][d] compact fresh rows aligned with row_pos_prev, K before
+ * rotary embedding (only the first n_prev rows are read). row_pos_prev: [n_req][R_prev], context
+ * rows ascending in [0, L). dev: out [n_req][n_prev]. row_pos_next: out
+ * [n_req][n_keep + R_prev - n_prev]. 0 <= n_keep <= n_prev <= R_prev <= L.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_ALIAS, SRA_E_HIP. */
+int sra_hkvd_select(const sra_shape* shape, int32_t n_req, const void* k_fused, const void* v_fused,
+                    int32_t L, const void* k_new, const void* v_new, const int32_t* row_pos_prev,
+                    int32_t R_prev, int32_t n_prev, int32_t n_keep, float* dev, int32_t* row_pos_next,
+                    hipStream_t stream);
+
 /* ------------------------------------------------------------------------ S4 */
 
 /* Location-aware sparse causal attention (QCFuse summary (zh) §2.A: discrete recomputed
@@ -257,7 +284,8 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
 
 /* One layer of the fusion step on one stream (KVCache reuse 01 §1.3.4 per-layer flow;
  * QCFuse summary (ja) §2 workflow): S1 re-rotation, then S2 scoring and selection when
- * args->q_crit is set (otherwise args->row_pos is taken as given), then S3 scatter of the
+ * args->q_crit is set, or gradual filtering of args->hkvd_prev when that is set (otherwise
+ * args->row_pos is taken as given), then S3 scatter of the
  * fresh K/V rows gathered from the position-indexed fresh buffers at row_pos, then S4
  * attention of those rows. Fills k_fused/v_fused (the cache handed on to decoding), out,
  * lse, row_pos and scores. ws: at least

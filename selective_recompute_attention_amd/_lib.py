@@ -42,6 +42,8 @@ class LayerArgs(ctypes.Structure):
         ("n_select", ctypes.c_int32), ("chunk_quota", ctypes.POINTER(ctypes.c_int32)),
         ("scores", ctypes.c_void_p),
         ("anchors_k", ctypes.c_int32), ("anchor_rows", ctypes.c_void_p), ("anchor_norms", ctypes.c_void_p),
+        ("hkvd_prev", ctypes.c_void_p), ("hkvd_prev_rows", ctypes.c_int32), ("hkvd_prev_ctx", ctypes.c_int32),
+        ("hkvd_dev", ctypes.c_void_p),
         ("q_fresh", ctypes.c_void_p), ("k_fresh", ctypes.c_void_p), ("v_fresh", ctypes.c_void_p),
         ("row_pos", ctypes.c_void_p), ("n_rows", ctypes.c_int32),
         ("k_fused", ctypes.c_void_p), ("v_fused", ctypes.c_void_p),
@@ -68,6 +70,8 @@ _SIGS = {
                                    _c.POINTER(Chunk), _c.c_int32, _c.c_int32, _P, _P]),
     "sra_scatter_kv": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _P, _c.c_int32, _P, _P,
                                   _c.c_int32, _P]),
+    "sra_hkvd_select": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int32, _P, _P, _P, _c.c_int32,
+                                   _c.c_int32, _c.c_int32, _P, _P, _P]),
     "sra_sparse_causal_attn": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int32, _P, _P,
                                           _c.c_int32, _P, _P, _P, _c.c_size_t, _P]),
     "sra_fused_layer": (_c.c_int, [_c.POINTER(LayerArgs), _P, _c.c_size_t, _P]),

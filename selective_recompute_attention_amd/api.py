@@ -13,7 +13,7 @@ import torch
 from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, check, lib)  # noqa: F401
 
 __all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors",
-           "score_select", "select_topn", "scatter_kv", "sparse_causal_attn", "fused_layer",
+           "score_select", "select_topn", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
            "check_rows", "chunk_array", "SRAError"]
 
 
@@ -117,6 +117,16 @@ def scatter_kv(shape, k_new, v_new, row_pos, k_fused, v_fused, stream=None):
                                _ptr(k_fused), _ptr(v_fused), k_fused.shape[-3], _stream(stream)))
 
 
+def hkvd_select(shape, k_fused, v_fused, k_new, v_new, row_pos_prev, n_prev, n_keep, dev, row_pos_next,
+                stream=None):
+    """KV deviation of the previous rows' first n_prev context rows (dev [n_req][n_prev] float32) and the
+    next layer's rows (row_pos_next [n_req][n_keep + R_prev - n_prev]): see sra_hkvd_select."""
+    n_req, R_prev = row_pos_prev.shape
+    check(lib().sra_hkvd_select(ctypes.byref(shape), n_req, _ptr(k_fused), _ptr(v_fused), k_fused.shape[-3],
+                                _ptr(k_new), _ptr(v_new), _ptr(row_pos_prev), R_prev, int(n_prev), int(n_keep),
+                                _ptr(dev), _ptr(row_pos_next), _stream(stream)))
+
+
 def sparse_causal_attn(shape, q_new, row_pos, k_fused, v_fused, out, lse, ws, stream=None):
     n_req, R = row_pos.shape
     check(lib().sra_sparse_causal_attn(ctypes.byref(shape), n_req, _ptr(q_new), _ptr(row_pos), R,
@@ -126,10 +136,13 @@ def sparse_causal_attn(shape, q_new, row_pos, k_fused, v_fused, out, lse, ws, st
 
 def fused_layer(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, row_pos, k_fused, v_fused,
                 out, ws, lse=None, q_crit=None, k_crit_store=None, n_select=None, quotas=None, scores=None,
-                anchors_k=0, anchor_rows=None, anchor_norms=None, stage_events=None, stream=None):
+                anchors_k=0, anchor_rows=None, anchor_norms=None, hkvd_prev=None, hkvd_prev_ctx=0,
+                hkvd_dev=None, stage_events=None, stream=None):
     """stage_events: optional ctypes array of 8 hipEvent_t handles (see sra_layer_args).
     anchors_k > 0 also extracts key-norm anchors of every (request, chunk) into anchor_rows
-    [n_req][n_chunks][anchors_k] (int32) and, when given, anchor_norms [crit_store_rows] (float32)."""
+    [n_req][n_chunks][anchors_k] (int32) and, when given, anchor_norms [crit_store_rows] (float32).
+    hkvd_prev [n_req][hkvd_prev_ctx + Lq] (int32) selects by gradual filtering: the n_select previous
+    context rows of highest KV deviation (written to hkvd_dev [n_req][hkvd_prev_ctx]) are recomputed."""
     ch = np.asarray(chunks, dtype=np.int32)
     n_req, n_chunks = ch.shape[0], ch.shape[1]
     carr = chunk_array(ch)
@@ -148,6 +161,9 @@ def fused_layer(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, r
     a.chunk_quota = qp
     a.scores = _ptr(scores)
     a.anchors_k, a.anchor_rows, a.anchor_norms = int(anchors_k), _ptr(anchor_rows), _ptr(anchor_norms)
+    a.hkvd_prev, a.hkvd_dev = _ptr(hkvd_prev), _ptr(hkvd_dev)
+    a.hkvd_prev_rows = hkvd_prev.shape[1] if hkvd_prev is not None else 0
+    a.hkvd_prev_ctx = int(hkvd_prev_ctx)
     a.q_fresh, a.k_fresh, a.v_fresh = _ptr(q_fresh), _ptr(k_fresh), _ptr(v_fresh)
     a.row_pos, a.n_rows = _ptr(row_pos), row_pos.shape[1]
     a.k_fused, a.v_fused, a.out, a.lse = _ptr(k_fused), _ptr(v_fused), _ptr(out), _ptr(lse)

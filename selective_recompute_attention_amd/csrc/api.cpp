@@ -279,6 +279,33 @@ int do_select(int n_req, int Lctx, int Lq, int R, int N, const int32_t* quota, c
   return SRA_OK;
 }
 
+// Gradual filtering: deviation of the previous layer's n_prev context rows, then per request the
+// n_keep rows of highest deviation (ascending), mapped back to their positions, then the query rows.
+int do_hkvd(const sra_shape* s, int n_req, const void* kn, const void* vn, int fresh_rows, int indexed,
+            const int32_t* prev, int R_prev, int n_prev, const void* kf, const void* vf, int L, int n_keep,
+            float* dev, int32_t* rows_out, hipStream_t st) {
+  hipError_t e = sra::launch_kv_deviation(s->dtype, s->head_dim, s->n_kv_heads, n_req, R_prev, L, kn, vn,
+                                          fresh_rows, indexed, prev, kf, vf, dev, n_prev, s->rope_base, st);
+  if (e != hipSuccess) return hip_fail(e, "deviation launch");
+  const int Lq = R_prev - n_prev;
+  for (int q0 = 0; q0 < n_req; q0 += sra::kMaxEntries) {
+    sra::SelTab tab;
+    std::memset(&tab, 0, sizeof(tab));
+    for (int q = q0; q < n_req && tab.n < sra::kMaxEntries; ++q) {
+      tab.req[tab.n] = q;
+      tab.begin[tab.n] = 0;
+      tab.len[tab.n] = n_prev;
+      tab.quota[tab.n] = n_keep;
+      tab.out_off[tab.n] = 0;
+      tab.writes_query[tab.n] = 1;
+      ++tab.n;
+    }
+    e = sra::launch_select(tab, nullptr, 0, n_prev, Lq, n_keep + Lq, nullptr, dev, rows_out, st, prev, R_prev);
+    if (e != hipSuccess) return hip_fail(e, "selection launch");
+  }
+  return SRA_OK;
+}
+
 // Validates quota/n_select and returns N (selected context tokens per request).
 int resolve_count(int n_req, int n_chunks, const sra_chunk* ch, int Lctx, int n_select,
                   const int32_t* quota, int* N) {
@@ -587,6 +614,30 @@ int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, con
   return ok();
 }
 
+int sra_hkvd_select(const sra_shape* shape, int32_t n_req, const void* k_fused, const void* v_fused,
+                    int32_t L, const void* k_new, const void* v_new, const int32_t* row_pos_prev,
+                    int32_t R_prev, int32_t n_prev, int32_t n_keep, float* dev, int32_t* row_pos_next,
+                    hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (n_req <= 0 || L <= 0 || n_prev < 0 || R_prev < n_prev || R_prev > L || n_keep < 0 || n_keep > n_prev)
+    return fail(SRA_E_SHAPE, "need n_req > 0, 0 <= n_keep <= n_prev <= R_prev <= L");
+  if ((rc = check_ptr(k_fused, "k_fused")) || (rc = check_ptr(v_fused, "v_fused")) ||
+      (rc = check_ptr(k_new, "k_new")) || (rc = check_ptr(v_new, "v_new")))
+    return rc;
+  if (!row_pos_prev || !row_pos_next || !dev) return fail(SRA_E_NULL, "row_pos_prev, row_pos_next or dev is NULL");
+  const size_t ib = (size_t)n_req * R_prev * sizeof(int32_t);
+  const size_t ob = (size_t)n_req * (n_keep + (R_prev - n_prev)) * sizeof(int32_t);
+  const size_t db = (size_t)n_req * n_prev * sizeof(float);
+  if (overlap(row_pos_prev, ib, row_pos_next, ob) || overlap(dev, db, row_pos_next, ob) ||
+      overlap(dev, db, row_pos_prev, ib))
+    return fail(SRA_E_ALIAS, "row_pos_prev, row_pos_next and dev must not overlap");
+  if ((rc = do_hkvd(shape, n_req, k_new, v_new, R_prev, 0, row_pos_prev, R_prev, n_prev, k_fused, v_fused, L,
+                    n_keep, dev, row_pos_next, stream)))
+    return rc;
+  return ok();
+}
+
 int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_new,
                            const int32_t* row_pos, int32_t R, const void* k_fused,
                            const void* v_fused, int32_t L, void* out, float* lse, void* ws,
@@ -651,6 +702,20 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
       overlap(a->v_fresh, fb, a->k_fused, fb))
     return fail(SRA_E_ALIAS, "an input buffer overlaps an output buffer");
   int N = R - Lq;
+  const bool hkvd = a->hkvd_prev != nullptr;
+  if (hkvd) {
+    if (a->q_crit) return fail(SRA_E_SHAPE, "gradual filtering and scoring are exclusive: q_crit must be NULL");
+    if (!a->hkvd_dev) return fail(SRA_E_NULL, "hkvd_dev is NULL");
+    const int npv = a->hkvd_prev_ctx;
+    if (npv < 0 || a->hkvd_prev_rows != npv + Lq || npv > Lctx)
+      return fail(SRA_E_SHAPE, "hkvd_prev_rows %d != hkvd_prev_ctx %d + query %d", a->hkvd_prev_rows, npv, Lq);
+    if (a->n_select < 0 || a->n_select > npv)
+      return fail(SRA_E_SHAPE, "n_select %d outside [0, hkvd_prev_ctx = %d]", a->n_select, npv);
+    N = a->n_select;
+    if (N + Lq != R) return fail(SRA_E_SHAPE, "n_rows %d != kept %d + query %d", R, N, Lq);
+    const size_t ib = (size_t)n_req * a->hkvd_prev_rows * sizeof(int32_t), rb = (size_t)n_req * R * sizeof(int32_t);
+    if (overlap(a->hkvd_prev, ib, a->row_pos, rb)) return fail(SRA_E_ALIAS, "hkvd_prev overlaps row_pos");
+  }
   if (a->q_crit) {
     if (Lq < 1) return fail(SRA_E_SHAPE, "scoring needs at least one query row");
     if ((rc = check_ptr(a->k_crit_store, "k_crit_store"))) return rc;
@@ -691,6 +756,11 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
                         a->v_fused, L, stream)))
     return rc;
   if ((rc = mark(1)) || (rc = mark(2))) return rc;
+  if (hkvd) {   // deviation against the re-rotated reused rows, before the scatter replaces them
+    if ((rc = do_hkvd(s, n_req, a->k_fresh, a->v_fresh, L, 1, a->hkvd_prev, a->hkvd_prev_rows, a->hkvd_prev_ctx,
+                      a->k_fused, a->v_fused, L, N, a->hkvd_dev, a->row_pos, stream)))
+      return rc;
+  }
   if (a->q_crit) {
     sra::AnchorOut anc;
     if (anchors_fused) {   // the scoring passes take the anchors from their own K loads

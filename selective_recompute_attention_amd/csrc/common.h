@@ -198,6 +198,12 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
                           hipStream_t st);
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
                              double base, hipStream_t st);
+// KV deviation of the first n_dev recomputed rows (dev: [n_req][n_dev] float32). Fresh rows are
+// compact or position-indexed as in launch_scatter; kf/vf hold the reused rows (not yet scattered).
+hipError_t launch_kv_deviation(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
+                               const void* vn, int fresh_rows, int indexed, const int* row_pos,
+                               const void* kf, const void* vf, float* dev, int n_dev, double base,
+                               hipStream_t st);
 // tab: entries = chunks (src, len), dst = output slot, delta = offset of the chunk's sums in ss,
 // blk0 in blocks of anchor_rows_per_block(Hkv) rows.
 hipError_t launch_anchors(int dtype, int Hkv, int D, const ChunkTab& tab, int k, const void* ks,
@@ -233,9 +239,11 @@ hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, i
 hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, float* parts,
                              hipStream_t st);
 // Scores come from fixed-point totals (fx), from nparts float partials added in order, or (both
-// absent) from `scores` itself.
+// absent) from `scores` itself. With map, every written index i becomes map[req * map_stride + i]
+// (the query rows are indices Lctx .. Lctx + Lq - 1).
 hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
-                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st);
+                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
+                         const int* map = nullptr, int map_stride = 0);
 // qop: prepared query operand (qop_blocks blocks of 32 vectors per group); tilecum: [n_req][tiles+1]
 // ints; part_o / part_ml: [n_groups][pieces][2][128] partial results.
 hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,

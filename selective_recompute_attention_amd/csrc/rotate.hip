@@ -259,6 +259,90 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
   }
 }
 
+// KV deviation of recomputed rows (KVCache reuse 01, §1.3.2-§1.3.3: tokens are ranked by the
+// difference between their reused and their recomputed KV). One block per (row r < n_dev,
+// request), at p = row_pos[r]: the Euclidean norm over every KV head and dimension of the fresh K
+// rotated at p and rounded as the scatter stores it, minus the reused K at p, together with the
+// fresh V minus the reused V. Differences and squares are float64; the block total is rounded to
+// float32 once. Fresh rows are compact (row r) or position-indexed (row p). Rows must lie in
+// [0, L) (the row check's contract); others are measured at row 0.
+template <typename T, int D>
+__global__ __launch_bounds__(128) void k_kv_deviation(int Hkv, int R, int L, const T* __restrict__ kn,
+                                                      const T* __restrict__ vn, int fresh_rows,
+                                                      int indexed, const int* __restrict__ row_pos,
+                                                      const T* __restrict__ kf, const T* __restrict__ vf,
+                                                      float* __restrict__ dev, int n_dev, Theta th) {
+  constexpr int H = D / 2;
+  constexpr int VW = Vec<T>::N;
+  constexpr int UPH = H / VW;
+  constexpr int NT = 128;
+  __shared__ float2 cs[H];
+  __shared__ double wtot[NT / 64];
+  const int r = blockIdx.x, q = blockIdx.y;
+  const int p0 = row_pos[(int64_t)q * R + r];
+  const int p = (p0 >= 0 && p0 < L) ? p0 : 0;
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t src0 = ((int64_t)q * fresh_rows + (indexed ? p : r)) * row_elems;
+  const int64_t old0 = ((int64_t)q * L + p) * row_elems;
+  const int nV = (int)(row_elems * (int64_t)sizeof(T) / 16), nK = Hkv * UPH;
+  // first batch (V chunk tid, K pair tid, fresh and reused) before the angles are formed
+  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vn + src0);
+  const u32x4* vold = reinterpret_cast<const u32x4*>(vf + old0);
+  const int u0 = min((int)threadIdx.x, nK - 1);
+  const int64_t k0 = (u0 / UPH) * D + (u0 % UPH) * VW;
+  u32x4 va = vsrc[min((int)threadIdx.x, nV - 1)], vb = vold[min((int)threadIdx.x, nV - 1)];
+  u32x4 ka = *reinterpret_cast<const u32x4*>(kn + src0 + k0), kb = *reinterpret_cast<const u32x4*>(kn + src0 + k0 + H);
+  u32x4 oa = *reinterpret_cast<const u32x4*>(kf + old0 + k0), ob = *reinterpret_cast<const u32x4*>(kf + old0 + k0 + H);
+  for (int i = threadIdx.x; i < H; i += NT) cs[i] = rope_cs((double)p, th.v[i]);
+  __syncthreads();
+
+  double acc = 0.0;
+  auto vdiff = [&](u32x4 a, u32x4 b) {
+    float fa[VW], fb[VW];
+    Vec<T>::unpack(a, fa);
+    Vec<T>::unpack(b, fb);
+#pragma unroll
+    for (int k = 0; k < VW; ++k) {
+      const double d = (double)fa[k] - (double)fb[k];
+      acc += d * d;
+    }
+  };
+  // the fresh pair rotated at p exactly as the scatter computes and rounds it
+  auto kdiff = [&](int u, u32x4 a, u32x4 b, u32x4 oa_, u32x4 ob_) {
+    const int i0 = (u % UPH) * VW;
+    float fa[VW], fb[VW], ra[VW], rb[VW];
+    Vec<T>::unpack(a, fa);
+    Vec<T>::unpack(b, fb);
+#pragma unroll
+    for (int k = 0; k < VW; ++k) {
+      const float c = cs[i0 + k].x, sn = cs[i0 + k].y;
+      ra[k] = fa[k] * c - fb[k] * sn;
+      rb[k] = fa[k] * sn + fb[k] * c;
+    }
+    vdiff(Vec<T>::pack(ra), oa_);
+    vdiff(Vec<T>::pack(rb), ob_);
+  };
+  if ((int)threadIdx.x < nV) vdiff(va, vb);
+  for (int u = threadIdx.x + NT; u < nV; u += NT) vdiff(vsrc[u], vold[u]);
+  if ((int)threadIdx.x < nK) kdiff(threadIdx.x, ka, kb, oa, ob);
+  for (int u = threadIdx.x + NT; u < nK; u += NT) {
+    const int64_t o = (u / UPH) * D + (u % UPH) * VW;
+    kdiff(u, *reinterpret_cast<const u32x4*>(kn + src0 + o), *reinterpret_cast<const u32x4*>(kn + src0 + o + H),
+          *reinterpret_cast<const u32x4*>(kf + old0 + o), *reinterpret_cast<const u32x4*>(kf + old0 + o + H));
+  }
+  // block total in a fixed order: lane tree within each wave, then the waves in order
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) t += wtot[w];
+    dev[(int64_t)q * n_dev + r] = (float)sqrt(t);
+  }
+}
+
 template <int D>
 __global__ void k_rope_table(int R, const int* __restrict__ row_pos, float2* __restrict__ cs_out,
                              Theta th) {
@@ -330,6 +414,35 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
     k_scatter<float, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
                                            (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
                                            (float*)vf, cs_out, nullptr, 0, scale_log2, th);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_deviation(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,
+                               const void* vn, int fresh_rows, int indexed, const int* row_pos,
+                               const void* kf, const void* vf, float* dev, int n_dev, double base,
+                               hipStream_t st) {
+  if (n_dev == 0 || n_req == 0) return hipSuccess;
+  const dim3 g((unsigned)n_dev, (unsigned)n_req), b(128);
+  const Theta th = make_theta(D, base);
+  if (dtype == 0) {
+    auto k = (const uint16_t*)kn;
+    auto v = (const uint16_t*)vn;
+    if (D == 128)
+      k_kv_deviation<uint16_t, 128><<<g, b, 0, st>>>(Hkv, R, L, k, v, fresh_rows, indexed, row_pos,
+                                                     (const uint16_t*)kf, (const uint16_t*)vf, dev, n_dev, th);
+    else
+      k_kv_deviation<uint16_t, 64><<<g, b, 0, st>>>(Hkv, R, L, k, v, fresh_rows, indexed, row_pos,
+                                                    (const uint16_t*)kf, (const uint16_t*)vf, dev, n_dev, th);
+  } else {
+    auto k = (const float*)kn;
+    auto v = (const float*)vn;
+    if (D == 128)
+      k_kv_deviation<float, 128><<<g, b, 0, st>>>(Hkv, R, L, k, v, fresh_rows, indexed, row_pos,
+                                                  (const float*)kf, (const float*)vf, dev, n_dev, th);
+    else
+      k_kv_deviation<float, 64><<<g, b, 0, st>>>(Hkv, R, L, k, v, fresh_rows, indexed, row_pos,
+                                                 (const float*)kf, (const float*)vf, dev, n_dev, th);
+  }
   return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
                                                         int nparts, int Lctx, int Lq, int R,
                                                         const float* __restrict__ parts,
                                                         float* __restrict__ scores,
-                                                        int* __restrict__ row_pos) {
+                                                        int* __restrict__ row_pos,
+                                                        const int* __restrict__ map, int map_stride) {
   constexpr int NW = kSelThreads / 64;
   constexpr int KREG = 16;   // keys per thread held in registers (units up to 4096 keys)
   constexpr int kSub = 4;
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
   const int quota = tab.quota[e], off = tab.out_off[e];
   float* srow = scores + (int64_t)req * Lctx + begin;
   int* out = row_pos + (int64_t)req * R;
+  const int* mrow = map ? map + (int64_t)req * map_stride : nullptr;   // index -> written value
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // thread t owns the contiguous positions [jlo, jhi): block prefix sums of per-thread counts then
   // give ascending output slots
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
         ++eq_rank;
       }
       if (take) {
-        if (pos < quota) out[off + pos] = begin + j;
+        if (pos < quota) out[off + pos] = mrow ? mrow[begin + j] : begin + j;
         ++pos;
       }
     };
@@ -266,16 +268,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
     }
   }
   if (tab.writes_query[e]) {
-    for (int i = threadIdx.x; i < Lq; i += blockDim.x) out[R - Lq + i] = Lctx + i;
+    for (int i = threadIdx.x; i < Lq; i += blockDim.x) out[R - Lq + i] = mrow ? mrow[Lctx + i] : Lctx + i;
   }
 }
 
 }  // namespace
 
 hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
-                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st) {
+                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
+                         const int* map, int map_stride) {
   if (tab.n == 0) return hipSuccess;
-  k_select<<<dim3(tab.n), dim3(kSelThreads), 0, st>>>(tab, fx, nparts, Lctx, Lq, R, parts, scores, row_pos);
+  k_select<<<dim3(tab.n), dim3(kSelThreads), 0, st>>>(tab, fx, nparts, Lctx, Lq, R, parts, scores, row_pos,
+                                                      map, map_stride);
   return hipGetLastError();
 }
 

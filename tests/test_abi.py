@@ -180,3 +180,44 @@ def test_fused_layer_host_errors():
     a.out = FAKE[8]
     assert lib.sra_fused_layer(ctypes.byref(a), None, 0, None) == L.SRA_E_WORKSPACE
     assert lib.sra_fused_layer(None, None, 0, None) == L.SRA_E_NULL
+
+
+def test_hkvd_host_errors():
+    lib = L.lib()
+    s = shape()
+    ok_args = [FAKE[0], FAKE[1], 100, FAKE[2], FAKE[3], FAKE[4], 40, 30, 20, FAKE[5], FAKE[6], None]
+    def call(**kw):
+        a = list(ok_args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.sra_hkvd_select(ctypes.byref(s), 1, *a)
+    assert call(a9=None) == L.SRA_E_NULL                     # dev
+    assert call(a10=None) == L.SRA_E_NULL                    # row_pos_next
+    assert call(a8=31) == L.SRA_E_SHAPE                      # n_keep > n_prev
+    assert call(a7=41) == L.SRA_E_SHAPE                      # n_prev > R_prev
+    assert call(a6=101) == L.SRA_E_SHAPE                     # R_prev > L
+    assert call(a10=FAKE[4]) == L.SRA_E_ALIAS                # next rows written over the previous rows
+    assert call(a0=None) == L.SRA_E_NULL
+    # the fused layer's filtering mode
+    ch = chunks([[0, 64, 0, 0], [64, 64, 64, 0]])
+    a = L.LayerArgs()
+    a.shape = shape()
+    a.n_req, a.n_chunks, a.chunks = 1, 2, ctypes.cast(ch, ctypes.POINTER(L.Chunk))
+    a.query_len, a.total_len = 8, 136
+    a.k_store, a.v_store, a.store_rows = FAKE[0], FAKE[1], 128
+    a.q_fresh, a.k_fresh, a.v_fresh = FAKE[2], FAKE[3], FAKE[4]
+    a.row_pos, a.n_rows = FAKE[5], 20
+    a.k_fused, a.v_fused, a.out = FAKE[6], FAKE[7], FAKE[8]
+    a.hkvd_prev, a.hkvd_prev_rows, a.hkvd_prev_ctx, a.hkvd_dev, a.n_select = FAKE[9], 38, 30, FAKE[10], 12
+    a.q_crit, a.k_crit_store, a.crit_store_rows = FAKE[11], FAKE[12], 128
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_SHAPE   # with q_crit
+    a.q_crit = None
+    a.hkvd_dev = None
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_NULL
+    a.hkvd_dev = FAKE[10]
+    a.hkvd_prev_rows = 37                                                                  # != ctx + Lq
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_SHAPE
+    a.hkvd_prev_rows, a.n_select = 38, 31                                                  # keeps more than given
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_SHAPE
+    a.n_select, a.hkvd_prev = 12, FAKE[5]                                                  # prev == row_pos
+    assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_ALIAS
