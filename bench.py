@@ -102,6 +102,139 @@ def traffic_for(kernel_key):
     return ent.get("bytes_per_launch")
 
 
+def timed_calls(hip, sp, fn, n):
+    """Mean duration of n back-to-back calls of fn on the stream, from HIP events on it."""
+    import torch
+    a, b = hip.event(), hip.event()
+    fn()
+    torch.cuda._sleep(int(2e7))   # everything below is queued before the GPU reaches it
+    assert hip.h.hipEventRecord(a, sp) == 0
+    for _ in range(n):
+        fn()
+    assert hip.h.hipEventRecord(b, sp) == 0
+    return hip.elapsed_ms(a, b) / n
+
+
+def hkvd_leg(sra, shape, rep, N, Lq, Lctx, kv_row_bytes, hip, sp):
+    """Gradual filtering at this layer's shape: deviation of the N recomputed context rows against
+    the reused cache, then the rows of the next (13%) layer. Algorithmic bytes: fresh and reused K
+    and V of every measured row."""
+    import torch
+    ins, outs = rep
+    prev = outs["row_pos"].clone()
+    rp = prev.long()[0]
+    kn = ins["k_new"][0][rp].unsqueeze(0).contiguous()
+    vn = ins["v_new"][0][rp].unsqueeze(0).contiguous()
+    keep = sra.select_count(13, 100, Lctx)
+    dev = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    nxt = torch.empty((1, keep + Lq), dtype=torch.int32, device="cuda")
+    ms = timed_calls(hip, sp, lambda: sra.hkvd_select(shape, outs["k_fused"], outs["v_fused"], kn, vn, prev, N,
+                                                       keep, dev, nxt), 50)
+    byts = 4.0 * kv_row_bytes * N
+    return {"rows": N, "keep": keep, "ms_per_call": ms, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
+            "algorithmic_bytes": byts, "kernels": "k_kv_deviation + k_select"}
+
+
+def pipeline_leg(sra, shape, w, ins, ws, Lq, Lctx, hip, sp, n_layers=8):
+    """Eight layers of this shape with the CacheBlend-style taper N_l = ceil((14 - l) L_ctx / 70)
+    (layer 0 by the critical-layer score, later layers by gradual filtering), each layer's chunk
+    store (K and V) coming from pinned host memory. Timed three ways on HIP events: the host-to-
+    device copies alone, the layers alone (stores already on the device), and the pipelined run
+    where layer l+1's copy overlaps layer l's step."""
+    import torch
+    cfg = w.cfg
+    L, Hq, Hkv, D = Lctx + Lq, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    counts = [sra.select_count(14 - l, 70, Lctx) for l in range(n_layers)]
+    ws = torch.empty(sra.workspace_size(shape, 1, w.chunks.shape[1], L, counts[0] + Lq, Lq), dtype=torch.uint8,
+                     device="cuda")   # sized for the largest layer
+    S = ins["k_store"].shape[0]
+    store_bytes = ins["k_store"].numel() * 2
+    hk = torch.empty(ins["k_store"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty(ins["v_store"].shape, dtype=torch.bfloat16, pin_memory=True)
+    hk.copy_(ins["k_store"])
+    hv.copy_(ins["v_store"])
+    # one device buffer pair per layer (168 MB here): the copy stream never waits for compute
+    k_buf = [torch.empty_like(ins["k_store"]) for _ in range(n_layers)]
+    v_buf = [torch.empty_like(ins["v_store"]) for _ in range(n_layers)]
+    outs = []
+    for l, n in enumerate(counts):
+        R = n + Lq
+        outs.append({"k_fused": torch.empty((1, L, Hkv, D), dtype=torch.bfloat16, device="cuda"),
+                     "v_fused": torch.empty((1, L, Hkv, D), dtype=torch.bfloat16, device="cuda"),
+                     "out": torch.empty((1, R, Hq, D), dtype=torch.bfloat16, device="cuda"),
+                     "row_pos": torch.empty((1, R), dtype=torch.int32, device="cuda"),
+                     "dev": torch.empty((1, counts[l - 1] if l else 1), dtype=torch.float32, device="cuda"),
+                     "scores": torch.empty((1, Lctx), dtype=torch.float32, device="cuda")})
+    layers = []
+    for l in range(n_layers):
+        kw = dict(chunks=w.chunks, q_fresh=ins["q_new"], k_fresh=ins["k_new"], v_fresh=ins["v_new"],
+                  row_pos=outs[l]["row_pos"], k_fused=outs[l]["k_fused"], v_fused=outs[l]["v_fused"],
+                  out=outs[l]["out"], n_select=counts[l], store_rows=S)
+        if l == 0:
+            kw.update(q_crit=ins["q_crit"], k_crit_store=ins["k_crit"], scores=outs[l]["scores"])
+        else:
+            kw.update(hkvd_prev=outs[l - 1]["row_pos"], hkvd_prev_ctx=counts[l - 1], hkvd_dev=outs[l]["dev"])
+        layers.append(kw)
+    copy_stream = torch.cuda.Stream()
+    cp = ctypes.c_void_p(copy_stream.cuda_stream)
+    ev = sra.create_events(2 * n_layers)
+    stream = torch.cuda.current_stream()
+
+    def span(fn, st, reps=5):
+        a, b = hip.event(), hip.event()
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            assert hip.h.hipEventRecord(a, st) == 0
+            fn()
+            assert hip.h.hipEventRecord(b, st) == 0
+            ms.append(hip.elapsed_ms(a, b))
+            torch.cuda.synchronize()
+        return float(np.median(ms))
+
+    def copies():
+        with torch.cuda.stream(copy_stream):
+            for l in range(n_layers):
+                k_buf[l].copy_(hk, non_blocking=True)
+                v_buf[l].copy_(hv, non_blocking=True)
+
+    def compute():
+        for l in range(n_layers):
+            sra.fused_layer(shape, ws=ws, k_store=ins["k_store"], v_store=ins["v_store"],
+                            **{k: v for k, v in layers[l].items() if k != "store_rows"})
+
+    def pipelined():
+        sra.pipelined_layers(shape, layers, [hk] * n_layers, [hv] * n_layers, k_buf, v_buf, ev, ws,
+                             copy_stream=copy_stream)
+
+    try:
+        t_copy = span(copies, cp)
+        t_comp = span(compute, sp)
+        # the pipelined run starts with the first copy on the copy stream: bracket it on both
+        a, b = hip.event(), hip.event()
+        pipelined()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(5):
+            assert hip.h.hipEventRecord(a, cp) == 0
+            copy_stream.wait_stream(stream)
+            pipelined()
+            assert hip.h.hipEventRecord(b, sp) == 0
+            ms.append(hip.elapsed_ms(a, b))
+            torch.cuda.synchronize()
+        t_pipe = float(np.median(ms))
+    finally:
+        torch.cuda.synchronize()
+        sra.destroy_events(ev)
+    hidden = (t_copy + t_comp - t_pipe) / min(t_copy, t_comp)
+    return {"layers": n_layers, "counts": counts, "store_mb_per_layer": 2 * store_bytes / 1e6,
+            "copy_ms": t_copy, "compute_ms": t_comp, "pipelined_ms": t_pipe,
+            "h2d_gbs": n_layers * 2 * store_bytes / (t_copy * 1e-3) / 1e9,
+            "overlap_of_shorter": hidden,
+            "note": "pipelined_ms near max(copy_ms, compute_ms) means the recompute hides under the load"}
+
+
 def cpu_baseline(w, N, budget_s):
     """The fp64 oracle (as it stands) on the same workload: whole steps until the budget is used."""
     import oracle as O
@@ -247,6 +380,8 @@ def main():
         "scatter_hbm_gbs": s3_bytes / (stage_ms["scatter"] * 1e-3) / 1e9,
         "score_flops_tflops": s2_flops / (stage_ms["score_select"] * 1e-3) / 1e12,
     }
+    result["hkvd"] = hkvd_leg(sra, shape, reps[0], N, Lq, Lctx, kv_row_bytes, hip, sp)
+    result["pipeline"] = pipeline_leg(sra, shape, w, reps[0][0], ws, Lq, Lctx, hip, sp)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, N, args.cpu_seconds)
     # the parity of this exact output against the oracle is covered by the GPU tests

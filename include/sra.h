@@ -293,6 +293,30 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
  * Errors: as the stage calls. */
 int sra_fused_layer(const sra_layer_args* args, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Layer-pipelined reconstruction (QCFuse summary (zh) §2.A: while the GPU rebuilds layer i's
+ * selected tokens, layer i+1's KV cache is prefetched; KVCache reuse 01 §1.3.5: layer i's
+ * recompute runs in parallel with loading layer i+1's cache, and adds no latency when loading
+ * takes at least as long). Runs sra_fused_layer for layers[0 .. n_layers) in order on `stream`;
+ * layer l's chunk store is read from the device buffer pair (k_buf[l % n_buf], v_buf[l % n_buf],
+ * each store_bytes), filled from that layer's host store (host_k[l], host_v[l]; pinned host
+ * memory, store_rows * Hkv * d elements each) by hipMemcpyAsync on `copy_stream`. The copies
+ * start after the work already queued on `stream` (which may still read the buffers) and run
+ * back to back on copy_stream; the copy of layer l waits only for layer l - n_buf (the previous
+ * user of its buffer pair), so with n_buf >= n_layers the copy stream never waits, and layer l's
+ * step waits only for its own copy. The layers' k_store/v_store fields are ignored; every other
+ * field is as for sra_fused_layer (a layer may read an earlier layer's outputs, e.g. hkvd_prev =
+ * the previous layer's row_pos). n_buf in [2, 64]. events: 2 * n_buf caller-created events.
+ * ws is shared by the layers (sized for the largest). Every layer is validated before anything
+ * is enqueued; the caller keeps the host stores, buffers, events and streams alive until
+ * `stream` has passed the last layer.
+ * Errors: as sra_fused_layer; SRA_E_NULL (host stores, buffers, events), SRA_E_SHAPE (a store
+ * larger than store_bytes, n_buf out of range), SRA_E_ALIAS (buffers overlap each other or a
+ * layer's outputs). */
+int sra_pipelined_layers(const sra_layer_args* layers, int32_t n_layers, const void* const* host_k,
+                         const void* const* host_v, size_t store_bytes, void* const* k_buf,
+                         void* const* v_buf, int32_t n_buf, hipEvent_t* events, void* ws,
+                         size_t ws_bytes, hipStream_t stream, hipStream_t copy_stream);
+
 /* ------------------------------------------------------------------------ checks */
 
 /* Synchronous check that every row_pos[q] is strictly increasing with values in [0, L).

@@ -76,7 +76,25 @@ _SIGS = {
                                           _c.c_int32, _P, _P, _P, _c.c_size_t, _P]),
     "sra_fused_layer": (_c.c_int, [_c.POINTER(LayerArgs), _P, _c.c_size_t, _P]),
     "sra_check_rows": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int32), _P]),
+    "sra_pipelined_layers": (_c.c_int, [_c.POINTER(LayerArgs), _c.c_int32, _c.POINTER(_P), _c.POINTER(_P),
+                                        _c.c_size_t, _c.POINTER(_P), _c.POINTER(_P), _c.c_int32, _c.POINTER(_P),
+                                        _P, _c.c_size_t, _P, _P]),
 }
+
+_hip = None
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime, for the few calls the binding makes itself (event handles)."""
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventCreateWithFlags.restype = ctypes.c_int
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventDestroy.restype = ctypes.c_int
+        _hip = h
+    return _hip
 
 _lib = None
 

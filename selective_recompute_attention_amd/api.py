@@ -10,11 +10,11 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, check, lib)  # noqa: F401
+from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, check, hip_runtime, lib)  # noqa: F401
 
 __all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors",
            "score_select", "select_topn", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
-           "check_rows", "chunk_array", "SRAError"]
+           "pipelined_layers", "create_events", "destroy_events", "check_rows", "chunk_array", "SRAError"]
 
 
 def make_shape(n_q_heads: int, n_kv_heads: int, head_dim: int, dtype, rope_base: float = 10000.0) -> Shape:
@@ -134,26 +134,23 @@ def sparse_causal_attn(shape, q_new, row_pos, k_fused, v_fused, out, lse, ws, st
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def fused_layer(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, row_pos, k_fused, v_fused,
-                out, ws, lse=None, q_crit=None, k_crit_store=None, n_select=None, quotas=None, scores=None,
+def _layer_args(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, row_pos, k_fused, v_fused,
+                out, lse=None, q_crit=None, k_crit_store=None, n_select=None, quotas=None, scores=None,
                 anchors_k=0, anchor_rows=None, anchor_norms=None, hkvd_prev=None, hkvd_prev_ctx=0,
-                hkvd_dev=None, stage_events=None, stream=None):
-    """stage_events: optional ctypes array of 8 hipEvent_t handles (see sra_layer_args).
-    anchors_k > 0 also extracts key-norm anchors of every (request, chunk) into anchor_rows
-    [n_req][n_chunks][anchors_k] (int32) and, when given, anchor_norms [crit_store_rows] (float32).
-    hkvd_prev [n_req][hkvd_prev_ctx + Lq] (int32) selects by gradual filtering: the n_select previous
-    context rows of highest KV deviation (written to hkvd_dev [n_req][hkvd_prev_ctx]) are recomputed."""
+                hkvd_dev=None, stage_events=None, store_rows=None):
+    """A filled sra_layer_args and the host arrays it points to (keep both alive during the call)."""
     ch = np.asarray(chunks, dtype=np.int32)
     n_req, n_chunks = ch.shape[0], ch.shape[1]
     carr = chunk_array(ch)
-    _qa, qp = _quota_array(quotas)
+    qa, qp = _quota_array(quotas)
     L = k_fused.shape[-3]
     Lq = q_crit.shape[1] if q_crit is not None else L - int(ch[0, :, 1].sum())
     a = LayerArgs()
     a.shape = shape
     a.n_req, a.n_chunks, a.chunks = n_req, n_chunks, ctypes.cast(carr, ctypes.POINTER(Chunk))
     a.query_len, a.total_len = Lq, L
-    a.k_store, a.v_store, a.store_rows = _ptr(k_store), _ptr(v_store), k_store.shape[0]
+    a.k_store, a.v_store = _ptr(k_store), _ptr(v_store)
+    a.store_rows = k_store.shape[0] if store_rows is None else int(store_rows)
     a.q_crit = _ptr(q_crit)
     a.k_crit_store = _ptr(k_crit_store)
     a.crit_store_rows = k_crit_store.shape[0] if k_crit_store is not None else 0
@@ -169,7 +166,63 @@ def fused_layer(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, r
     a.k_fused, a.v_fused, a.out, a.lse = _ptr(k_fused), _ptr(v_fused), _ptr(out), _ptr(lse)
     if stage_events is not None:
         a.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
+    return a, (carr, qa)
+
+
+def fused_layer(shape, *, ws, stream=None, **kw):
+    """One layer (sra_fused_layer). Keyword arguments as the fields of sra_layer_args:
+    chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, row_pos, k_fused, v_fused, out; optional lse,
+    q_crit, k_crit_store, n_select, quotas, scores; anchors_k > 0 with anchor_rows
+    [n_req][n_chunks][anchors_k] (int32) and optional anchor_norms [crit_store_rows] (float32);
+    hkvd_prev [n_req][hkvd_prev_ctx + Lq] (int32) to select by gradual filtering (the n_select
+    previous context rows of highest KV deviation, written to hkvd_dev [n_req][hkvd_prev_ctx]);
+    stage_events: optional ctypes array of 8 hipEvent_t handles."""
+    a, keep = _layer_args(shape, **kw)
     check(lib().sra_fused_layer(ctypes.byref(a), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    del keep
+
+
+def create_events(n: int = 4):
+    """n hipEvent_t handles (timing disabled) for pipelined_layers; release with destroy_events."""
+    arr = (ctypes.c_void_p * n)()
+    for i in range(n):
+        e = ctypes.c_void_p()
+        if hip_runtime().hipEventCreateWithFlags(ctypes.byref(e), 2) != 0:   # hipEventDisableTiming
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        arr[i] = e.value
+    return arr
+
+
+def destroy_events(arr):
+    for e in arr:
+        if e:
+            hip_runtime().hipEventDestroy(ctypes.c_void_p(e))
+
+
+def pipelined_layers(shape, layers, host_k, host_v, k_buf, v_buf, events, ws, stream=None, copy_stream=None):
+    """Layers in order with each layer's chunk store prefetched from pinned host memory on
+    copy_stream while the previous layer runs (sra_pipelined_layers). layers: one dict of
+    fused_layer keyword arguments per layer, without k_store/v_store (store_rows given instead);
+    host_k/host_v: pinned host tensors per layer; k_buf/v_buf: n_buf >= 2 device buffers each (bytes
+    of the largest store; n_buf >= len(layers) keeps the copy stream from ever waiting); events:
+    create_events(2 * n_buf)."""
+    n = len(layers)
+    args = (LayerArgs * n)()
+    keep = []
+    for l, kw in enumerate(layers):
+        a, k = _layer_args(shape, k_store=None, v_store=None, **kw)
+        args[l] = a
+        keep.append(k)
+    hk = (ctypes.c_void_p * n)(*[t.data_ptr() for t in host_k])
+    hv = (ctypes.c_void_p * n)(*[t.data_ptr() for t in host_v])
+    nb = len(k_buf)
+    kb = (ctypes.c_void_p * nb)(*[t.data_ptr() for t in k_buf])
+    vb = (ctypes.c_void_p * nb)(*[t.data_ptr() for t in v_buf])
+    nbytes = min(t.numel() * t.element_size() for t in list(k_buf) + list(v_buf))
+    cs = ctypes.c_void_p(copy_stream.cuda_stream) if copy_stream is not None else None
+    check(lib().sra_pipelined_layers(args, n, hk, hv, nbytes, kb, vb, nb, events, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream), cs))
+    del keep
 
 
 def check_rows(row_pos, L: int, stream=None) -> int:

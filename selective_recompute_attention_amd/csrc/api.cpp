@@ -672,7 +672,12 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
   return ok();
 }
 
-int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates one layer's arguments and, unless dry, enqueues its stages on `stream`.
+int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream, bool dry) {
   int rc;
   if (!a) return fail(SRA_E_NULL, "args is NULL");
   const sra_shape* s = &a->shape;
@@ -743,6 +748,7 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
   const Plan p = make_plan(s, n_req, a->n_chunks, L, R, Lq);
   const size_t need = a->q_crit ? p.total : p.attn_end;
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+  if (dry) return SRA_OK;
 
   hipEvent_t* ev = a->stage_events;
   auto mark = [&](int i) -> int {
@@ -805,6 +811,83 @@ int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStrea
                     a->lse, ws, p, stream)))
     return rc;
   if ((rc = mark(7))) return rc;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fused_layer_impl(a, ws, ws_bytes, stream, false);
+}
+
+int sra_pipelined_layers(const sra_layer_args* layers, int32_t n_layers, const void* const* host_k,
+                         const void* const* host_v, size_t store_bytes, void* const* k_buf, void* const* v_buf,
+                         int32_t n_buf, hipEvent_t* events, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipStream_t copy_stream) {
+  int rc;
+  if (!layers || !host_k || !host_v || !k_buf || !v_buf || !events)
+    return fail(SRA_E_NULL, "layers, host stores, buffers or events is NULL");
+  if (n_layers < 1) return fail(SRA_E_SHAPE, "n_layers must be >= 1");
+  if (n_buf < 2 || n_buf > 64) return fail(SRA_E_SHAPE, "n_buf must be in [2, 64]");
+  std::vector<void*> bufs;
+  for (int b = 0; b < n_buf; ++b) {
+    if (!k_buf[b] || !v_buf[b]) return fail(SRA_E_NULL, "device store buffer %d is NULL", b);
+    bufs.push_back(k_buf[b]);
+    bufs.push_back(v_buf[b]);
+  }
+  for (int i = 0; i < 2 * n_buf; ++i)
+    if (!events[i]) return fail(SRA_E_NULL, "event %d is NULL", i);
+  for (size_t i = 0; i < bufs.size(); ++i)
+    for (size_t j = i + 1; j < bufs.size(); ++j)
+      if (overlap(bufs[i], store_bytes, bufs[j], store_bytes))
+        return fail(SRA_E_ALIAS, "the device store buffers must be disjoint");
+  std::vector<sra_layer_args> la(layers, layers + n_layers);
+  std::vector<size_t> bytes(n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    if (!host_k[l] || !host_v[l]) return fail(SRA_E_NULL, "host store of layer %d is NULL", l);
+    la[l].k_store = k_buf[l % n_buf];
+    la[l].v_store = v_buf[l % n_buf];
+    if ((rc = check_shape(&la[l].shape))) return rc;
+    bytes[l] = (size_t)la[l].store_rows * la[l].shape.n_kv_heads * la[l].shape.head_dim * elem_size(&la[l].shape);
+    if (la[l].store_rows < 0 || bytes[l] > store_bytes)
+      return fail(SRA_E_SHAPE, "layer %d's store (%zu bytes) exceeds the buffers (%zu)", l, bytes[l], store_bytes);
+    const size_t es = elem_size(&la[l].shape);
+    const size_t fb = (size_t)la[l].n_req * la[l].total_len * la[l].shape.n_kv_heads * la[l].shape.head_dim * es;
+    const size_t ob = (size_t)la[l].n_req * la[l].n_rows * la[l].shape.n_q_heads * la[l].shape.head_dim * es;
+    for (void* buf : bufs)
+      if (overlap(buf, store_bytes, la[l].k_fused, fb) || overlap(buf, store_bytes, la[l].v_fused, fb) ||
+          overlap(buf, store_bytes, la[l].out, ob))
+        return fail(SRA_E_ALIAS, "layer %d writes into a store buffer", l);
+    if ((rc = fused_layer_impl(&la[l], ws, ws_bytes, stream, true))) return rc;
+  }
+  hipEvent_t* copied = events;            // copied[b]: buffer b holds its newest layer's store
+  hipEvent_t* stepped = events + n_buf;    // stepped[b]: the newest layer reading buffer b is done
+  auto copy = [&](int l) -> int {
+    const int b = l % n_buf;
+    hipError_t e = hipSuccess;
+    if (l >= n_buf) e = hipStreamWaitEvent(copy_stream, stepped[b], 0);   // layer l - n_buf is done with b
+    if (e == hipSuccess) e = hipMemcpyAsync(k_buf[b], host_k[l], bytes[l], hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(v_buf[b], host_v[l], bytes[l], hipMemcpyHostToDevice, copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(copied[b], copy_stream);
+    return e == hipSuccess ? SRA_OK : hip_fail(e, "store prefetch");
+  };
+  // the buffers may still be read by work queued earlier on `stream` (a previous call): the
+  // copies start after it
+  hipError_t e0 = hipEventRecord(stepped[0], stream);
+  if (e0 == hipSuccess) e0 = hipStreamWaitEvent(copy_stream, stepped[0], 0);
+  if (e0 != hipSuccess) return hip_fail(e0, "join before the first copy");
+  if ((rc = copy(0))) return rc;
+  for (int l = 0; l < n_layers; ++l) {
+    if (l + 1 < n_layers && (rc = copy(l + 1))) return rc;   // overlaps layer l's step
+    hipError_t e = hipStreamWaitEvent(stream, copied[l % n_buf], 0);
+    if (e != hipSuccess) return hip_fail(e, "wait for a layer's store");
+    if ((rc = fused_layer_impl(&la[l], ws, ws_bytes, stream, false))) return rc;
+    if (l + n_buf >= n_layers) continue;   // no later copy reuses this buffer
+    e = hipEventRecord(stepped[l % n_buf], stream);
+    if (e != hipSuccess) return hip_fail(e, "layer step event");
+  }
   return ok();
 }
 

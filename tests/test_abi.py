@@ -221,3 +221,38 @@ def test_hkvd_host_errors():
     assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_SHAPE
     a.n_select, a.hkvd_prev = 12, FAKE[5]                                                  # prev == row_pos
     assert lib.sra_fused_layer(ctypes.byref(a), FAKE[13], 1 << 30, None) == L.SRA_E_ALIAS
+
+
+def test_pipelined_layers_host_errors():
+    lib = L.lib()
+    ch = chunks([[0, 64, 0, 0], [64, 64, 64, 0]])
+    a = (L.LayerArgs * 2)()
+    for i in range(2):
+        a[i].shape = shape()
+        a[i].n_req, a[i].n_chunks, a[i].chunks = 1, 2, ctypes.cast(ch, ctypes.POINTER(L.Chunk))
+        a[i].query_len, a[i].total_len = 8, 136
+        a[i].store_rows = 128
+        a[i].q_fresh, a[i].k_fresh, a[i].v_fresh = FAKE[2], FAKE[3], FAKE[4]
+        a[i].row_pos, a[i].n_rows = FAKE[5], 20
+        a[i].k_fused, a[i].v_fused, a[i].out = FAKE[6], FAKE[7], FAKE[8]
+    P = ctypes.c_void_p
+    hk = (P * 2)(0x1000, 0x2000)
+    hv = (P * 2)(0x3000, 0x4000)
+    nb = 128 * 8 * 128 * 2
+    kb = (P * 2)(0xA0000000, 0xA4000000)
+    vb = (P * 2)(0xA8000000, 0xAC000000)
+    ev = (P * 4)(1, 2, 3, 4)
+    args = [a, 2, hk, hv, nb, kb, vb, 2, ev, FAKE[11], 1 << 30, None, None]
+    def call(i=None, v=None):
+        x = list(args)
+        if i is not None:
+            x[i] = v
+        return lib.sra_pipelined_layers(*x)
+    assert call(8, None) == L.SRA_E_NULL                                   # events
+    assert call(7, 1) == L.SRA_E_SHAPE                                     # one buffer pair
+    assert call(1, 0) == L.SRA_E_SHAPE                                     # no layers
+    assert call(4, nb - 2) == L.SRA_E_SHAPE                                # stores larger than the buffers
+    assert call(5, (P * 2)(0xA0000000, 0xA0000100)) == L.SRA_E_ALIAS       # buffers overlap
+    assert call(2, (P * 2)(0x1000, None)) == L.SRA_E_NULL                  # a host store
+    a[1].row_pos, a[1].n_rows = FAKE[5], 137                               # layer 1 invalid: nothing enqueued
+    assert call() == L.SRA_E_SHAPE
