@@ -43,6 +43,7 @@ __all__ = [
     "chunk_layout", "fuse_rerotate", "key_norms", "extract_anchors", "critical_scores",
     "select_count", "select_topn", "select_topn_quota", "row_positions", "scatter_kv",
     "sparse_causal_attn", "fused_layer", "kv_deviation", "hkvd_filter", "gradual_filter_layers",
+    "anchor_prefix", "anchor_probe", "query_centric_layers",
 ]
 
 
@@ -165,6 +166,59 @@ def extract_anchors(k_crit_store, chunks, k: int, dtype: str) -> np.ndarray:
         order = sorted(range(T), key=lambda t: (-nt[t], t))
         out.append(order[:k])
     return np.asarray(out, dtype=np.int32)
+
+
+def anchor_prefix(k_store, v_store, chunks, anchors, dtype: str, base: float):
+    """Anchors as a compact prefix for the query probe (QCFuse summary (zh) §2.A: the anchors are
+    injected into the query's forward pass as a lightweight prefix).
+
+    Reading: the anchors of each chunk in ascending token order, chunks in request order, occupy
+    prefix rows a = 0 .. A-1 (A = n_chunks * k). A key cached at position orig_c + t moves to row a:
+    K_pre[a] = round(R(a - orig_c - t) K_store[src_c + t]); V_pre[a] = V_store[src_c + t].
+    anchors: [n_chunks, k] token offsets. Returns float64 (K_pre, V_pre) [A, Hkv, d].
+    """
+    ks, vs = to_f64(k_store, dtype), to_f64(v_store, dtype)
+    kp, vp = [], []
+    a = 0
+    for (src, _T, _dst, orig), anc in zip(np.asarray(chunks).tolist(), np.asarray(anchors).tolist()):
+        for t in sorted(int(x) for x in anc):
+            kp.append(round_to_storage(rope(ks[src + t], a - int(orig) - t, base), dtype))
+            vp.append(vs[src + t])
+            a += 1
+    d = ks.shape[-1]
+    shape = (a, ks.shape[1], d)
+    return np.asarray(kp).reshape(shape), np.asarray(vp).reshape(shape)
+
+
+def anchor_probe(k_pre, v_pre, q_new, k_new, v_new, dtype: str, base: float):
+    """The query's forward pass over the anchor prefix: the Lq query rows sit at rows A .. A+Lq-1
+    after the A prefix rows; their K/V are stored there (K rotated at its row) and every query row
+    attends causally to the prefix and the query rows up to itself.
+    q_new, k_new, v_new: stored values [Lq, H, d]. Returns (O [Lq, Hq, d], LSE [Lq, Hq])."""
+    A = k_pre.shape[0]
+    Lq = np.asarray(q_new).shape[0]
+    kf = np.concatenate([k_pre, np.full((Lq,) + k_pre.shape[1:], np.nan)])
+    vf = np.concatenate([v_pre, np.full((Lq,) + v_pre.shape[1:], np.nan)])
+    rp = (A + np.arange(Lq)).astype(np.int32)
+    kf, vf = scatter_kv(kf, vf, k_new, v_new, rp, dtype, base)
+    return sparse_causal_attn(q_new, rp, kf, vf, dtype, base)
+
+
+def query_centric_layers(q_layers, k_layers, chunks, n_kv_heads: int, dtype: str, base: float,
+                         n_select: int, mode: str):
+    """The query-centric baselines the QCFuse pages compare against (QCFuse summary (zh) §4
+    results; (ja) §3): QCAll scores every layer with that layer's own query and cached keys and
+    recomputes each layer's own top-N; QCLast scores only the last layer and uses its top-N for
+    every layer. q_layers[l]: [Lq, Hq, d]; k_layers[l]: the layer's chunk store.
+    Returns (scores [n_layers or 1][L_ctx], selections [n_layers][N])."""
+    if mode == "all":
+        sc = [critical_scores(q, k, chunks, n_kv_heads, dtype, base) for q, k in zip(q_layers, k_layers)]
+        return np.asarray(sc), [select_topn(s, n_select) for s in sc]
+    if mode == "last":
+        s = critical_scores(q_layers[-1], k_layers[-1], chunks, n_kv_heads, dtype, base)
+        sel = select_topn(s, n_select)
+        return s[None], [sel for _ in q_layers]
+    raise ValueError(mode)
 
 
 # ----------------------------------------------------------------------------- S2b: scoring
