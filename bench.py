@@ -235,6 +235,58 @@ def pipeline_leg(sra, shape, w, ins, ws, Lq, Lctx, hip, sp, n_layers=8):
             "note": "pipelined_ms near max(copy_ms, compute_ms) means the recompute hides under the load"}
 
 
+def probe_leg(sra, shape, w, rep, Lq, Lctx, hip, sp):
+    """The query's anchor-grounded probe pass: gather the chunks' anchors into a compact prefix
+    (keys re-rotated to their prefix rows), store the query's K/V after it and attend every query
+    row over prefix and query."""
+    import torch
+    ins, outs = rep
+    cfg = w.cfg
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n_chunks, k = w.chunks.shape[1], cfg.anchors_k
+    A = n_chunks * k
+    Lp = A + Lq
+    kp = torch.empty((1, Lp, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    qn = ins["q_new"][:, Lctx:].contiguous()
+    kn = ins["k_new"][:, Lctx:].contiguous()
+    vn = ins["v_new"][:, Lctx:].contiguous()
+    rows = torch.arange(A, Lp, dtype=torch.int32, device="cuda")[None].contiguous()
+    out = torch.empty((1, Lq, Hq, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(sra.workspace_size(shape, 1, 1, Lp, Lq, 1), dtype=torch.uint8, device="cuda")
+
+    def probe():
+        sra.anchor_prefix(shape, ins["k_store"], ins["v_store"], w.chunks, outs["anchors"], kp, vp)
+        sra.scatter_kv(shape, kn, vn, rows, kp, vp)
+        sra.sparse_causal_attn(shape, qn, rows, kp, vp, out, None, ws)
+
+    ms = timed_calls(hip, sp, probe, 50)
+    return {"prefix_rows": A, "query_rows": Lq, "ms_per_probe": ms,
+            "kernels": "k_anchor_prefix + k_scatter + k_attn_mfma + k_attn_combine"}
+
+
+def qc_layers_leg(sra, shape, w, ins, N, Lq, Lctx, hip, sp, n_layers=8):
+    """Scoring cost of the query-centric baselines at this shape: QCAll scores every layer with
+    its own query and keys (8 layers here), against the one critical layer QCFuse scores; QCLast
+    costs one layer like the critical one."""
+    import torch
+    n_chunks = w.chunks.shape[1]
+    L = Lctx + Lq
+    ws = torch.empty(sra.workspace_size(shape, 1, n_chunks, L, N + Lq, Lq), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((1, Lctx), dtype=torch.float32, device="cuda")
+    rp = torch.empty((1, N + Lq), dtype=torch.int32, device="cuda")
+    one = timed_calls(hip, sp, lambda: sra.score_select(shape, ins["q_crit"], ins["k_crit"], w.chunks, N, None,
+                                                        sc, rp, ws), 50)
+
+    def all_layers():
+        for _ in range(n_layers):
+            sra.score_select(shape, ins["q_crit"], ins["k_crit"], w.chunks, N, None, sc, rp, ws)
+
+    qc_all = timed_calls(hip, sp, all_layers, 10)
+    return {"critical_layer_ms": one, "qcall_ms": qc_all, "layers": n_layers,
+            "qcall_over_critical": qc_all / one}
+
+
 def cpu_baseline(w, N, budget_s):
     """The fp64 oracle (as it stands) on the same workload: whole steps until the budget is used."""
     import oracle as O
@@ -382,6 +434,8 @@ def main():
     }
     result["hkvd"] = hkvd_leg(sra, shape, reps[0], N, Lq, Lctx, kv_row_bytes, hip, sp)
     result["pipeline"] = pipeline_leg(sra, shape, w, reps[0][0], ws, Lq, Lctx, hip, sp)
+    result["anchor_probe"] = probe_leg(sra, shape, w, reps[0], Lq, Lctx, hip, sp)
+    result["query_centric_layers"] = qc_layers_leg(sra, shape, w, reps[0][0], N, Lq, Lctx, hip, sp)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, N, args.cpu_seconds)
     # the parity of this exact output against the oracle is covered by the GPU tests

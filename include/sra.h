@@ -180,6 +180,23 @@ int sra_fuse_rerotate(const sra_shape* shape, int32_t n_req,
 
 /* ------------------------------------------------------------------------ S2 */
 
+/* Anchor probe prefix (QCFuse summary (zh) §2.A: the chunks' anchors are injected into the
+ * query's forward pass as a lightweight prefix, grounding the query in the context without the
+ * full cache). For request q, the anchors of each chunk in ascending token order, chunks in
+ * request order, fill rows a = 0 .. n_chunks*k - 1 of the probe caches: a token cached at
+ * position orig_pos + t moves to row a,
+ *   k_probe[q][a] = round(R(a - orig_pos - t) k_store[src_row + t]),  v_probe[q][a] = v_store[src_row + t]
+ * (bits kept when the shift is 0). The query's own rows follow at a >= n_chunks*k (written with
+ * sra_scatter_kv; the probe attention is sra_sparse_causal_attn over those rows).
+ * anchor_rows: [n_req][n_chunks][k] device token offsets (distinct, < n_tokens: e.g. from
+ * sra_extract_anchors or the fused layer). k_probe, v_probe: [n_req][L_probe][Hkv][d]; rows
+ * >= n_chunks*k are left untouched. 1 <= k <= min(n_tokens, SRA_MAX_ANCHOR_K).
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_CHUNKS, SRA_E_LIMIT, SRA_E_ALIAS, SRA_E_HIP. */
+int sra_anchor_prefix(const sra_shape* shape, int32_t n_req, const void* k_store, const void* v_store,
+                      int64_t store_rows, const sra_chunk* chunks, int32_t n_chunks,
+                      const int32_t* anchor_rows, int32_t k, void* k_probe, void* v_probe,
+                      int32_t L_probe, hipStream_t stream);
+
 /* Key-norm anchors (QCFuse summary (zh) §2.A anchor-based lightweight query probing: keep
  * the few tokens of each precomputed chunk with the largest key norm). For chunk c the
  * norm of token t is the L2 norm of k_store[src_c + t] over all Hkv*d values; anchors are

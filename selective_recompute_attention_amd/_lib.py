@@ -63,6 +63,8 @@ _SIGS = {
                                      _c.c_int32, _P, _P, _c.c_int32, _P]),
     "sra_extract_anchors": (_c.c_int, [_c.POINTER(Shape), _P, _c.c_int64, _c.POINTER(Chunk), _c.c_int32,
                                        _c.c_int32, _P, _P, _P, _c.c_size_t, _P]),
+    "sra_anchor_prefix": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int64, _c.POINTER(Chunk),
+                                     _c.c_int32, _P, _c.c_int32, _P, _P, _c.c_int32, _P]),
     "sra_score_select": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _c.c_int32, _P, _c.c_int64,
                                     _c.POINTER(Chunk), _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int32),
                                     _P, _P, _P, _c.c_size_t, _P]),

@@ -12,7 +12,7 @@ import torch
 
 from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, check, hip_runtime, lib)  # noqa: F401
 
-__all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors",
+__all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors", "anchor_prefix",
            "score_select", "select_topn", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
            "pipelined_layers", "create_events", "destroy_events", "check_rows", "chunk_array", "SRAError"]
 
@@ -87,6 +87,18 @@ def extract_anchors(shape, k_store, chunks, k, anchor_rows, ws, norms=None, stre
     check(lib().sra_extract_anchors(ctypes.byref(shape), _ptr(k_store), k_store.shape[0], chunk_array(ch),
                                     len(ch), int(k), _ptr(anchor_rows), _ptr(norms), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def anchor_prefix(shape, k_store, v_store, chunks, anchor_rows, k_probe, v_probe, stream=None):
+    """Anchor probe prefix rows [0, n_chunks * k) of k_probe/v_probe [n_req][L_probe][Hkv][d]
+    (sra_anchor_prefix); anchor_rows: [n_req][n_chunks][k] int32 on the device."""
+    ch = np.asarray(chunks, dtype=np.int32)
+    n_req, n_chunks = ch.shape[0], ch.shape[1]
+    carr = chunk_array(ch)
+    check(lib().sra_anchor_prefix(ctypes.byref(shape), n_req, _ptr(k_store), _ptr(v_store), k_store.shape[0],
+                                  ctypes.cast(carr, ctypes.POINTER(Chunk)), n_chunks, _ptr(anchor_rows),
+                                  anchor_rows.shape[-1], _ptr(k_probe), _ptr(v_probe), k_probe.shape[-3],
+                                  _stream(stream)))
 
 
 def score_select(shape, q_crit, k_crit_store, chunks, n_select, quotas, scores, row_pos, ws, stream=None):

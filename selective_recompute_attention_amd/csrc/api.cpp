@@ -550,6 +550,43 @@ int sra_extract_anchors(const sra_shape* shape, const void* k_store, int64_t sto
   return ok();
 }
 
+int sra_anchor_prefix(const sra_shape* shape, int32_t n_req, const void* k_store, const void* v_store,
+                      int64_t store_rows, const sra_chunk* chunks, int32_t n_chunks, const int32_t* anchor_rows,
+                      int32_t k, void* k_probe, void* v_probe, int32_t L_probe, hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (n_req <= 0 || n_chunks <= 0) return fail(SRA_E_SHAPE, "need n_req > 0 and n_chunks > 0");
+  if ((rc = check_ptr(k_store, "k_store")) || (rc = check_ptr(v_store, "v_store")) ||
+      (rc = check_ptr(k_probe, "k_probe")) || (rc = check_ptr(v_probe, "v_probe")))
+    return rc;
+  if (!anchor_rows || !chunks) return fail(SRA_E_NULL, "anchor_rows or chunks is NULL");
+  if (k < 1) return fail(SRA_E_SHAPE, "k must be >= 1");
+  if (k > SRA_MAX_ANCHOR_K) return fail(SRA_E_LIMIT, "k = %d exceeds %d", k, SRA_MAX_ANCHOR_K);
+  if ((int64_t)n_chunks * k > L_probe) return fail(SRA_E_SHAPE, "prefix of %lld rows exceeds L_probe = %d",
+                                                   (long long)n_chunks * k, L_probe);
+  std::vector<Entry> ents;
+  for (int q = 0; q < n_req; ++q)
+    for (int c = 0; c < n_chunks; ++c) {
+      const sra_chunk& ch = chunks[(int64_t)q * n_chunks + c];
+      if (ch.src_row < 0 || ch.n_tokens < 0 || (int64_t)ch.src_row + ch.n_tokens > store_rows)
+        return fail(SRA_E_CHUNKS, "chunk %d of request %d reads outside the store", c, q);
+      if (ch.n_tokens < k) return fail(SRA_E_SHAPE, "chunk %d has %d tokens < k = %d", c, ch.n_tokens, k);
+      ents.push_back({q, ch.src_row, ch.n_tokens, c * k, ch.orig_pos, k, c});
+    }
+  const size_t row = (size_t)shape->n_kv_heads * shape->head_dim * elem_size(shape);
+  const size_t sb = (size_t)store_rows * row, pb = (size_t)n_req * L_probe * row;
+  if (overlap(k_store, sb, k_probe, pb) || overlap(k_store, sb, v_probe, pb) || overlap(v_store, sb, k_probe, pb) ||
+      overlap(v_store, sb, v_probe, pb) || overlap(k_probe, pb, v_probe, pb))
+    return fail(SRA_E_ALIAS, "the store and the probe caches overlap");
+  hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
+    return sra::launch_anchor_prefix(shape->dtype, shape->head_dim, shape->n_kv_heads, tab, k, n_chunks,
+                                     anchor_rows, k_store, v_store, k_probe, v_probe, L_probe, shape->rope_base,
+                                     stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "anchor prefix launch");
+  return ok();
+}
+
 int sra_score_select(const sra_shape* shape, int32_t n_req, const void* q_crit, int32_t Lq,
                      const void* k_crit_store, int64_t store_rows, const sra_chunk* chunks,
                      int32_t n_chunks, int32_t n_select, const int32_t* chunk_quota, float* scores,

@@ -198,6 +198,11 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
                           hipStream_t st);
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
                              double base, hipStream_t st);
+// Anchor probe prefix rows [0, n_chunks * k) of [n_req][Lp][Hkv][D] probe caches; tab entries
+// (req, src, len, dst = first prefix row, delta = orig_pos, aux = chunk index), k blocks each.
+hipError_t launch_anchor_prefix(int dtype, int D, int Hkv, const ChunkTab& tab, int k, int n_chunks,
+                                const int* anchors, const void* ks, const void* vs, void* kp, void* vp, int Lp,
+                                double base, hipStream_t st);
 // KV deviation of the first n_dev recomputed rows (dev: [n_req][n_dev] float32). Fresh rows are
 // compact or position-indexed as in launch_scatter; kf/vf hold the reused rows (not yet scattered).
 hipError_t launch_kv_deviation(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,

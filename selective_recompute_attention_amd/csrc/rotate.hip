@@ -259,6 +259,73 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
   }
 }
 
+// Anchor probe prefix (QCFuse summary (zh) §2.A: the chunks' anchors enter the query's forward
+// pass as a lightweight prefix). One block per prefix row a = c * k + j of a request: the j-th
+// smallest of chunk c's k anchor offsets t (offsets ranked in LDS, ties by index) is cached at
+// position orig_c + t and moves to row a, so its key turns by a - orig_c - t (bits kept when that
+// is 0); V is copied. Offsets are clamped into the chunk (distinct in-range offsets are the
+// caller's contract). tab entries: (req, src, len, dst = first prefix row, delta = orig, aux = c).
+template <typename T, int D>
+__global__ __launch_bounds__(128) void k_anchor_prefix(ChunkTab tab, int k, int n_chunks, const int* __restrict__ anchors,
+                                                       int Hkv, const T* __restrict__ ks, const T* __restrict__ vs,
+                                                       T* __restrict__ kp, T* __restrict__ vp, int Lp, Theta th) {
+  constexpr int H = D / 2;
+  constexpr int VW = Vec<T>::N;
+  constexpr int UPH = H / VW;
+  constexpr int NT = 128;
+  __shared__ float2 cs[H];
+  __shared__ int sh_t;
+  const int e = find_entry(tab, blockIdx.x);
+  const int j = blockIdx.x - tab.blk0[e];
+  const int q = tab.req[e], len = tab.len[e];
+  const int* arow = anchors + ((int64_t)q * n_chunks + tab.aux[e]) * k;
+  if ((int)threadIdx.x < k) {
+    const int ti = min(max(arow[threadIdx.x], 0), len - 1);
+    int rank = 0;
+    for (int i = 0; i < k; ++i) {
+      const int tv = min(max(arow[i], 0), len - 1);
+      rank += (tv < ti || (tv == ti && i < (int)threadIdx.x)) ? 1 : 0;
+    }
+    if (rank == j) sh_t = ti;
+  }
+  __syncthreads();
+  const int t = sh_t;
+  const int a = tab.dst[e] + j;
+  const int delta = a - tab.delta[e] - t;
+  if (delta != 0)
+    for (int i = threadIdx.x; i < H; i += NT) cs[i] = rope_cs((double)delta, th.v[i]);
+  __syncthreads();
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t src0 = ((int64_t)tab.src[e] + t) * row_elems;
+  const int64_t dst0 = ((int64_t)q * Lp + a) * row_elems;
+  const int nV = (int)(row_elems * (int64_t)sizeof(T) / 16), nK = Hkv * UPH;
+  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vs + src0);
+  u32x4* vdst = reinterpret_cast<u32x4*>(vp + dst0);
+  for (int u = threadIdx.x; u < nV; u += NT) vdst[u] = vsrc[u];
+  for (int u = threadIdx.x; u < nK; u += NT) {
+    const int i0 = (u % UPH) * VW;
+    const int64_t o = (u / UPH) * D + i0;
+    const u32x4 ka = *reinterpret_cast<const u32x4*>(ks + src0 + o);
+    const u32x4 kb = *reinterpret_cast<const u32x4*>(ks + src0 + o + H);
+    if (delta == 0) {
+      *reinterpret_cast<u32x4*>(kp + dst0 + o) = ka;
+      *reinterpret_cast<u32x4*>(kp + dst0 + o + H) = kb;
+    } else {
+      float fa[VW], fb[VW], ra[VW], rb[VW];
+      Vec<T>::unpack(ka, fa);
+      Vec<T>::unpack(kb, fb);
+#pragma unroll
+      for (int m = 0; m < VW; ++m) {
+        const float c = cs[i0 + m].x, sn = cs[i0 + m].y;
+        ra[m] = fa[m] * c - fb[m] * sn;
+        rb[m] = fa[m] * sn + fb[m] * c;
+      }
+      *reinterpret_cast<u32x4*>(kp + dst0 + o) = Vec<T>::pack(ra);
+      *reinterpret_cast<u32x4*>(kp + dst0 + o + H) = Vec<T>::pack(rb);
+    }
+  }
+}
+
 // KV deviation of recomputed rows (KVCache reuse 01, §1.3.2-§1.3.3: tokens are ranked by the
 // difference between their reused and their recomputed KV). One block per (row r < n_dev,
 // request), at p = row_pos[r]: the Euclidean norm over every KV head and dimension of the fresh K
@@ -414,6 +481,34 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
     k_scatter<float, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
                                            (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
                                            (float*)vf, cs_out, nullptr, 0, scale_log2, th);
+  return hipGetLastError();
+}
+
+hipError_t launch_anchor_prefix(int dtype, int D, int Hkv, const ChunkTab& tab, int k, int n_chunks,
+                                const int* anchors, const void* ks, const void* vs, void* kp, void* vp, int Lp,
+                                double base, hipStream_t st) {
+  if (tab.n == 0 || tab.blk0[tab.n] == 0) return hipSuccess;
+  const dim3 g((unsigned)tab.blk0[tab.n]), b(128);
+  const Theta th = make_theta(D, base);
+  if (dtype == 0) {
+    auto k_ = (const uint16_t*)ks;
+    auto v_ = (const uint16_t*)vs;
+    if (D == 128)
+      k_anchor_prefix<uint16_t, 128><<<g, b, 0, st>>>(tab, k, n_chunks, anchors, Hkv, k_, v_, (uint16_t*)kp,
+                                                      (uint16_t*)vp, Lp, th);
+    else
+      k_anchor_prefix<uint16_t, 64><<<g, b, 0, st>>>(tab, k, n_chunks, anchors, Hkv, k_, v_, (uint16_t*)kp,
+                                                     (uint16_t*)vp, Lp, th);
+  } else {
+    auto k_ = (const float*)ks;
+    auto v_ = (const float*)vs;
+    if (D == 128)
+      k_anchor_prefix<float, 128><<<g, b, 0, st>>>(tab, k, n_chunks, anchors, Hkv, k_, v_, (float*)kp,
+                                                   (float*)vp, Lp, th);
+    else
+      k_anchor_prefix<float, 64><<<g, b, 0, st>>>(tab, k, n_chunks, anchors, Hkv, k_, v_, (float*)kp,
+                                                  (float*)vp, Lp, th);
+  }
   return hipGetLastError();
 }
 

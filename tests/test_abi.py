@@ -256,3 +256,21 @@ def test_pipelined_layers_host_errors():
     assert call(2, (P * 2)(0x1000, None)) == L.SRA_E_NULL                  # a host store
     a[1].row_pos, a[1].n_rows = FAKE[5], 137                               # layer 1 invalid: nothing enqueued
     assert call() == L.SRA_E_SHAPE
+
+
+def test_anchor_prefix_host_errors():
+    lib = L.lib()
+    s = shape()
+    ch = chunks([[0, 8, 0, 0], [8, 8, 8, 0]])
+    base = [ctypes.byref(s), 1, FAKE[0], FAKE[1], 16, ch, 2, FAKE[2], 4, FAKE[3], FAKE[4], 12, None]
+    def call(i=None, v=None):
+        x = list(base)
+        if i is not None:
+            x[i] = v
+        return lib.sra_anchor_prefix(*x)
+    assert call(11, 7) == L.SRA_E_SHAPE          # prefix of 8 rows does not fit 7
+    assert call(8, 9) == L.SRA_E_SHAPE           # k > n_tokens
+    assert call(8, 65) == L.SRA_E_LIMIT
+    assert call(4, 15) == L.SRA_E_CHUNKS         # second chunk reads outside the store
+    assert call(7, None) == L.SRA_E_NULL
+    assert call(9, FAKE[0]) == L.SRA_E_ALIAS     # probe cache over the store
