@@ -43,7 +43,8 @@ __all__ = [
     "chunk_layout", "fuse_rerotate", "key_norms", "extract_anchors", "critical_scores",
     "select_count", "select_topn", "select_topn_quota", "row_positions", "scatter_kv",
     "sparse_causal_attn", "fused_layer", "kv_deviation", "hkvd_filter", "gradual_filter_layers",
-    "anchor_prefix", "anchor_probe", "query_centric_layers",
+    "anchor_prefix", "anchor_probe", "query_centric_layers", "chunk_attention_stats",
+    "cache_context_impact", "preceding_chunk_scores", "prefix_overlap", "cachecraft_count",
 ]
 
 
@@ -372,6 +373,98 @@ def sparse_causal_attn(q_new, row_pos, k_fused, v_fused, dtype: str, base: float
         outs.append(o)
         lses.append(lse)
     return np.asarray(outs).reshape(len(outs), Hq, d), np.asarray(lses).reshape(len(lses), Hq)
+
+
+# ----------------------------------------------------------------------------- Cache-Craft selection
+
+def chunk_attention_stats(q_new, k_cache, chunks, n_kv_heads: int, dtype: str, base: float, rows=None):
+    """Per-token inter-chunk attention of a full causal prefill (Cache-Craft: inter-attention is the
+    sum of attention weights between chunks, KVCache reuse 01 §2.3.1; the per-token table is what
+    the token selection sums, Cache-Craft CSDN article §2.2.2).
+
+    For context token t (query, rotated at t) and chunk j: inter[t, j] = sum over query heads h of the
+    softmax probability, over the keys s <= t of the context, of the keys s in chunk j. The keys are
+    the prefill's cache rows (k_cache: stored values [>= L_ctx, Hkv, d], already rotated at their
+    positions); q_new: stored [>= L_ctx, Hq, d] before rotation. rows: optional subset of tokens.
+    Returns float64 [n_rows, n_chunks]; every row sums to Hq.
+    """
+    L_ctx, lay = chunk_layout(chunks)
+    q = to_f64(np.asarray(q_new)[:L_ctx], dtype)
+    kc = to_f64(np.asarray(k_cache)[:L_ctx], dtype)
+    Hq, d = q.shape[1], q.shape[2]
+    g = Hq // n_kv_heads
+    rows = np.arange(L_ctx) if rows is None else np.asarray(rows, dtype=np.int64)
+    qr = rope(q[rows], rows[:, None], base)                              # [n, Hq, d]
+    chunk_of = np.empty(L_ctx, dtype=np.int64)
+    for c, (_src, T, n, _delta) in enumerate(lay):
+        chunk_of[n:n + T] = c
+    inter = np.zeros((len(rows), len(lay)))
+    visible = np.arange(L_ctx)[None, :] <= rows[:, None]                # key s <= token t
+    for h in range(Hq):
+        x = qr[:, h, :] @ kc[:, h // g, :].T / math.sqrt(d)             # [n, L_ctx]
+        x = np.where(visible, x, -np.inf)
+        x = x - x.max(axis=1, keepdims=True)
+        p = np.exp(x)
+        p = p / p.sum(axis=1, keepdims=True)
+        for c in range(len(lay)):
+            inter[:, c] += p[:, chunk_of == c].sum(axis=1)
+    return inter
+
+
+def preceding_chunk_scores(inter, chunks) -> np.ndarray:
+    """Token score for recompute selection (KVCache reuse 01 §2.3.3: T(C_i) = argtop_N of
+    sum_{j<i} inter(C_j, t)): the attention mass token t of chunk i puts on the chunks before it."""
+    L_ctx, lay = chunk_layout(chunks)
+    inter = np.asarray(inter, dtype=np.float64)
+    s = np.zeros(L_ctx)
+    for c, (_src, T, n, _delta) in enumerate(lay):
+        s[n:n + T] = inter[n:n + T, :c].sum(axis=1)
+    return s
+
+
+def cache_context_impact(inter, chunks) -> np.ndarray:
+    """CCI per chunk (Cache-Craft CSDN article §2.2.1: CCI = sigmoid(sum inter / sum intra); KVCache
+    reuse 01 §2.3.1 with inter and intra normalised alike, which leaves the ratio unchanged).
+    sum inter: the chunk's tokens' attention on earlier chunks; sum intra: on their own chunk."""
+    _L, lay = chunk_layout(chunks)
+    inter = np.asarray(inter, dtype=np.float64)
+    out = []
+    for c, (_src, T, n, _delta) in enumerate(lay):
+        a = inter[n:n + T, :c].sum()
+        b = inter[n:n + T, c].sum()
+        out.append(1.0 / (1.0 + math.exp(-a / b)))
+    return np.asarray(out)
+
+
+def prefix_overlap(inter_to_old, old_prefix: Sequence[int], new_prefix: Sequence[int]) -> float:
+    """Adjusted prefix overlap beta' of one chunk (Cache-Craft CSDN article §2.2.1; KVCache reuse 01
+    §2.3.2): beta' = (sum of the chunk's inter-attention on old-prefix chunks also in the new prefix)
+    x (1 - gamma) / (sum on all old-prefix chunks), gamma = Kendall tau distance between the shared
+    chunks' order in the old and the new prefix (discordant pairs / all pairs; 0 below two shared).
+    inter_to_old[c]: the chunk's inter-attention on old-prefix chunk id c. Reading: an empty old
+    prefix (no attention outside the chunk was recorded) gives beta' = 0."""
+    old = [int(c) for c in old_prefix]
+    new = [int(c) for c in new_prefix]
+    den = sum(float(inter_to_old[c]) for c in old)
+    if den <= 0.0:
+        return 0.0
+    shared = [c for c in old if c in new]
+    num = sum(float(inter_to_old[c]) for c in shared)
+    n = len(shared)
+    gamma = 0.0
+    if n >= 2:
+        pos_new = {c: i for i, c in enumerate(new)}
+        disc = sum(1 for i in range(n) for j in range(i + 1, n) if pos_new[shared[i]] > pos_new[shared[j]])
+        gamma = disc / (n * (n - 1) / 2)
+    return num * (1.0 - gamma) / den
+
+
+def cachecraft_count(alpha: float, cci: float, beta: float, n_tokens: int) -> int:
+    """Tokens to recompute in one chunk: N = ceil(alpha * CCI * (1 - beta') * |C|) (Cache-Craft CSDN
+    article §2.1; CFO = alpha * CCI * (1 - beta'), §2.2.1), evaluated in float64 in this order and
+    clamped to [0, |C|]."""
+    x = float(alpha) * float(cci) * (1.0 - float(beta)) * float(n_tokens)
+    return int(min(max(math.ceil(x), 0), int(n_tokens)))
 
 
 # ----------------------------------------------------------------------------- fused layer
