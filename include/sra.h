@@ -246,6 +246,48 @@ int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t
                     const int32_t* chunk_quota, const sra_chunk* chunks, int32_t n_chunks,
                     int32_t Lq, int32_t* row_pos, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ Cache-Craft selection */
+
+/* Attention statistics of a full causal prefill, per token and chunk (Cache-Craft: the
+ * inter-attention between chunks, KVCache reuse 01 §2.3.1; the per-token table the token selection
+ * sums, Cache-Craft CSDN article §2.2.2). For context token t of request q (query rotated at t)
+ * and chunk j:
+ *   inter[q][t][j] = sum over query heads h of sum_{s in chunk j, s <= t} softmax_{s' <= t}(q_th . k_s' / sqrt(d))
+ *   token_scores[q][t] = sum_{j < c(t)} inter[q][t][j]   (mass on the chunks before t's own;
+ *                        KVCache reuse 01 §2.3.3 selects argtop_N of it per chunk)
+ *   cci[q][c] = sigmoid(sum_{t in c} token_scores / sum_{t in c} inter[t][c])  (CSDN article §2.2.1)
+ * q_fresh: [n_req][q_rows][Hq][d] position-indexed queries before rotary embedding (rows < L_ctx
+ * used). k_cache: [n_req][k_rows][Hkv][d] the prefill's cached keys (rotated at their positions,
+ * as the fused cache stores them). chunks: host [n_req][n_chunks] tiling the context (only the
+ * token ranges are used). inter [n_req][L_ctx][n_chunks], token_scores [n_req][L_ctx] and cci
+ * [n_req][n_chunks] are float32 outputs, each optional (NULL). Sums are exact 64-bit fixed point
+ * (2^-40) over float32 probabilities. bf16 only. ws: sra_stats_workspace_size bytes.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_CHUNKS, SRA_E_LIMIT (n_chunks > 80),
+ * SRA_E_ALIAS, SRA_E_WORKSPACE, SRA_E_HIP. */
+int sra_chunk_attention_stats(const sra_shape* shape, int32_t n_req, const void* q_fresh, int32_t q_rows,
+                              const void* k_cache, int32_t k_rows, const sra_chunk* chunks,
+                              int32_t n_chunks, float* inter, float* token_scores, float* cci, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of sra_chunk_attention_stats (0 for invalid sizes). */
+size_t sra_stats_workspace_size(const sra_shape* shape, int32_t n_req, int32_t ctx_len, int32_t n_chunks);
+
+/* Adjusted prefix overlap of one chunk (Cache-Craft CSDN article §2.2.1; KVCache reuse 01 §2.3.2),
+ * host only: beta' = (sum of inter_to_old[i] over old-prefix chunks also in the new prefix)
+ * x (1 - gamma) / (sum of inter_to_old[i] over the old prefix), gamma = Kendall tau distance
+ * between the shared chunks' order in the old and the new prefix (discordant pairs / all pairs,
+ * 0 below two shared). inter_to_old[i]: the chunk's inter-attention on old_ids[i] (e.g. a sum of
+ * sra_chunk_attention_stats rows). An old prefix with no attention gives beta' = 0.
+ * Errors: SRA_E_NULL, SRA_E_SHAPE. */
+int sra_prefix_overlap(const double* inter_to_old, const int32_t* old_ids, int32_t n_old,
+                       const int32_t* new_ids, int32_t n_new, double* beta_out);
+
+/* Tokens to recompute in one chunk, host only: N = ceil(alpha * cci * (1 - beta) * n_tokens)
+ * (Cache-Craft CSDN article §2.1; CFO = alpha * CCI * (1 - beta'), §2.2.1), evaluated in double
+ * in this order and clamped to [0, n_tokens]. Use the counts as per-chunk quotas of
+ * sra_select_topn over the token scores. Errors: SRA_E_NULL, SRA_E_SHAPE. */
+int sra_cachecraft_count(double alpha, double cci, double beta, int32_t n_tokens, int32_t* n_out);
+
 /* ------------------------------------------------------------------------ S3 */
 
 /* Scatter fresh K/V of the recomputed rows into the fused cache (KVCache reuse 01 §1.3.4:

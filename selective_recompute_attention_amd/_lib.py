@@ -65,6 +65,12 @@ _SIGS = {
                                        _c.c_int32, _P, _P, _P, _c.c_size_t, _P]),
     "sra_anchor_prefix": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int64, _c.POINTER(Chunk),
                                      _c.c_int32, _P, _c.c_int32, _P, _P, _c.c_int32, _P]),
+    "sra_chunk_attention_stats": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _c.c_int32, _P, _c.c_int32,
+                                             _c.POINTER(Chunk), _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "sra_stats_workspace_size": (_c.c_size_t, [_c.POINTER(Shape), _c.c_int32, _c.c_int32, _c.c_int32]),
+    "sra_prefix_overlap": (_c.c_int, [_c.POINTER(_c.c_double), _c.POINTER(_c.c_int32), _c.c_int32,
+                                      _c.POINTER(_c.c_int32), _c.c_int32, _c.POINTER(_c.c_double)]),
+    "sra_cachecraft_count": (_c.c_int, [_c.c_double, _c.c_double, _c.c_double, _c.c_int32, _c.POINTER(_c.c_int32)]),
     "sra_score_select": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _c.c_int32, _P, _c.c_int64,
                                     _c.POINTER(Chunk), _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int32),
                                     _P, _P, _P, _c.c_size_t, _P]),

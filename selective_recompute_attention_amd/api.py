@@ -13,6 +13,7 @@ import torch
 from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, check, hip_runtime, lib)  # noqa: F401
 
 __all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors", "anchor_prefix",
+           "stats_workspace_size", "chunk_attention_stats", "prefix_overlap", "cachecraft_count",
            "score_select", "select_topn", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
            "pipelined_layers", "create_events", "destroy_events", "check_rows", "chunk_array", "SRAError"]
 
@@ -99,6 +100,42 @@ def anchor_prefix(shape, k_store, v_store, chunks, anchor_rows, k_probe, v_probe
                                   ctypes.cast(carr, ctypes.POINTER(Chunk)), n_chunks, _ptr(anchor_rows),
                                   anchor_rows.shape[-1], _ptr(k_probe), _ptr(v_probe), k_probe.shape[-3],
                                   _stream(stream)))
+
+
+def stats_workspace_size(shape: Shape, n_req: int, ctx_len: int, n_chunks: int) -> int:
+    return int(lib().sra_stats_workspace_size(ctypes.byref(shape), n_req, ctx_len, n_chunks))
+
+
+def chunk_attention_stats(shape, q_fresh, k_cache, chunks, ws, inter=None, token_scores=None, cci=None,
+                          stream=None):
+    """Per-token, per-chunk attention statistics of a full causal prefill (sra_chunk_attention_stats):
+    inter [n_req][L_ctx][n_chunks], token_scores [n_req][L_ctx], cci [n_req][n_chunks] (float32, each
+    optional). q_fresh [n_req][q_rows][Hq][d] before rotation; k_cache [n_req][k_rows][Hkv][d] rotated."""
+    ch = np.asarray(chunks, dtype=np.int32)
+    n_req, n_chunks = ch.shape[0], ch.shape[1]
+    carr = chunk_array(ch)
+    check(lib().sra_chunk_attention_stats(ctypes.byref(shape), n_req, _ptr(q_fresh), q_fresh.shape[1],
+                                          _ptr(k_cache), k_cache.shape[1], ctypes.cast(carr, ctypes.POINTER(Chunk)),
+                                          n_chunks, _ptr(inter), _ptr(token_scores), _ptr(cci), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def prefix_overlap(inter_to_old, old_ids, new_ids) -> float:
+    """beta' of one chunk (sra_prefix_overlap); inter_to_old[i] belongs to old_ids[i]."""
+    n_old, n_new = len(old_ids), len(new_ids)
+    a = (ctypes.c_double * max(n_old, 1))(*[float(x) for x in inter_to_old])
+    o = (ctypes.c_int32 * max(n_old, 1))(*[int(x) for x in old_ids])
+    n = (ctypes.c_int32 * max(n_new, 1))(*[int(x) for x in new_ids])
+    out = ctypes.c_double()
+    check(lib().sra_prefix_overlap(a, o, n_old, n, n_new, ctypes.byref(out)))
+    return float(out.value)
+
+
+def cachecraft_count(alpha: float, cci: float, beta: float, n_tokens: int) -> int:
+    """N = ceil(alpha * cci * (1 - beta) * n_tokens), clamped (sra_cachecraft_count)."""
+    out = ctypes.c_int32()
+    check(lib().sra_cachecraft_count(float(alpha), float(cci), float(beta), int(n_tokens), ctypes.byref(out)))
+    return int(out.value)
 
 
 def score_select(shape, q_crit, k_crit_store, chunks, n_select, quotas, scores, row_pos, ws, stream=None):

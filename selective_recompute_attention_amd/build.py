@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsra.so")
-SOURCES = ["api.cpp", "rotate.hip", "anchors.hip", "score.hip", "score_f32.hip", "select.hip", "attn.hip"]
+SOURCES = ["api.cpp", "rotate.hip", "anchors.hip", "score.hip", "score_f32.hip", "select.hip", "attn.hip",
+           "stats.hip"]
 ARCH = os.environ.get("SRA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

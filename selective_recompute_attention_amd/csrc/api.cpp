@@ -587,6 +587,126 @@ int sra_anchor_prefix(const sra_shape* shape, int32_t n_req, const void* k_store
   return ok();
 }
 
+namespace {
+struct StatsPlan {
+  int n_tiles = 0, qop_blocks = 0;
+  size_t qop = 0, fx = 0, total = 0;
+};
+StatsPlan stats_plan(const sra_shape* s, int n_req, int Lctx, int n_chunks) {
+  StatsPlan p;
+  const int g = s->n_q_heads / s->n_kv_heads;
+  p.n_tiles = (int)ceil_div((int64_t)Lctx * g, 128);
+  p.qop_blocks = 4 * p.n_tiles;
+  size_t o = 0;
+  p.qop = o; o = align256(o + (size_t)n_req * s->n_kv_heads * p.qop_blocks * 32 * 2 * s->head_dim * sizeof(uint16_t));
+  p.fx = o; o = align256(o + (size_t)n_req * Lctx * n_chunks * sizeof(unsigned long long));
+  p.total = o;
+  return p;
+}
+}  // namespace
+
+size_t sra_stats_workspace_size(const sra_shape* shape, int32_t n_req, int32_t ctx_len, int32_t n_chunks) {
+  if (!shape || check_shape(shape) != SRA_OK || n_req <= 0 || ctx_len <= 0 || n_chunks <= 0) return 0;
+  return stats_plan(shape, n_req, ctx_len, n_chunks).total;
+}
+
+int sra_chunk_attention_stats(const sra_shape* shape, int32_t n_req, const void* q_fresh, int32_t q_rows,
+                              const void* k_cache, int32_t k_rows, const sra_chunk* chunks, int32_t n_chunks,
+                              float* inter, float* token_scores, float* cci, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  int rc;
+  if ((rc = check_shape(shape))) return rc;
+  if (shape->dtype != SRA_DTYPE_BF16) return fail(SRA_E_DTYPE, "chunk attention statistics are bf16 only");
+  if (n_req <= 0) return fail(SRA_E_SHAPE, "n_req must be positive");
+  if ((rc = check_ptr(q_fresh, "q_fresh")) || (rc = check_ptr(k_cache, "k_cache"))) return rc;
+  int Lctx = 0;
+  if ((rc = check_chunks(chunks, n_req, n_chunks, std::numeric_limits<int32_t>::max(), &Lctx))) return rc;
+  if (q_rows < Lctx || k_rows < Lctx) return fail(SRA_E_SHAPE, "q_rows %d and k_rows %d must cover the context %d",
+                                                  q_rows, k_rows, Lctx);
+  if (n_chunks > sra::kMaxEntries) return fail(SRA_E_LIMIT, "at most %d chunks per request", sra::kMaxEntries);
+  if ((int64_t)Lctx * (shape->n_q_heads / shape->n_kv_heads) > (int64_t)sra::kAttnMaxTiles * 128)
+    return fail(SRA_E_LIMIT, "context too long for the statistics kernel");
+  const StatsPlan p = stats_plan(shape, n_req, Lctx, n_chunks);
+  if ((rc = check_ws(ws, ws_bytes, p.total))) return rc;
+  const size_t kb = (size_t)n_req * k_rows * shape->n_kv_heads * shape->head_dim * 2;
+  const size_t fb = (size_t)n_req * Lctx * n_chunks * sizeof(float);
+  if ((inter && (overlap(inter, fb, k_cache, kb) || overlap(inter, fb, ws, p.total))) ||
+      (cci && overlap(cci, (size_t)n_req * n_chunks * sizeof(float), ws, p.total)) ||
+      (token_scores && overlap(token_scores, (size_t)n_req * Lctx * sizeof(float), ws, p.total)) ||
+      overlap(k_cache, kb, ws, p.total))
+    return fail(SRA_E_ALIAS, "outputs overlap the inputs or the workspace");
+  uint16_t* qop = reinterpret_cast<uint16_t*>(wsp(ws, p.qop));
+  unsigned long long* fx = reinterpret_cast<unsigned long long*>(wsp(ws, p.fx));
+  hipError_t e = hipMemsetAsync(fx, 0, (size_t)n_req * Lctx * n_chunks * sizeof(unsigned long long), stream);
+  if (e != hipSuccess) return hip_fail(e, "statistics slots clear");
+  // the query of every context token, rotated at its position and split hi/lo (identity rows)
+  e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads, n_req, Lctx, Lctx,
+                          q_fresh, nullptr, nullptr, q_rows, 1, nullptr, nullptr, nullptr, nullptr, qop,
+                          p.qop_blocks, attn_scale_log2(shape->head_dim), shape->rope_base, stream);
+  if (e != hipSuccess) return hip_fail(e, "query operand launch");
+  const int per = std::max(1, sra::kMaxEntries / n_chunks);   // requests per launch
+  for (int q0 = 0; q0 < n_req; q0 += per) {
+    const int nq = std::min(per, n_req - q0);
+    sra::ChunkTab tab;
+    std::memset(&tab, 0, sizeof(tab));
+    for (int q = q0; q < q0 + nq; ++q)
+      for (int c = 0; c < n_chunks; ++c) {
+        const sra_chunk& ch = chunks[(int64_t)q * n_chunks + c];
+        tab.req[tab.n] = q;
+        tab.dst[tab.n] = ch.dst_row;
+        tab.len[tab.n] = ch.n_tokens;
+        ++tab.n;
+      }
+    e = sra::launch_chunk_stats(shape->head_dim, nq, q0, shape->n_q_heads, shape->n_kv_heads, Lctx, k_rows, qop,
+                                p.qop_blocks, reinterpret_cast<const uint16_t*>(k_cache), tab, n_chunks, fx, inter,
+                                token_scores, cci, stream);
+    if (e != hipSuccess) return hip_fail(e, "statistics launch");
+  }
+  return ok();
+}
+
+int sra_prefix_overlap(const double* inter_to_old, const int32_t* old_ids, int32_t n_old, const int32_t* new_ids,
+                       int32_t n_new, double* beta_out) {
+  if (!beta_out || (n_old > 0 && (!inter_to_old || !old_ids)) || (n_new > 0 && !new_ids))
+    return fail(SRA_E_NULL, "a required array is NULL");
+  if (n_old < 0 || n_new < 0) return fail(SRA_E_SHAPE, "negative prefix length");
+  double den = 0.0, num = 0.0;
+  std::vector<int> pos_new;   // position in the new prefix of each shared old chunk, in old order
+  for (int i = 0; i < n_old; ++i) {
+    den += inter_to_old[i];
+    for (int j = 0; j < n_new; ++j)
+      if (new_ids[j] == old_ids[i]) {
+        num += inter_to_old[i];
+        pos_new.push_back(j);
+        break;
+      }
+  }
+  if (den <= 0.0) {
+    *beta_out = 0.0;
+    return ok();
+  }
+  const int n = (int)pos_new.size();
+  double gamma = 0.0;
+  if (n >= 2) {
+    int64_t disc = 0;
+    for (int i = 0; i < n; ++i)
+      for (int j = i + 1; j < n; ++j) disc += pos_new[i] > pos_new[j] ? 1 : 0;
+    gamma = (double)disc / ((double)n * (n - 1) / 2.0);
+  }
+  *beta_out = num * (1.0 - gamma) / den;
+  return ok();
+}
+
+int sra_cachecraft_count(double alpha, double cci, double beta, int32_t n_tokens, int32_t* n_out) {
+  if (!n_out) return fail(SRA_E_NULL, "n_out is NULL");
+  if (n_tokens < 0) return fail(SRA_E_SHAPE, "n_tokens must be >= 0");
+  const double x = alpha * cci * (1.0 - beta) * (double)n_tokens;
+  double n = std::ceil(x);
+  n = std::min(std::max(n, 0.0), (double)n_tokens);
+  *n_out = (int32_t)n;
+  return ok();
+}
+
 int sra_score_select(const sra_shape* shape, int32_t n_req, const void* q_crit, int32_t Lq,
                      const void* k_crit_store, int64_t store_rows, const sra_chunk* chunks,
                      int32_t n_chunks, int32_t n_select, const int32_t* chunk_quota, float* scores,

@@ -187,7 +187,7 @@ namespace sra {
 hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
                            const void* ks, const void* vs, void* kf, void* vf, int64_t L,
                            double base, hipStream_t st);
-// Per recomputed row (row_pos[r] = p in [0, L)): the row's cos/sin table (cs_out, optional), the
+// Per recomputed row (row_pos[r] = p in [0, L); row_pos NULL: p = r): the row's cos/sin table (cs_out, optional), the
 // fresh K/V scatter (kn/vn optional) and, for bf16, the attention's prepared query operand (qn/qop
 // optional; rows outside [0, L) get zeros). Fresh rows are compact (row r) or, when indexed,
 // position-indexed (row p); fresh_rows is their count per request.
@@ -203,6 +203,12 @@ hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2
 hipError_t launch_anchor_prefix(int dtype, int D, int Hkv, const ChunkTab& tab, int k, int n_chunks,
                                 const int* anchors, const void* ks, const void* vs, void* kp, void* vp, int Lp,
                                 double base, hipStream_t st);
+// Chunk attention statistics of requests [req0, req0 + n_req_launch): tab holds their
+// (request, chunk) entries (dst = first token, len); fx: zeroed [n_req][Lctx][n_chunks] slots.
+hipError_t launch_chunk_stats(int D, int n_req_launch, int req0, int Hq, int Hkv, int Lctx, int Lk,
+                              const uint16_t* qop, int qop_blocks, const uint16_t* kc, const ChunkTab& tab,
+                              int n_chunks, unsigned long long* fx, float* inter, float* score, float* cci,
+                              hipStream_t st);
 // KV deviation of the first n_dev recomputed rows (dev: [n_req][n_dev] float32). Fresh rows are
 // compact or position-indexed as in launch_scatter; kf/vf hold the reused rows (not yet scattered).
 hipError_t launch_kv_deviation(int dtype, int D, int Hkv, int n_req, int R, int L, const void* kn,

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
   constexpr int NT = 128;
   __shared__ float2 cs[H];
   const int r = blockIdx.x, q = blockIdx.y;
-  const int p = row_pos[(int64_t)q * R + r];
+  const int p = row_pos ? row_pos[(int64_t)q * R + r] : r;   // no table: row r sits at position r
   const bool valid = p >= 0 && p < L;  // rows outside the cache are never written
   const int srow = valid ? (indexed ? p : r) : 0;
   const int64_t row_elems = (int64_t)Hkv * D;

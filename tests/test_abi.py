@@ -274,3 +274,41 @@ def test_anchor_prefix_host_errors():
     assert call(4, 15) == L.SRA_E_CHUNKS         # second chunk reads outside the store
     assert call(7, None) == L.SRA_E_NULL
     assert call(9, FAKE[0]) == L.SRA_E_ALIAS     # probe cache over the store
+
+
+def test_cachecraft_host_helpers_match_oracle():
+    import selective_recompute_attention_amd as sra
+    rng = np.random.default_rng(9)
+    for _ in range(500):
+        a, c, b = float(rng.uniform(0, 1)), float(rng.uniform(0, 1)), float(rng.choice([0.0, 0.25, rng.uniform(0, 1)]))
+        n = int(rng.integers(0, 600))
+        assert sra.cachecraft_count(a, c, b, n) == O.cachecraft_count(a, c, b, n)
+    for _ in range(300):
+        ids = list(rng.permutation(12)[:int(rng.integers(0, 8))])
+        new = list(rng.permutation(12)[:int(rng.integers(0, 10))])
+        att = {int(i): float(rng.uniform(0, 2)) for i in range(12)}
+        got = sra.prefix_overlap([att[i] for i in ids], ids, new)
+        assert got == O.prefix_overlap(att, ids, new)
+
+
+def test_stats_host_errors():
+    lib = L.lib()
+    ch = chunks([[0, 8, 0, 0], [8, 8, 8, 0]])
+    s = shape()
+    ws_need = lib.sra_stats_workspace_size(ctypes.byref(s), 1, 16, 2)
+    assert ws_need > 0
+    ok = [ctypes.byref(s), 1, FAKE[0], 20, FAKE[1], 20, ch, 2, FAKE[2], FAKE[3], FAKE[4], FAKE[5], ws_need, None]
+    def call(i=None, v=None):
+        x = list(ok)
+        if i is not None:
+            x[i] = v
+        return lib.sra_chunk_attention_stats(*x)
+    assert call(12, ws_need - 8) == L.SRA_E_WORKSPACE
+    assert call(3, 15) == L.SRA_E_SHAPE            # queries do not cover the context
+    assert call(4, None) == L.SRA_E_NULL
+    sf = shape(dtype=L.DTYPE_F32)
+    assert call(0, ctypes.byref(sf)) == L.SRA_E_DTYPE
+    assert call(8, FAKE[5]) == L.SRA_E_ALIAS        # inter written over the workspace
+    out = ctypes.c_int32()
+    assert lib.sra_cachecraft_count(0.5, 0.5, 0.0, -1, ctypes.byref(out)) == L.SRA_E_SHAPE
+    assert lib.sra_prefix_overlap(None, None, 2, None, 0, ctypes.byref(ctypes.c_double())) == L.SRA_E_NULL
