@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the side measurements (gradual filtering, pipelined layers, anchor probe, "
+                         "query-centric layers, chunk statistics): profiler runs then see only the step's kernels")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only plain device copies of known size (for scaling memory counters)")
@@ -287,6 +290,25 @@ def qc_layers_leg(sra, shape, w, ins, N, Lq, Lctx, hip, sp, n_layers=8):
             "qcall_over_critical": qc_all / one}
 
 
+def stats_leg(sra, shape, w, ins, Lctx, hip, sp):
+    """Cache-Craft attention statistics of this layer's full causal prefill (every context token
+    over the keys before it, per chunk). Algorithmic flops: 2 Hq d per (token, visible key) for the
+    logits (the two passes and the hi/lo split are the implementation's extra work)."""
+    import torch
+    cfg = w.cfg
+    n_chunks = w.chunks.shape[1]
+    kc = ins["k_new"]   # any bf16 keys of the right shape: the timing does not depend on values
+    inter = torch.empty((1, Lctx, n_chunks), dtype=torch.float32, device="cuda")
+    score = torch.empty((1, Lctx), dtype=torch.float32, device="cuda")
+    cci = torch.empty((1, n_chunks), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sra.stats_workspace_size(shape, 1, Lctx, n_chunks), dtype=torch.uint8, device="cuda")
+    ms = timed_calls(hip, sp, lambda: sra.chunk_attention_stats(shape, ins["q_new"], kc, w.chunks, ws, inter, score,
+                                                                 cci), 10)
+    flops = 2.0 * cfg.n_q_heads * cfg.head_dim * Lctx * (Lctx + 1) / 2.0
+    return {"tokens": Lctx, "ms_per_call": ms, "algorithmic_tflops": flops / (ms * 1e-3) / 1e12,
+            "kernels": "k_scatter (query operand) + k_chunk_stats + k_stats_finish"}
+
+
 def cpu_baseline(w, N, budget_s):
     """The fp64 oracle (as it stands) on the same workload: whole steps until the budget is used."""
     import oracle as O
@@ -432,10 +454,12 @@ def main():
         "scatter_hbm_gbs": s3_bytes / (stage_ms["scatter"] * 1e-3) / 1e9,
         "score_flops_tflops": s2_flops / (stage_ms["score_select"] * 1e-3) / 1e12,
     }
-    result["hkvd"] = hkvd_leg(sra, shape, reps[0], N, Lq, Lctx, kv_row_bytes, hip, sp)
-    result["pipeline"] = pipeline_leg(sra, shape, w, reps[0][0], ws, Lq, Lctx, hip, sp)
-    result["anchor_probe"] = probe_leg(sra, shape, w, reps[0], Lq, Lctx, hip, sp)
-    result["query_centric_layers"] = qc_layers_leg(sra, shape, w, reps[0][0], N, Lq, Lctx, hip, sp)
+    if not args.no_legs:
+        result["hkvd"] = hkvd_leg(sra, shape, reps[0], N, Lq, Lctx, kv_row_bytes, hip, sp)
+        result["pipeline"] = pipeline_leg(sra, shape, w, reps[0][0], ws, Lq, Lctx, hip, sp)
+        result["anchor_probe"] = probe_leg(sra, shape, w, reps[0], Lq, Lctx, hip, sp)
+        result["query_centric_layers"] = qc_layers_leg(sra, shape, w, reps[0][0], N, Lq, Lctx, hip, sp)
+        result["chunk_stats"] = stats_leg(sra, shape, w, reps[0][0], Lctx, hip, sp)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, N, args.cpu_seconds)
     # the parity of this exact output against the oracle is covered by the GPU tests

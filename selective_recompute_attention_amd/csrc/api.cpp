@@ -158,8 +158,8 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
     p.qop = ao; ao = align256(ao + (size_t)groups * p.qop_blocks * 32 * 2 * D * sizeof(uint16_t));
     p.tilecum = ao; ao = align256(ao + (size_t)n_req * (p.n_tiles + 1) * sizeof(int));
     const int64_t slots = groups * p.pieces * 2 * 128;
-    p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(float));
-    p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float2));
+    p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(uint16_t));
+    p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float4));
   }
   p.attn_end = ao;
   p.total = std::max(p.score_end, p.attn_end);
@@ -410,8 +410,8 @@ int do_attn(const sra_shape* s, int n_req, const void* q, int q_rows, int indexe
     e = sra::launch_attn_bf16(D, n_req, Hq, Hkv, R, L, reinterpret_cast<const uint16_t*>(wsp(ws, p.qop)),
                               p.qop_blocks, row_pos, (const uint16_t*)kf, (const uint16_t*)vf,
                               (uint16_t*)out, lse, p.pieces, reinterpret_cast<int*>(wsp(ws, p.tilecum)),
-                              reinterpret_cast<float*>(wsp(ws, p.part_o)),
-                              reinterpret_cast<float2*>(wsp(ws, p.part_ml)), st);
+                              reinterpret_cast<uint16_t*>(wsp(ws, p.part_o)),
+                              reinterpret_cast<float4*>(wsp(ws, p.part_ml)), st);
   } else {
     e = sra::launch_attn_f32(D, n_req, Hq, Hkv, R, L, (const float*)q, q_rows, indexed, row_pos,
                              reinterpret_cast<const float2*>(wsp(ws, p.cs)), (const float*)kf,

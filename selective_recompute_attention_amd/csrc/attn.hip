@@ -51,13 +51,19 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   int* tilecum;
-  float* part_o;
-  float2* part_ml;
+  uint16_t* part_o;   // fp16, scaled per vector
+  float4* part_ml;    // (max, sum, scale, 0) per vector
   int n_req, Hq, Hkv, g, R, L;
   int n_groups, n_tiles, qop_blocks, pieces;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// float pair -> two fp16 (round to nearest even) in one word, and back
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ float h2f(uint32_t h16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h16); }
 
 __device__ __forceinline__ int64_t part_index(const AttnArgs& a, int group, int piece, int slot) {
   return ((int64_t)(group * a.pieces + piece) * 2 + slot) * 128;
@@ -335,18 +341,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
               l_tot > 0.f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
       }
     } else {
-      // the wave's 32 vectors of the slot: a uniform base and 32-bit lane offsets
+      // the wave's 32 vectors of the slot (a uniform base and 32-bit lane offsets), O as fp16 scaled by
+      // the vector's largest |O|: half the bytes of float32, 11-bit significands at any magnitude
+      float mx = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, fabsf(o[dt][rr]));
+      mx = half_max(mx);
+      const float osc = mx > 0.f ? mx : 1.f, oinv = 1.f / osc;
       const int64_t pw = part_index(a, group, piece, slot) + __builtin_amdgcn_readfirstlane(wave) * 32;
-      float* pob = a.part_o + pw * D;
+      uint16_t* pob = a.part_o + pw * D;
       const uint32_t lo = (uint32_t)(e32 * D + 4 * ehh);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
-          const f32x4 w = {o[dt][4 * b4], o[dt][4 * b4 + 1], o[dt][4 * b4 + 2], o[dt][4 * b4 + 3]};
-          *reinterpret_cast<f32x4*>(pob + (lo + (uint32_t)(32 * dt + 8 * b4))) = w;
+          u32x2 w;
+          w[0] = pack_h2(o[dt][4 * b4] * oinv, o[dt][4 * b4 + 1] * oinv);
+          w[1] = pack_h2(o[dt][4 * b4 + 2] * oinv, o[dt][4 * b4 + 3] * oinv);
+          *reinterpret_cast<u32x2*>(pob + (lo + (uint32_t)(32 * dt + 8 * b4))) = w;
         }
-      if (ehh == 0) a.part_ml[pw + e32] = make_float2(l_tot > 0.f ? m_ref : -INFINITY, l_tot);
+      if (ehh == 0) a.part_ml[pw + e32] = make_float4(l_tot > 0.f ? m_ref : -INFINITY, l_tot, osc, 0.f);
     }
     slot = 1;
     u = se;
@@ -385,17 +401,20 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   float M = -INFINITY, Ls = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < n; k0 += B) {
-    float2 ml[B];
-    f32x4 ov[B];
+    float4 ml[B];
+    u32x2 hv[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {   // clamped, unconditional loads: all in flight at once
       const int64_t pi = pidx(min(k0 + k, n - 1));
       ml[k] = a.part_ml[pi];
-      ov[k] = *reinterpret_cast<const f32x4*>(a.part_o + pi * D + 4 * dc);
+      hv[k] = *reinterpret_cast<const u32x2*>(a.part_o + pi * D + 4 * dc);
     }
+    f32x4 ov[B];
 #pragma unroll
-    for (int k = 0; k < B; ++k)
-      if (k0 + k >= n) ml[k] = make_float2(-INFINITY, 0.f);
+    for (int k = 0; k < B; ++k) {
+      if (k0 + k >= n) ml[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+      ov[k] = f32x4{h2f(hv[k][0] & 0xffffu), h2f(hv[k][0] >> 16), h2f(hv[k][1] & 0xffffu), h2f(hv[k][1] >> 16)} * ml[k].z;
+    }
     float mb = M;
 #pragma unroll
     for (int k = 0; k < B; ++k) mb = fmaxf(mb, ml[k].x);
@@ -523,7 +542,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(int Hq, int Hkv, int R, int L,
 hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,
                             int qop_blocks, const int* row_pos, const uint16_t* kf,
                             const uint16_t* vf, uint16_t* out, float* lse, int pieces,
-                            int* tilecum, float* part_o, float2* part_ml, hipStream_t st) {
+                            int* tilecum, uint16_t* part_o, float4* part_ml, hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   AttnArgs a;
   a.qop = qop; a.row_pos = row_pos; a.kf = kf; a.vf = vf; a.out = out; a.lse = lse;

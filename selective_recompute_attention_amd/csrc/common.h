@@ -256,11 +256,12 @@ hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int np
                          int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
                          const int* map = nullptr, int map_stride = 0);
 // qop: prepared query operand (qop_blocks blocks of 32 vectors per group); tilecum: [n_req][tiles+1]
-// ints; part_o / part_ml: [n_groups][pieces][2][128] partial results.
+// ints; part_o ([..][D] fp16, scaled) / part_ml ((max, sum, scale, 0)): [n_groups][pieces][2][128]
+// partial results.
 hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,
                             int qop_blocks, const int* row_pos, const uint16_t* kf,
                             const uint16_t* vf, uint16_t* out, float* lse, int pieces,
-                            int* tilecum, float* part_o, float2* part_ml, hipStream_t st);
+                            int* tilecum, uint16_t* part_o, float4* part_ml, hipStream_t st);
 hipError_t launch_attn_f32(int D, int n_req, int Hq, int Hkv, int R, int L, const float* q,
                            int q_rows, int indexed, const int* row_pos, const float2* cs,
                            const float* kf, const float* vf, float* out, float* lse,
