@@ -13,9 +13,10 @@
 //   * Persistent split: a fixed grid of work groups per group (two per compute unit in total).
 //     Each work group computes the tiles' unit counts from row_pos, takes the contiguous unit range
 //     [U i / P, U (i+1) / P) and walks it tile by tile. A tile it covers whole is written directly;
-//     a cut tile leaves a partial (O, max, sum) in one of two slots (first / last tile of the
-//     range) and the merge kernel combines the pieces of such tiles in key order. Every work group
-//     therefore gets the same number of key units, whatever the position mix.
+//     a cut tile leaves a partial (O as fp16 scaled by the vector's largest |O|, max, sum) in one of
+//     two slots (first / last tile of the range) and the merge kernel combines the pieces of such
+//     tiles in key order. Every work group therefore gets the same number of key units, whatever
+//     the position mix.
 //   * Four waves, 32 query vectors each. S^T = K Q^T puts one query vector per lane column, so the
 //     online-softmax row reductions stay in-lane plus one cross-half shuffle, and the probabilities
 //     feed O^T = V^T P^T directly from registers (keys permuted consistently on both operands).
@@ -23,7 +24,8 @@
 //     planes (rounding the rotated query to one bf16 would move the logits by ~1e-3 relative, the
 //     dominant output error); each wave reads it as consecutive 1 KB blocks.
 //   * 64-key tiles of K (row-major, padded) and V (transposed on the way into LDS) are shared by
-//     the four waves; float32 accumulation, exp2 in the log2 domain. Work groups are numbered with
+//     the four waves; float32 accumulation, exp2 in the log2 domain against a lazily moved
+//     reference maximum; each 32-key half is one online-softmax step. Work groups are numbered with
 //     the group index fastest, so all work of one KV head lands on one XCD (work groups are dealt
 //     round-robin over the 8 XCDs) and its K/V stay in that XCD's L2.
 // f32 path: plain float32 arithmetic, one block per (row, KV head), exact online softmax.

@@ -1,6 +1,6 @@
-"""HIP graph capture of the whole step (anchors on a second stream, the fused layer with its own
-internal fork/join): every replay must leave exactly what eager calls leave, also when eager work
-on other inputs has run in between and overwritten the shared workspace.
+"""HIP graph capture of a step (standalone anchors on a second stream, then the fused layer on the
+capturing stream): every replay must leave exactly what eager calls leave, also when eager work on
+other inputs has run in between and overwritten the shared workspace.
 """
 import numpy as np
 import pytest
