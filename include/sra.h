@@ -136,7 +136,9 @@ typedef struct {
     float* lse;                    /* [n_req][R][Hq] natural-log sum of exp, or NULL         */
     /* optional profiling: host array of 8 events, or NULL. When set, stage s (0 re-rotation,
      * 1 scoring and selection, 2 scatter, 3 attention) is bracketed by hipEventRecord of
-     * stage_events[2s] and stage_events[2s+1] on `stream` (stage 1 is empty without q_crit). */
+     * stage_events[2s] and stage_events[2s+1] on `stream` (stage 1 is empty without q_crit;
+     * with q_crit and bfloat16 storage the re-rotation runs inside the scoring launch, so stage
+     * 0 is empty and stage 1 covers both). */
     hipEvent_t* stage_events;
 } sra_layer_args;
 
@@ -346,7 +348,8 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
  * args->q_crit is set, or gradual filtering of args->hkvd_prev when that is set (otherwise
  * args->row_pos is taken as given), then S3 scatter of the
  * fresh K/V rows gathered from the position-indexed fresh buffers at row_pos, then S4
- * attention of those rows. Fills k_fused/v_fused (the cache handed on to decoding), out,
+ * attention of those rows (S1 and S2 are independent; with bfloat16 scoring S1 shares the
+ * scoring's first launch). Fills k_fused/v_fused (the cache handed on to decoding), out,
  * lse, row_pos and scores. ws: at least
  * sra_workspace_size(&args->shape, n_req, n_chunks, total_len, n_rows, query_len) bytes.
  * Errors: as the stage calls. */

@@ -336,7 +336,8 @@ int resolve_count(int n_req, int n_chunks, const sra_chunk* ch, int Lctx, int n_
 int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const void* kc,
                     const sra_chunk* ch, int n_chunks, int Lctx, int N, const int32_t* quota,
                     float* scores, int32_t* row_pos, void* ws, const Plan& p, hipStream_t st,
-                    const sra::AnchorOut& anc = sra::AnchorOut()) {
+                    const sra::AnchorOut& anc = sra::AnchorOut(),
+                    const sra::RerotFused& rf = sra::RerotFused()) {
   const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads, g = Hq / Hkv;
   const int R = N + Lq;
   float* sc = scores ? scores : reinterpret_cast<float*>(wsp(ws, p.scores_tmp));
@@ -371,7 +372,7 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
       e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
         return sra::launch_score_pass(pass, D, tab, req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, Lctx, kc,
                                       qrot, p.qrot_plane, first, blk_base, ml_part, ml_final, fuse_merge,
-                                      fx, anc, st);
+                                      fx, anc, rf, st);
       });
       if (e != hipSuccess) return hip_fail(e, pass == 1 ? "score pass 1 launch" : "score pass 2 launch");
     }
@@ -913,10 +914,22 @@ int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStre
     hipError_t er = hipEventRecord(ev[i], stream);
     return er == hipSuccess ? SRA_OK : hip_fail(er, "stage event record");
   };
-  // one stream: a second stream's fork/join costs more host and GPU time than S1 || S2 saves
+  // One stream: a second stream's fork/join costs more host and GPU time than S1 || S2 saves.
+  // With bfloat16 scoring, S1 runs as extra blocks of scoring pass 1 instead (pass 1 fills a
+  // fraction of the chip), so S1's stage events then mark an empty interval.
+  const bool s1_in_score = a->q_crit && s->dtype == SRA_DTYPE_BF16;
+  sra::RerotFused rf;
+  if (s1_in_score) {
+    rf.ks = static_cast<const uint16_t*>(a->k_store);
+    rf.vs = static_cast<const uint16_t*>(a->v_store);
+    rf.kf = static_cast<uint16_t*>(a->k_fused);
+    rf.vf = static_cast<uint16_t*>(a->v_fused);
+    rf.L = L;
+    rf.base = s->rope_base;
+  }
   if ((rc = mark(0))) return rc;
-  if ((rc = do_rerotate(s, n_req, a->k_store, a->v_store, a->chunks, a->n_chunks, a->k_fused,
-                        a->v_fused, L, stream)))
+  if (!s1_in_score && (rc = do_rerotate(s, n_req, a->k_store, a->v_store, a->chunks, a->n_chunks, a->k_fused,
+                                        a->v_fused, L, stream)))
     return rc;
   if ((rc = mark(1)) || (rc = mark(2))) return rc;
   if (hkvd) {   // deviation against the re-rotated reused rows, before the scatter replaces them
@@ -935,7 +948,7 @@ int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStre
       anc.n_chunks = a->n_chunks;
     }
     if ((rc = do_score_select(s, n_req, a->q_crit, Lq, a->k_crit_store, a->chunks, a->n_chunks, Lctx,
-                              N, a->chunk_quota, a->scores, a->row_pos, ws, p, stream, anc)))
+                              N, a->chunk_quota, a->scores, a->row_pos, ws, p, stream, anc, rf)))
       return rc;
     if (ak > 0 && !anchors_fused) {   // the standalone kernels, over every (request, chunk)
       std::vector<Entry> ents;

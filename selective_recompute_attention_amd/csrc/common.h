@@ -237,11 +237,26 @@ hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv
                              int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
                              int entry_base, float scale_log2, unsigned long long* fx, double base,
                              hipStream_t st);
+// S1 carried by pass 1 (bfloat16 storage): the pass adds, per KV head y, one block per kS1Fold
+// key blocks that re-rotates every head of those key blocks' rows [y * ceil(128 / Hkv), ...) of
+// the stored chunk (the same rows and chunk entries as a standalone re-rotation). Pass 1 holds one
+// work group per CU, so the extra blocks are few and long enough to fit beside the scoring blocks
+// in one round. kf == NULL: none.
+constexpr int kS1Fold = 2;
+struct RerotFused {
+  const uint16_t* ks = nullptr;
+  const uint16_t* vs = nullptr;
+  uint16_t* kf = nullptr;
+  uint16_t* vf = nullptr;
+  int64_t L = 0;
+  double base = 0.0;
+};
 hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
-                             unsigned long long* fx, const AnchorOut& anc, hipStream_t st);
+                             unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
+                             hipStream_t st);
 hipError_t launch_score_merge(const int* req_blk0, int n_req, int Hkv, int Mpad, int Mvalid,
                               const float2* ml_part, float2* ml_final, hipStream_t st);
 hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,

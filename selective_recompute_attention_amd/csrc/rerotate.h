@@ -1,0 +1,118 @@
+// S1 re-rotation of a run of cached chunk rows into the fused cache, shared by the standalone
+// re-rotation kernel and by the critical-layer scoring pass, whose spare blocks carry it.
+//
+// S1 follows "full KV reuse after adjusting the position encoding" (CacheBlend problem definition
+// page, §2.4): a chunk cached at original positions orig + t moves to fused rows n_c + t, so each
+// key pair (x_i, x_{i+d/2}) turns by delta_c * theta_i with delta_c = n_c - orig.
+#pragma once
+#include "common.h"
+
+namespace sra {
+namespace rerot {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Vec;  // 16-byte vector of T, unpacked to float
+template <>
+struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(v4u v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(v[k] << 16);
+      f[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+    }
+  }
+  __device__ static v4u pack(const float* f) {
+    v4u v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = pack_bf2(f[2 * k], f[2 * k + 1]);
+    return v;
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(v4u v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]);
+  }
+  __device__ static v4u pack(const float* f) {
+    v4u v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __float_as_uint(f[k]);
+    return v;
+  }
+};
+
+// Rows [t0, t0 + nr) of chunk entry e (nr >= 1), all KV heads, by one block of 256 threads (every
+// thread must call it). Each batch loads its V chunks and K pairs (16 bytes per half) before the
+// angles are formed, so the memory latency overlaps the float64 sin/cos; V is stored as is and K
+// rotated, its bits kept when delta = 0. cs is LDS scratch of d/2 float2.
+template <typename T, int D>
+__device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr, int Hkv,
+                                     const T* __restrict__ ks, const T* __restrict__ vs,
+                                     T* __restrict__ kf, T* __restrict__ vf, int64_t L,
+                                     const Theta& th, float2* cs) {
+  constexpr int H = D / 2;
+  constexpr int VW = Vec<T>::N;
+  constexpr int UPH = H / VW;   // K pair units per head
+  constexpr int UV = 4, UK = 2; // per thread and batch: V chunks, K pair units
+  const int delta = tab.delta[e];
+  const int64_t row_elems = (int64_t)Hkv * D;
+  const int64_t src0 = ((int64_t)tab.src[e] + t0) * row_elems;
+  const int64_t dst0 = ((int64_t)tab.req[e] * L + tab.dst[e] + t0) * row_elems;
+  const int64_t nV = (int64_t)nr * row_elems * (int64_t)sizeof(T) / 16;   // V 16-byte chunks
+  const int64_t nK = (int64_t)nr * Hkv * UPH;                             // K pair units
+  const v4u* vsrc = reinterpret_cast<const v4u*>(vs + src0);
+  v4u* vdst = reinterpret_cast<v4u*>(vf + dst0);
+  bool first = true;
+  for (int64_t bv = 0, bk = 0; bv < nV || bk < nK; bv += 256 * UV, bk += 256 * UK) {
+    v4u v[UV], ka[UK], kb[UK];
+#pragma unroll
+    for (int i = 0; i < UV; ++i) v[i] = vsrc[min(bv + threadIdx.x + 256 * i, nV - 1)];
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int64_t u = min(bk + threadIdx.x + 256 * i, nK - 1);
+      const T* a = ks + src0 + (u / UPH) * D + (u % UPH) * VW;
+      ka[i] = *reinterpret_cast<const v4u*>(a);
+      kb[i] = *reinterpret_cast<const v4u*>(a + H);
+    }
+    if (first) {   // uniform: the angles once per block, while the loads are in flight
+      if (delta != 0)
+        for (int i = threadIdx.x; i < H; i += 256) cs[i] = rope_cs((double)delta, th.v[i]);
+      __syncthreads();
+      first = false;
+    }
+#pragma unroll
+    for (int i = 0; i < UV; ++i)
+      if (bv + threadIdx.x + 256 * i < nV) vdst[bv + threadIdx.x + 256 * i] = v[i];
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int64_t u = bk + threadIdx.x + 256 * i;
+      if (u >= nK) continue;
+      const int i0 = (int)(u % UPH) * VW;
+      T* o = kf + dst0 + (u / UPH) * D + i0;
+      if (delta == 0) {   // rotation by zero is the identity: keep the cached bits
+        *reinterpret_cast<v4u*>(o) = ka[i];
+        *reinterpret_cast<v4u*>(o + H) = kb[i];
+      } else {
+        float fa[VW], fb[VW], ra[VW], rb[VW];
+        Vec<T>::unpack(ka[i], fa);
+        Vec<T>::unpack(kb[i], fb);
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+          const float c = cs[i0 + k].x, sn = cs[i0 + k].y;
+          ra[k] = fa[k] * c - fb[k] * sn;
+          rb[k] = fa[k] * sn + fb[k] * c;
+        }
+        *reinterpret_cast<v4u*>(o) = Vec<T>::pack(ra);
+        *reinterpret_cast<v4u*>(o + H) = Vec<T>::pack(rb);
+      }
+    }
+  }
+}
+
+}  // namespace rerot
+}  // namespace sra

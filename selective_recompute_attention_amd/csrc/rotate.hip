@@ -1,125 +1,32 @@
-// Streaming rotary kernels: S1 re-rotation of cached chunk keys into the fused cache, S3 scatter
-// of fresh K/V rows together with the sparse attention's per-row inputs (angle table or prepared
-// query operand), and the row check.
+// Streaming rotary kernels: S1 re-rotation of cached chunk keys into the fused cache (its body is
+// shared with the scoring pass that can carry it), S3 scatter of fresh K/V rows together with the
+// sparse attention's per-row inputs (angle table or prepared query operand), and the row check.
 //
-// S1 follows "full KV reuse after adjusting the position encoding" (CacheBlend problem definition
-// page, §2.4): a chunk cached at original positions orig + t moves to fused rows n_c + t, so each
-// key pair (x_i, x_{i+d/2}) turns by delta_c * theta_i with delta_c = n_c - orig. S3 follows the
-// per-layer selective recompute flow (KVCache reuse 01, §1.3.4): fresh K/V of the selected tokens
-// replace the reused rows, K rotated at the token's absolute position.
+// S3 follows the per-layer selective recompute flow (KVCache reuse 01, §1.3.4): fresh K/V of the
+// selected tokens replace the reused rows, K rotated at the token's absolute position.
 //
 // Both are pure HBM streams: every thread moves 16-byte vectors, rows are contiguous, angles are
 // formed once per block in float64 and kept in LDS as float32 cos/sin.
 #include "common.h"
+#include "rerotate.h"
 
 namespace sra {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
-struct Vec;  // 16-byte vector of T, unpacked to float
-template <>
-struct Vec<uint16_t> {
-  static constexpr int N = 8;
-  __device__ static void unpack(u32x4 v, float* f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[2 * k] = __uint_as_float(v[k] << 16);
-      f[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
-    }
-  }
-  __device__ static u32x4 pack(const float* f) {
-    u32x4 v;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = pack_bf2(f[2 * k], f[2 * k + 1]);
-    return v;
-  }
-};
-template <>
-struct Vec<float> {
-  static constexpr int N = 4;
-  __device__ static void unpack(u32x4 v, float* f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]);
-  }
-  __device__ static u32x4 pack(const float* f) {
-    u32x4 v;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = __float_as_uint(f[k]);
-    return v;
-  }
-};
+using rerot::Vec;
 
-// One block per (chunk entry, block of rows_per_blk rows of that chunk). Each batch loads its V
-// chunks and K pairs (16 bytes per half) before the angles are formed, so the memory latency
-// overlaps the float64 sin/cos; then V is stored as is and K rotated (bits kept when delta = 0).
+// One block per (chunk entry, block of rows_per_blk rows of that chunk), all KV heads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int rows_per_blk,
                                                   const T* __restrict__ ks,
                                                   const T* __restrict__ vs, T* __restrict__ kf,
                                                   T* __restrict__ vf, int64_t L, Theta th) {
-  constexpr int H = D / 2;
-  constexpr int VW = Vec<T>::N;
-  constexpr int UPH = H / VW;   // K pair units per head
-  constexpr int UV = 4, UK = 2; // per thread and batch: V chunks, K pair units
-  __shared__ float2 cs[H];
+  __shared__ float2 cs[D / 2];
   const int e = find_entry(tab, blockIdx.x);
   const int t0 = (blockIdx.x - tab.blk0[e]) * rows_per_blk;
-  const int nr = min(rows_per_blk, tab.len[e] - t0);
-  const int delta = tab.delta[e];
-  const int64_t row_elems = (int64_t)Hkv * D;
-  const int64_t src0 = ((int64_t)tab.src[e] + t0) * row_elems;
-  const int64_t dst0 = ((int64_t)tab.req[e] * L + tab.dst[e] + t0) * row_elems;
-  const int64_t nV = (int64_t)nr * row_elems * (int64_t)sizeof(T) / 16;   // V 16-byte chunks
-  const int64_t nK = (int64_t)nr * Hkv * UPH;                             // K pair units
-  const u32x4* vsrc = reinterpret_cast<const u32x4*>(vs + src0);
-  u32x4* vdst = reinterpret_cast<u32x4*>(vf + dst0);
-  bool first = true;
-  for (int64_t bv = 0, bk = 0; bv < nV || bk < nK; bv += 256 * UV, bk += 256 * UK) {
-    u32x4 v[UV], ka[UK], kb[UK];
-#pragma unroll
-    for (int i = 0; i < UV; ++i) v[i] = vsrc[min(bv + threadIdx.x + 256 * i, nV - 1)];
-#pragma unroll
-    for (int i = 0; i < UK; ++i) {
-      const int64_t u = min(bk + threadIdx.x + 256 * i, nK - 1);
-      const T* a = ks + src0 + (u / UPH) * D + (u % UPH) * VW;
-      ka[i] = *reinterpret_cast<const u32x4*>(a);
-      kb[i] = *reinterpret_cast<const u32x4*>(a + H);
-    }
-    if (first) {   // uniform: the angles once per block, while the loads are in flight
-      if (delta != 0)
-        for (int i = threadIdx.x; i < H; i += blockDim.x) cs[i] = rope_cs((double)delta, th.v[i]);
-      __syncthreads();
-      first = false;
-    }
-#pragma unroll
-    for (int i = 0; i < UV; ++i)
-      if (bv + threadIdx.x + 256 * i < nV) vdst[bv + threadIdx.x + 256 * i] = v[i];
-#pragma unroll
-    for (int i = 0; i < UK; ++i) {
-      const int64_t u = bk + threadIdx.x + 256 * i;
-      if (u >= nK) continue;
-      const int i0 = (int)(u % UPH) * VW;
-      T* o = kf + dst0 + (u / UPH) * D + i0;
-      if (delta == 0) {   // rotation by zero is the identity: keep the cached bits
-        *reinterpret_cast<u32x4*>(o) = ka[i];
-        *reinterpret_cast<u32x4*>(o + H) = kb[i];
-      } else {
-        float fa[VW], fb[VW], ra[VW], rb[VW];
-        Vec<T>::unpack(ka[i], fa);
-        Vec<T>::unpack(kb[i], fb);
-#pragma unroll
-        for (int k = 0; k < VW; ++k) {
-          const float c = cs[i0 + k].x, sn = cs[i0 + k].y;
-          ra[k] = fa[k] * c - fb[k] * sn;
-          rb[k] = fa[k] * sn + fb[k] * c;
-        }
-        *reinterpret_cast<u32x4*>(o) = Vec<T>::pack(ra);
-        *reinterpret_cast<u32x4*>(o + H) = Vec<T>::pack(rb);
-      }
-    }
-  }
+  rerot::rows<T, D>(tab, e, t0, min(rows_per_blk, tab.len[e] - t0), Hkv, ks, vs, kf, vf, L, th, cs);
 }
 
 // One block per (recomputed row r, request) at position p = row_pos[r]: forms the row's angles

@@ -22,6 +22,7 @@
 #include <float.h>
 
 #include "common.h"
+#include "rerotate.h"
 
 namespace sra {
 namespace {
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
                                                     const float2* __restrict__ ml_final,
                                                     int fuse_merge,
                                                     unsigned long long* __restrict__ fx,
-                                                    AnchorOut anc) {
+                                                    AnchorOut anc, RerotFused rf, Theta th) {
   constexpr int NKS = D / 16;
   constexpr int KB = 128;          // keys per block
   constexpr int KST = D + 8;       // LDS row stride (elements)
@@ -252,8 +253,22 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
   __shared__ float colred[4][KB];
   __shared__ float2 mlw[4][32];
   const int blk = blockIdx.x, kvh = blockIdx.y;
-  if (blk >= tab.blk0[tab.n]) {   // pass 2's extra blocks: one per chunk entry picks its anchors
-    if constexpr (PASS == 2) {
+  if (blk >= tab.blk0[tab.n]) {
+    if constexpr (PASS == 1) {   // extra blocks: S1 for a share of kS1Fold key blocks' rows
+      const int per = (KB + Hkv - 1) / Hkv;
+      for (int j = 0; j < kS1Fold; ++j) {
+        const int b = (blk - tab.blk0[tab.n]) * kS1Fold + j;
+        if (b >= tab.blk0[tab.n]) break;
+        const int e = find_entry(tab, b);
+        const int tb = (b - tab.blk0[e]) * KB;
+        const int nr = min(per, min(KB, tab.len[e] - tb) - kvh * per);
+        if (nr <= 0) continue;
+        if (j > 0) __syncthreads();   // the previous share's angles are retired
+        rerot::rows<uint16_t, D>(tab, e, tb + kvh * per, nr, Hkv, rf.ks, rf.vs, rf.kf, rf.vf, rf.L, th,
+                                 reinterpret_cast<float2*>(Ks));
+      }
+    } else {   // one block per chunk entry picks its anchors
+
       const int e = blk - tab.blk0[tab.n];
       if (kvh == 0)
         anchor_block(tab.len[e], (int64_t)tab.req[e] * Lctx + tab.dst[e], tab.src[e],
@@ -438,18 +453,22 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
-                             unsigned long long* fx, const AnchorOut& anc, hipStream_t st) {
+                             unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
+                             hipStream_t st) {
   const int nblk = tab.blk0[tab.n];
   if (nblk == 0) return hipSuccess;
   ReqBlocks rb;
   for (int r = 0; r <= n_req; ++r) rb.blk0[r] = req_blk0[r];
-  // pass 2 carries one extra block per entry for the anchors
-  dim3 g(nblk + (pass == 2 && anc.k > 0 ? tab.n : 0), Hkv), b(256);
+  // pass 1 may carry S1 (one extra block per key block and KV head), pass 2 the anchors (one
+  // extra block per entry)
+  const int extra = pass == 1 ? (rf.kf ? (nblk + kS1Fold - 1) / kS1Fold : 0) : (anc.k > 0 ? tab.n : 0);
+  dim3 g(nblk + extra, Hkv), b(256);
   const uint16_t* k = (const uint16_t*)kc;
+  const Theta th = rf.kf ? make_theta(D, rf.base) : Theta{};
 #define SRA_PASS(DD, PP)                                                                        \
   k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
                                           entry_base, blk_base, ml_part, ml_final, fuse_merge,  \
-                                          fx, anc)
+                                          fx, anc, rf, th)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);
   else if (D == 128) SRA_PASS(128, 2);
   else if (pass == 1) SRA_PASS(64, 1);
