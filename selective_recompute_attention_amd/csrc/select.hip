@@ -4,11 +4,16 @@
 //
 // One block of 256 threads per selection unit (a whole request, or one chunk of a request when
 // per-chunk quotas are given). The block first forms the scores (fixed-point totals over KV heads,
-// or per-head float partials added in a fixed order), then finds the score of the N-th best token exactly with an 8-bit radix
-// select over order-preserving 32-bit keys (leading bytes shared by every key are skipped), and
-// finally writes, in ascending position order, every token above that score plus the lowest-index
-// tokens equal to it. All decisions are integer comparisons of the same float32 bits, so the result
-// is deterministic.
+// or per-head float partials added in a fixed order), then finds the score of the N-th best token
+// exactly with an 8-bit radix select over order-preserving 32-bit keys (leading bytes shared by
+// every key are skipped), and finally writes, in ascending position order, every token above that
+// score plus the lowest-index tokens equal to it. All decisions are integer comparisons of the
+// same float32 bits, so the result is deterministic.
+//
+// The kernel is a chain of dependent steps on one CU, so it is written for latency: the score
+// loads go out before the histograms are cleared, each radix pass costs two barriers (count, then
+// one wave scans the 256 bins with 16-byte LDS reads), and one two-value block scan places the
+// output.
 #include "common.h"
 
 namespace sra {
@@ -16,30 +21,16 @@ namespace {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelLdsKeys = 12288;   // keys of one selection unit kept in LDS (48 KB)
+constexpr int kSelSub = 8;           // copies of each histogram bin, chosen by lane
+
+enum SelSrc { kFromFixed = 0, kFromParts = 1, kFromScores = 2 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of x over the block (4 waves, in thread order); also the total.
-__device__ __forceinline__ int block_excl_sum(int x, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int incl = (int)wave_incl_sum((uint32_t)x);
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
-    const int c = wsum[w];
-    before += (w < wave) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  total = tot;
-  return before + incl - x;
-}
-
+template <int SRC>
 __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsigned long long* __restrict__ fx,
                                                         int nparts, int Lctx, int Lq, int R,
                                                         const float* __restrict__ parts,
@@ -48,12 +39,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
                                                         const int* __restrict__ map, int map_stride) {
   constexpr int NW = kSelThreads / 64;
   constexpr int KREG = 16;   // keys per thread held in registers (units up to 4096 keys)
-  constexpr int kSub = 4;
-  __shared__ unsigned hist[4][NW][256 * kSub];   // per radix pass and wave: kSub copies of each bin
-  __shared__ uint32_t sh_prefix, sh_remaining;
-  __shared__ uint32_t sh_and[NW], sh_or[NW];
-  __shared__ int wsum[NW];
-  __shared__ uint32_t kl[kSelLdsKeys];   // larger units' keys when they fit
+  // one histogram per key byte, kSelSub copies of each bin (lanes of a wave that hit the same bin,
+  // common while the leading bytes take few values, spread over the copies)
+  __shared__ __attribute__((aligned(16))) uint32_t hist[4][256 * kSelSub];
+  __shared__ uint32_t kl[kSelLdsKeys];   // the unit's keys when they fit
+  __shared__ uint32_t sh_and[NW], sh_or[NW], sh_sel[2];
+  __shared__ uint32_t wsum[2][NW];
   const int e = blockIdx.x;
   const int req = tab.req[e], begin = tab.begin[e], len = tab.len[e];
   const int quota = tab.quota[e], off = tab.out_off[e];
@@ -67,24 +58,48 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
   const int jlo = min((int)threadIdx.x * per, len), jhi = min(jlo + per, len), cnt = jhi - jlo;
   const bool in_regs = len > 0 && per <= KREG;
   const bool in_lds = len <= kSelLdsKeys;
-  for (int i = threadIdx.x; i < 4 * NW * 256 * kSub; i += kSelThreads) (&hist[0][0][0])[i] = 0;
+  auto clear_hist = [&]() {
+    uint4* h = reinterpret_cast<uint4*>(&hist[0][0]);
+#pragma unroll
+    for (int i = 0; i < 4 * 256 * kSelSub / 4 / kSelThreads; ++i) h[threadIdx.x + kSelThreads * i] = uint4{0u, 0u, 0u, 0u};
+  };
+  auto score_at = [&](int j) -> float {   // one score, loads in order (large units)
+    if constexpr (SRC == kFromFixed) {
+      return (float)((double)fx[(int64_t)req * Lctx + begin + j] * (1.0 / kScoreFixScale));
+    } else if constexpr (SRC == kFromParts) {
+      const float* prow = parts + (int64_t)req * nparts * Lctx + begin;
+      float sv = 0.f;
+      for (int p0 = 0; p0 < nparts; p0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = prow[(int64_t)min(p0 + u, nparts - 1) * Lctx + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (p0 + u < nparts) sv += v[u];
+      }
+      return sv;
+    } else {
+      return srow[j];
+    }
+  };
 
-  // scores: per-KV-head partial column sums added in head order, then order-preserving keys. The
-  // loads are coalesced (position j = tid + 256 i); small units then pass their keys through LDS
-  // into this thread's contiguous range of registers.
-  const float* prow = parts + (int64_t)req * nparts * Lctx + begin;
+  // scores -> order-preserving keys; coalesced loads (position j = tid + 256 i), all issued before
+  // the histograms are cleared; small units then pass their keys through LDS into this thread's
+  // contiguous range of registers
   uint32_t kreg[KREG];
   uint32_t kand = ~0u, kor = 0u;
   if (in_regs) {
     float sv[KREG];
-    if (fx) {
+    if constexpr (SRC == kFromFixed) {
       const unsigned long long* frow = fx + (int64_t)req * Lctx + begin;
-      unsigned long long fv[KREG];   // one batch of independent loads
+      unsigned long long fv[KREG];
 #pragma unroll
       for (int i = 0; i < KREG; ++i) fv[i] = frow[min((int)threadIdx.x + kSelThreads * i, len - 1)];
+      clear_hist();
 #pragma unroll
       for (int i = 0; i < KREG; ++i) sv[i] = (float)((double)fv[i] * (1.0 / kScoreFixScale));
-    } else if (nparts > 0) {
+    } else if constexpr (SRC == kFromParts) {
+      const float* prow = parts + (int64_t)req * nparts * Lctx + begin;
 #pragma unroll
       for (int i = 0; i < KREG; ++i) sv[i] = 0.f;
       for (int p0 = 0; p0 < nparts; p0 += 8) {
@@ -93,71 +108,54 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
         for (int i = 0; i < KREG; ++i)
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            v[i][u] = (i < per) ? prow[(int64_t)min(p0 + u, nparts - 1) * Lctx +
-                                       min((int)threadIdx.x + kSelThreads * i, len - 1)] : 0.f;
+            v[i][u] = prow[(int64_t)min(p0 + u, nparts - 1) * Lctx + min((int)threadIdx.x + kSelThreads * i, len - 1)];
+        if (p0 == 0) clear_hist();
 #pragma unroll
         for (int i = 0; i < KREG; ++i)
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             if (p0 + u < nparts) sv[i] += v[i][u];
       }
+      if (nparts <= 0) clear_hist();
     } else {
 #pragma unroll
-      for (int i = 0; i < KREG; ++i)
-        sv[i] = (i < per) ? srow[min((int)threadIdx.x + kSelThreads * i, len - 1)] : 0.f;
+      for (int i = 0; i < KREG; ++i) sv[i] = srow[min((int)threadIdx.x + kSelThreads * i, len - 1)];
+      clear_hist();
     }
 #pragma unroll
     for (int i = 0; i < KREG; ++i) {
       const int j = threadIdx.x + kSelThreads * i;
-      if (i < per && j < len) {
-        if (fx || nparts > 0) srow[j] = sv[i];
-        kl[j] = order_key(sv[i]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KREG; ++i) {
-      kreg[i] = kl[min(jlo + i, len - 1)];
-      if (i < cnt) {
-        kand &= kreg[i];
-        kor |= kreg[i];
+      if (j < len) {
+        const uint32_t u = order_key(sv[i]);
+        if constexpr (SRC != kFromScores) srow[j] = sv[i];
+        kl[j] = u;
+        kand &= u;
+        kor |= u;
       }
     }
   } else {
-    for (int i = 0; i < per; ++i) {
-      const int j = threadIdx.x + kSelThreads * i;
-      if (j >= len) break;
-      float sv = 0.f;
-      if (fx) {
-        sv = (float)((double)fx[(int64_t)req * Lctx + begin + j] * (1.0 / kScoreFixScale));
-        srow[j] = sv;
-      } else if (nparts > 0) {
-        for (int p0 = 0; p0 < nparts; p0 += 8) {
-          float v[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = prow[(int64_t)min(p0 + u, nparts - 1) * Lctx + j];
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (p0 + u < nparts) sv += v[u];
-        }
-        srow[j] = sv;
-      } else {
-        sv = srow[j];
-      }
+    clear_hist();
+    for (int j = threadIdx.x; j < len; j += kSelThreads) {
+      const float sv = score_at(j);
+      if constexpr (SRC != kFromScores) srow[j] = sv;
       const uint32_t u = order_key(sv);
       if (in_lds) kl[j] = u;
       kand &= u;
       kor |= u;
     }
   }
-  // bits shared by every key of the unit
+  // bits shared by every key of the unit (the same barrier publishes the keys in LDS)
   kand = wave_reduce(kand, [](uint32_t a, uint32_t b) { return a & b; });
   kor = wave_reduce(kor, [](uint32_t a, uint32_t b) { return a | b; });
   if (lane == 0) { sh_and[wave] = kand; sh_or[wave] = kor; }
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < NW; ++w) { kand &= sh_and[w]; kor |= sh_or[w]; }
-  // keys are read back after the barrier below (LDS, or global writes of this block)
+  if (in_regs) {
+#pragma unroll
+    for (int i = 0; i < KREG; ++i) kreg[i] = kl[min(jlo + i, len - 1)];
+  }
+  // keys of large units are read back from LDS, or re-derived from the scores written above
   auto key_at = [&](int j) -> uint32_t { return in_lds ? kl[j] : order_key(srow[j]); };
 
   if (quota > 0 && len > 0) {
@@ -171,57 +169,53 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
         mask |= 255u << shift;
       }
       for (; shift >= 0; shift -= 8) {
-        unsigned* h = &hist[shift >> 3][wave][0];
-        // each bin has kSub copies, chosen by lane: lanes of one wave that hit the same bin (the
-        // leading bytes of the scores take few values) spread over kSub addresses
-        auto count = [&](uint32_t u, bool valid) {
-          if (valid && (u & mask) == prefix) atomicAdd(&h[((u >> shift) & 255u) * kSub + (lane & (kSub - 1))], 1u);
-        };
+        uint32_t* h = hist[shift >> 3];
+        const uint32_t sub = lane & (kSelSub - 1);
         if (in_regs) {
 #pragma unroll
           for (int i = 0; i < KREG; ++i)
-            if (i < per) count(kreg[i], i < cnt);
+            if (i < cnt && (kreg[i] & mask) == prefix) atomicAdd(&h[((kreg[i] >> shift) & 255u) * kSelSub + sub], 1u);
         } else {
-          for (int i = 0; i < per; ++i) count(key_at(min(jlo + i, len - 1)), i < cnt);
+          for (int j = jlo; j < jhi; ++j) {
+            const uint32_t u = key_at(j);
+            if ((u & mask) == prefix) atomicAdd(&h[((u >> shift) & 255u) * kSelSub + sub], 1u);
+          }
         }
         __syncthreads();
-        if (threadIdx.x < 64) {
-          // one wave scans the 256 bins from the top: lane l holds bins 255-4l .. 252-4l
+        if (wave == 0) {
+          // lane l holds bins 255-4l .. 252-4l (descending): the 32 copies of bins 252-4l .. 255-4l
+          // are contiguous, eight 16-byte reads
+          const uint4* hp = reinterpret_cast<const uint4*>(h + (252 - 4 * lane) * kSelSub);
           uint32_t c[4], tot = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int bin = 255 - 4 * lane - i;
-            uint32_t cc = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w)
-#pragma unroll
-              for (int sb = 0; sb < kSub; ++sb) cc += hist[shift >> 3][w][bin * kSub + sb];
-            c[i] = cc;
-            tot += cc;
+          for (int k = 0; k < 4; ++k) {   // bin 255 - 4 lane - k
+            const uint4 a = hp[2 * (3 - k)], b = hp[2 * (3 - k) + 1];
+            c[k] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+            tot += c[k];
           }
           const uint32_t incl = wave_incl_sum(tot);
           uint32_t cum = incl - tot, before = 0;
           int found = -1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (found < 0 && cum + c[i] >= remaining) {
-              found = 255 - 4 * lane - i;
+          for (int k = 0; k < 4; ++k) {
+            if (found < 0 && cum + c[k] >= remaining) {
+              found = 255 - 4 * lane - k;
               before = cum;
             }
-            cum += c[i];
+            cum += c[k];
           }
           // the lowest lane with a hit holds the highest qualifying bin
           const int first = __ffsll((unsigned long long)__ballot(found >= 0)) - 1;
           const int bsel = __builtin_amdgcn_readlane(found, first);
           const uint32_t bef = __builtin_amdgcn_readlane(before, first);
           if (lane == 0) {
-            sh_prefix = prefix | ((uint32_t)bsel << shift);
-            sh_remaining = remaining - bef;
+            sh_sel[0] = prefix | ((uint32_t)bsel << shift);
+            sh_sel[1] = remaining - bef;
           }
         }
         __syncthreads();
-        prefix = sh_prefix;
-        remaining = sh_remaining;
+        prefix = sh_sel[0];
+        remaining = sh_sel[1];
         mask |= 255u << shift;
       }
       thr = prefix;
@@ -229,33 +223,40 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
     }
     // quota >= len: take every token
     const bool all = quota >= len;
-    int n_gt = 0, n_eq = 0;
+    uint32_t n_gt = 0, n_eq = 0;
     if (in_regs) {
 #pragma unroll
       for (int i = 0; i < KREG; ++i)
         if (i < cnt) {
-          n_gt += (all || kreg[i] > thr) ? 1 : 0;
-          n_eq += (!all && kreg[i] == thr) ? 1 : 0;
+          n_gt += (all || kreg[i] > thr) ? 1u : 0u;
+          n_eq += (!all && kreg[i] == thr) ? 1u : 0u;
         }
     } else {
       for (int j = jlo; j < jhi; ++j) {
         const uint32_t u = key_at(j);
-        n_gt += (all || u > thr) ? 1 : 0;
-        n_eq += (!all && u == thr) ? 1 : 0;
+        n_gt += (all || u > thr) ? 1u : 0u;
+        n_eq += (!all && u == thr) ? 1u : 0u;
       }
     }
-    int tot;
-    int eq_rank = block_excl_sum(n_eq, wsum, tot);
-    const int eq_take = max(0, min(n_eq, (int)need_eq - eq_rank));   // the lowest-index ties win
-    int pos = block_excl_sum(n_gt + eq_take, wsum, tot);
+    // exclusive block sums of both counts (threads in order); the ties taken before this thread
+    // are the first need_eq of them, so its first slot is gt_before + min(need_eq, eq_before)
+    const uint32_t gi = wave_incl_sum(n_gt), ei = wave_incl_sum(n_eq);
+    if (lane == 63) { wsum[0][wave] = gi; wsum[1][wave] = ei; }
+    __syncthreads();
+    uint32_t gt_before = gi - n_gt, eq_before = ei - n_eq;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) { gt_before += wsum[0][w]; eq_before += wsum[1][w]; }
+    uint32_t eq_rank = eq_before;
+    uint32_t pos = gt_before + min(need_eq, eq_before);
     auto emit = [&](uint32_t u, int j) {
       bool take = all || u > thr;
       if (!all && u == thr) {
-        take = (uint32_t)eq_rank < need_eq;
+        take = eq_rank < need_eq;
         ++eq_rank;
       }
       if (take) {
-        if (pos < quota) out[off + pos] = mrow ? mrow[begin + j] : begin + j;
+        if (pos < (uint32_t)quota) out[off + pos] = mrow ? mrow[begin + j] : begin + j;
         ++pos;
       }
     };
@@ -278,8 +279,15 @@ hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int np
                          int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
                          const int* map, int map_stride) {
   if (tab.n == 0) return hipSuccess;
-  k_select<<<dim3(tab.n), dim3(kSelThreads), 0, st>>>(tab, fx, nparts, Lctx, Lq, R, parts, scores, row_pos,
-                                                      map, map_stride);
+  const dim3 g(tab.n), b(kSelThreads);
+  if (fx)
+    k_select<kFromFixed><<<g, b, 0, st>>>(tab, fx, 0, Lctx, Lq, R, parts, scores, row_pos, map, map_stride);
+  else if (nparts > 0)
+    k_select<kFromParts><<<g, b, 0, st>>>(tab, nullptr, nparts, Lctx, Lq, R, parts, scores, row_pos, map,
+                                          map_stride);
+  else
+    k_select<kFromScores><<<g, b, 0, st>>>(tab, nullptr, 0, Lctx, Lq, R, parts, scores, row_pos, map,
+                                           map_stride);
   return hipGetLastError();
 }
 
