@@ -384,9 +384,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int req = group / a.Hkv, kvh = group % a.Hkv;
   const int nt = a.n_tiles;
   const int* cum = a.tilecum + (int64_t)req * (nt + 1);
-  const int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt];
+  // the tile's unit range and the request's total as one batch of loads
+  int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt], pieces = a.pieces;
+  asm volatile("" : "+s"(c0), "+s"(c1), "+s"(U), "+s"(pieces) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
   if (c1 <= c0) return;
-  const int P = attn_pieces_used(U, a.pieces);
+  const int P = attn_pieces_used(U, pieces);
   const int i0 = attn_piece_of(U, P, c0), i1 = attn_piece_of(U, P, c1 - 1);
   if (i0 == i1) return;  // written directly by its only piece
   const int g = a.g, Mv = a.R * g;
@@ -394,7 +396,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int v = tile * 128 + ql;
   if (v >= Mv) return;
   const int r = v / g, hq = kvh * g + v % g;
-  if (a.row_pos[(int64_t)req * a.R + r] < 0) return;
+  // the row's position is loaded with the first batch of pieces and checked at the end
+  const int pos_r = a.row_pos[(int64_t)req * a.R + r];
   // piece i0 ends in this tile: its slot is 1 unless the tile is also where it starts
   const int slot0 = attn_piece_start(U, P, i0) < c0 ? 1 : 0;
   const int n = i1 - i0 + 1;
@@ -411,6 +414,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
       ml[k] = a.part_ml[pi];
       hv[k] = *reinterpret_cast<const u32x2*>(a.part_o + pi * D + 4 * dc);
     }
+    // both halves of the batch are in flight before either is used (a piece skipped below would
+    // otherwise have its values loaded only after that test)
+    asm volatile("" ::"v"(hv[0][0]), "v"(hv[0][1]), "v"(hv[1][0]), "v"(hv[1][1]), "v"(hv[2][0]), "v"(hv[2][1]),
+                 "v"(hv[3][0]), "v"(hv[3][1]), "v"(hv[4][0]), "v"(hv[4][1]), "v"(hv[5][0]), "v"(hv[5][1]),
+                 "v"(hv[6][0]), "v"(hv[6][1]), "v"(hv[7][0]), "v"(hv[7][1]));
     f32x4 ov[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {
@@ -438,6 +446,10 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   u32x2 w;
   w[0] = pack_bf2(acc[0] * inv, acc[1] * inv);
   w[1] = pack_bf2(acc[2] * inv, acc[3] * inv);
+  // the merge is finished for every row (the asm keeps it out of the branch), and only then a row
+  // outside the cache is dropped: nothing is written for it
+  asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(M), "v"(Ls));
+  if (pos_r < 0) return;
   *reinterpret_cast<u32x2*>(a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 4 * dc) = w;
   if (dc == 0 && a.lse)
     a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;

@@ -37,9 +37,18 @@ struct SelTab {
   int writes_query[kMaxEntries];
 };
 
+// The entry owning block blk: the number of entries i >= 1 with blk0[i] <= blk (blk0 ascends),
+// counted over batches of 16 independent scalar loads at fixed offsets rather than a chain of
+// dependent ones (constant indices keep the table in the kernel arguments).
 __device__ __forceinline__ int find_entry(const ChunkTab& t, int blk) {
   int e = 0;
-  while (e + 1 < t.n && t.blk0[e + 1] <= blk) ++e;
+#pragma unroll
+  for (int b = 1; b <= kMaxEntries; b += 16) {
+    if (b >= t.n) break;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (b + k <= kMaxEntries) e += (b + k < t.n && t.blk0[b + k] <= blk) ? 1 : 0;
+  }
   return e;
 }
 

@@ -24,6 +24,8 @@
 #include "common.h"
 #include "rerotate.h"
 
+#include <algorithm>
+
 namespace sra {
 namespace {
 
@@ -45,8 +47,16 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
   __shared__ float2 cs[H];
   const int i = blockIdx.x, e = blockIdx.y;
   const int req = tab.req[e];
-  const int g = Hq / Hkv;
   const int eg = entry_base + e;
+  // every argument, fetched as one batch of scalar loads (the asm takes them all, and hands back
+  // the head counts so the division waits for it)
+  int hq = Hq, hkv = Hkv;
+  {
+    const int delta_e = tab.delta[e];
+    asm volatile("" : "+s"(hq), "+s"(hkv) : "s"(req), "s"(delta_e), "s"(qc), "s"(qrot), "s"(plane), "s"(eg),
+                 "s"(Lq), "s"(Mpad), "s"(Lctx), "s"(scale_log2), "s"(fx));
+  }
+  const int g = hq / hkv;
   const uint16_t* q = qc + ((int64_t)req * Lq + i) * Hq * D;
   const int nu = Hq * (H / 8);
   const int u0 = min((int)threadIdx.x, nu - 1);
@@ -225,16 +235,24 @@ __device__ __forceinline__ void anchor_block(int len, int64_t base, int src, int
   }
 }
 
-// grid (key blocks, Hkv). A block owns 128 keys of one chunk (staged once in LDS, rows padded for
-// conflict-free 16-byte reads); wave w owns the 32-vector query tiles w, w+4, ... with their
-// operands in registers. Every global load of a tile (K, Q and, in pass 2, the merge inputs) is
-// issued before any of them is waited on, so each block pays about one memory latency.
+// The global block range of each entry's request (the blocks whose partials pass 2 merges).
+struct EntryReqBlocks {
+  int lo[kMaxEntries];
+  int hi[kMaxEntries];
+};
+
+// grid (bmax key blocks + extra blocks, Hkv, chunk entries). A block owns 128 keys of one chunk
+// (staged once in LDS, rows padded for conflict-free 16-byte reads); wave w owns the 32-vector
+// query tiles w, w+4, ... with their operands in registers. Every global load of a tile (K, Q and,
+// in pass 2, the merge inputs) is issued before any of them is waited on, so each block pays about
+// one memory latency after one round of kernel-argument reads.
 // PASS 1 writes ml_part[blk][kvh][v] = (max, sum exp2(y - max)) over the block's keys (S^T = K Q^T:
 // one query vector per lane column, its 128 keys across the registers of both half-waves).
 // PASS 2 adds sum_v exp2(y - M_v) * invS_v of its KV head to the key's fixed-point score (S = Q K^T:
 // one key per lane column), the four waves' sums added in wave order first.
+
 template <int D, int PASS>
-__global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, int Hkv, int Mpad,
+__global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks erb, int bmax, int Hkv, int Mpad,
                                                     int Mvalid, int Lctx,
                                                     const uint16_t* __restrict__ kc,
                                                     const uint16_t* __restrict__ qrot,
@@ -248,19 +266,28 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
   constexpr int KB = 128;          // keys per block
   constexpr int KST = D + 8;       // LDS row stride (elements)
   constexpr int NKL = KB * (D / 8) / 256;
-  constexpr int MB = 16;           // merge inputs per lane per batch
+  constexpr int MB = 10;           // merge inputs per lane per batch
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KST];
   __shared__ float colred[4][KB];
   __shared__ float2 mlw[4][32];
-  const int blk = blockIdx.x, kvh = blockIdx.y;
-  if (blk >= tab.blk0[tab.n]) {
+  // grid (bmax + extra, Hkv, entries): the entry comes from the grid, so every field of it is
+  // one independent scalar load
+  const int e = blockIdx.z, kvh = blockIdx.y, x = blockIdx.x;
+  const int b0e = tab.blk0[e], nbe = tab.blk0[e + 1] - b0e;
+  {   // every argument the block's first loads depend on, fetched as one batch of scalar loads
+    const int len_e = tab.len[e], src_e = tab.src[e], req_e = tab.req[e], dst_e = tab.dst[e];
+    const int lo_e = erb.lo[e], hi_e = erb.hi[e];
+    asm volatile("" ::"s"(b0e), "s"(nbe), "s"(bmax), "s"(len_e), "s"(src_e), "s"(req_e), "s"(dst_e),
+                 "s"(lo_e), "s"(hi_e), "s"(kc), "s"(qrot), "s"(ml_part), "s"(ml_final), "s"(plane),
+                 "s"(entry_base), "s"(blk_base), "s"(Mpad), "s"(Hkv), "s"(fuse_merge), "s"(fx));
+  }
+  if (x >= bmax) {
     if constexpr (PASS == 1) {   // extra blocks: S1 for a share of kS1Fold key blocks' rows
       const int per = (KB + Hkv - 1) / Hkv;
       for (int j = 0; j < kS1Fold; ++j) {
-        const int b = (blk - tab.blk0[tab.n]) * kS1Fold + j;
-        if (b >= tab.blk0[tab.n]) break;
-        const int e = find_entry(tab, b);
-        const int tb = (b - tab.blk0[e]) * KB;
+        const int xb = (x - bmax) * kS1Fold + j;
+        if (xb >= nbe) break;
+        const int tb = xb * KB;
         const int nr = min(per, min(KB, tab.len[e] - tb) - kvh * per);
         if (nr <= 0) continue;
         if (j > 0) __syncthreads();   // the previous share's angles are retired
@@ -268,8 +295,6 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
                                  reinterpret_cast<float2*>(Ks));
       }
     } else {   // one block per chunk entry picks its anchors
-
-      const int e = blk - tab.blk0[tab.n];
       if (kvh == 0)
         anchor_block(tab.len[e], (int64_t)tab.req[e] * Lctx + tab.dst[e], tab.src[e],
                      (int64_t)tab.req[e] * anc.n_chunks + tab.aux[e], Hkv, anc,
@@ -277,15 +302,18 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
     }
     return;
   }
-  const int e = find_entry(tab, blk);
-  const int t0 = (blk - tab.blk0[e]) * KB;
+  if (x >= nbe) return;   // a shorter entry's padding
+  const int blk = b0e + x;
+  const int t0 = x * KB;
   const int req = tab.req[e];
   const int nk = min(KB, tab.len[e] - t0);   // valid keys of this block (>= 1)
+  const int rb0 = erb.lo[e], rb1 = erb.hi[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int nqt = Mpad / 32;
 
-  // K rows of the block (dims fastest, 16 bytes per load); rows past the chunk's end are zero. The
-  // loads are unconditional (clamped row, zeroed afterwards) so they all go out before any wait.
+  // Every global load of the block goes out before any of them is waited on: K rows (dims
+  // fastest, 16 bytes per load; clamped rows, zeroed on their way to LDS), the wave's first query
+  // tile and, in pass 2, that tile's first batch of merge inputs.
   u32x4 kr[NKL];
   const uint16_t* kbase = kc + (((int64_t)tab.src[e] + t0) * Hkv + kvh) * D;
 #pragma unroll
@@ -294,47 +322,72 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, ReqBlocks rb, 
     const int row = u / (D / 8);
     kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)min(row, nk - 1) * Hkv * D + 8 * (u % (D / 8)));
   }
-#pragma unroll
-  for (int i = 0; i < NKL; ++i)
-    if ((threadIdx.x + 256 * i) / (D / 8) >= nk) kr[i] = u32x4{0u, 0u, 0u, 0u};
   const uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;
   bf16x8 qh[NKS], ql[NKS];
   if (wave < nqt) load_q<NKS>(qb + (int64_t)(32 * wave + l32) * D, plane, qh, ql);
 
   // pass 2: (max, 1/sum) of query vector 32 qt + l32 over the request's blocks; the two half-waves
-  // take alternate blocks and merge in a fixed order
-  auto merged_ml = [&](int qt) -> float2 {
-    const int v = 32 * qt + l32;
-    float M = -INFINITY, S = 0.f;
-    if (fuse_merge) {
-      const int b0 = rb.blk0[req], b1 = rb.blk0[req + 1];
-      for (int b = b0 + hh; b < b1; b += 2 * MB) {
-        float2 pm[MB];
+  // take alternate blocks (batches of MB, clamped loads) and merge in a fixed order
+  auto load_batch = [&](int qt, int b, float2* pm) {
+    const int b1 = rb1;
 #pragma unroll
-        for (int u = 0; u < MB; ++u)
-          pm[u] = ml_part[((int64_t)min(b + 2 * u, b1 - 1) * Hkv + kvh) * Mpad + v];
-#pragma unroll
-        for (int u = 0; u < MB; ++u)
-          if (b + 2 * u >= b1) pm[u] = make_float2(-INFINITY, 0.f);
-#pragma unroll
-        for (int u = 0; u < MB; ++u) ml_merge(M, S, pm[u]);
-      }
-      float Mo = half_partner(M), So = half_partner(S);
-      if (hh == 1) { const float tm = M, ts = S; M = Mo; S = So; Mo = tm; So = ts; }
-      ml_merge(M, S, make_float2(Mo, So));   // half 0's blocks first, then half 1's
-      return (v < Mvalid && S > 0.f) ? make_float2(M, 1.f / S) : make_float2(0.f, 0.f);
-    }
-    return ml_final[((int64_t)req * Hkv + kvh) * Mpad + v];
+    for (int u = 0; u < MB; ++u)
+      pm[u] = ml_part[((int64_t)min(b + 2 * u, b1 - 1) * Hkv + kvh) * Mpad + 32 * qt + l32];
   };
-  float2 mlv = make_float2(0.f, 0.f);
+  auto merge_batch = [&](float& M, float& S, int b, const float2* pm) {
+    const int b1 = rb1;
+#pragma unroll
+    for (int u = 0; u < MB; ++u) ml_merge(M, S, b + 2 * u < b1 ? pm[u] : make_float2(-INFINITY, 0.f));
+  };
+  auto finish_ml = [&](float M, float S, int v) -> float2 {
+    float Mo = half_partner(M), So = half_partner(S);
+    if (hh == 1) { const float tm = M, ts = S; M = Mo; S = So; Mo = tm; So = ts; }
+    ml_merge(M, S, make_float2(Mo, So));   // half 0's blocks first, then half 1's
+    return (v < Mvalid && S > 0.f) ? make_float2(M, 1.f / S) : make_float2(0.f, 0.f);
+  };
+  auto merged_ml = [&](int qt) -> float2 {   // later query tiles
+    const int v = 32 * qt + l32;
+    if (!fuse_merge) return ml_final[((int64_t)req * Hkv + kvh) * Mpad + v];
+    float M = -INFINITY, S = 0.f;
+    for (int b = rb0 + hh; b < rb1; b += 2 * MB) {
+      float2 pm[MB];
+      load_batch(qt, b, pm);
+      merge_batch(M, S, b, pm);
+    }
+    return finish_ml(M, S, v);
+  };
+  float2 pm0[MB];   // the first tile's first batch (or its merged pair)
   if constexpr (PASS == 2) {
-    if (wave < nqt) mlv = merged_ml(wave);
+    if (wave < nqt) {
+      if (fuse_merge) load_batch(wave, rb0 + hh, pm0);
+      else pm0[0] = ml_final[((int64_t)req * Hkv + kvh) * Mpad + 32 * wave + l32];
+    }
   }
 
 #pragma unroll
   for (int i = 0; i < NKL; ++i) {
     const int u = threadIdx.x + 256 * i;
-    *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) = kr[i];
+    *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) =
+        u / (D / 8) < nk ? kr[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+  float2 mlv = make_float2(0.f, 0.f);
+  if constexpr (PASS == 2) {
+    if (wave < nqt) {   // the first tile, from the batch loaded above
+      if (fuse_merge) {
+        float M = -INFINITY, S = 0.f;
+        int b = rb0 + hh;
+        if (b < rb1) merge_batch(M, S, b, pm0);
+        for (b += 2 * MB; b < rb1; b += 2 * MB) {
+          float2 pm[MB];
+          load_batch(wave, b, pm);
+          merge_batch(M, S, b, pm);
+        }
+        mlv = finish_ml(M, S, 32 * wave + l32);
+      } else {
+        mlv = pm0[0];
+      }
+      mlw[wave][l32] = mlv;   // published before the barrier, so the merge is done before the MFMAs
+    }
   }
   __syncthreads();
   if constexpr (PASS == 1) {
@@ -455,19 +508,24 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              float2* ml_part, const float2* ml_final, int fuse_merge,
                              unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
                              hipStream_t st) {
-  const int nblk = tab.blk0[tab.n];
-  if (nblk == 0) return hipSuccess;
-  ReqBlocks rb;
-  for (int r = 0; r <= n_req; ++r) rb.blk0[r] = req_blk0[r];
-  // pass 1 may carry S1 (one extra block per key block and KV head), pass 2 the anchors (one
-  // extra block per entry)
-  const int extra = pass == 1 ? (rf.kf ? (nblk + kS1Fold - 1) / kS1Fold : 0) : (anc.k > 0 ? tab.n : 0);
-  dim3 g(nblk + extra, Hkv), b(256);
+  if (tab.n == 0 || tab.blk0[tab.n] == 0) return hipSuccess;
+  (void)n_req;
+  EntryReqBlocks erb;
+  int bmax = 0;
+  for (int i = 0; i < tab.n; ++i) {
+    erb.lo[i] = req_blk0[tab.req[i]];
+    erb.hi[i] = req_blk0[tab.req[i] + 1];
+    bmax = std::max(bmax, tab.blk0[i + 1] - tab.blk0[i]);
+  }
+  // pass 1 may carry S1 (per entry and KV head, one extra block per kS1Fold key blocks), pass 2
+  // the anchors (one extra block per entry)
+  const int extra = pass == 1 ? (rf.kf ? (bmax + kS1Fold - 1) / kS1Fold : 0) : (anc.k > 0 ? 1 : 0);
+  dim3 g(bmax + extra, Hkv, tab.n), b(256);
   const uint16_t* k = (const uint16_t*)kc;
   const Theta th = rf.kf ? make_theta(D, rf.base) : Theta{};
-#define SRA_PASS(DD, PP)                                                                        \
-  k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, rb, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,     \
-                                          entry_base, blk_base, ml_part, ml_final, fuse_merge,  \
+#define SRA_PASS(DD, PP)                                                                            \
+  k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, erb, bmax, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,  \
+                                          entry_base, blk_base, ml_part, ml_final, fuse_merge,      \
                                           fx, anc, rf, th)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);
   else if (D == 128) SRA_PASS(128, 2);

@@ -47,7 +47,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
   __shared__ uint32_t wsum[2][NW];
   const int e = blockIdx.x;
   const int req = tab.req[e], begin = tab.begin[e], len = tab.len[e];
-  const int quota = tab.quota[e], off = tab.out_off[e];
+  const int quota = tab.quota[e], off = tab.out_off[e], wq = tab.writes_query[e];
+  // every argument, fetched as one batch of scalar loads before the first global load
+  asm volatile("" ::"s"(req), "s"(begin), "s"(len), "s"(quota), "s"(off), "s"(wq), "s"(fx), "s"(parts),
+               "s"(scores), "s"(row_pos), "s"(map), "s"(map_stride), "s"(nparts), "s"(Lctx), "s"(Lq), "s"(R));
   float* srow = scores + (int64_t)req * Lctx + begin;
   int* out = row_pos + (int64_t)req * R;
   const int* mrow = map ? map + (int64_t)req * map_stride : nullptr;   // index -> written value
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
       for (int j = jlo; j < jhi; ++j) emit(key_at(j), j);
     }
   }
-  if (tab.writes_query[e]) {
+  if (wq) {
     for (int i = threadIdx.x; i < Lq; i += blockDim.x) out[R - Lq + i] = mrow ? mrow[Lctx + i] : Lctx + i;
   }
 }
