@@ -246,11 +246,11 @@ hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv
                              int Lctx, const void* qc, uint16_t* qrot, int64_t plane,
                              int entry_base, float scale_log2, unsigned long long* fx, double base,
                              hipStream_t st);
-// S1 carried by pass 1 (bfloat16 storage): the pass adds, per KV head y, one block per kS1Fold
-// key blocks that re-rotates every head of those key blocks' rows [y * ceil(128 / Hkv), ...) of
-// the stored chunk (the same rows and chunk entries as a standalone re-rotation). Pass 1 holds one
-// work group per CU, so the extra blocks are few and long enough to fit beside the scoring blocks
-// in one round. kf == NULL: none.
+// S1 carried by pass 1 (bfloat16 storage): the pass adds, per chunk entry and KV head y, one block
+// per kS1Fold key blocks that re-rotates every head of rows [y * ceil(span / Hkv), ...) of that
+// span of the stored chunk (the same rows and chunk entries as a standalone re-rotation). Pass 1
+// holds one work group per CU, so the extra blocks are few and move their share in one batch,
+// beside the scoring blocks in the same round. kf == NULL: none.
 constexpr int kS1Fold = 2;
 struct RerotFused {
   const uint16_t* ks = nullptr;

@@ -49,8 +49,10 @@ struct Vec<float> {
 // Rows [t0, t0 + nr) of chunk entry e (nr >= 1), all KV heads, by one block of 256 threads (every
 // thread must call it). Each batch loads its V chunks and K pairs (16 bytes per half) before the
 // angles are formed, so the memory latency overlaps the float64 sin/cos; V is stored as is and K
-// rotated, its bits kept when delta = 0. cs is LDS scratch of d/2 float2.
-template <typename T, int D>
+// rotated, its bits kept when delta = 0. cs is LDS scratch of d/2 float2. UV and UK are a thread's
+// V chunks and K pair units per batch: small where many blocks share a CU, large where one block
+// has a CU (more bytes in flight per round trip).
+template <typename T, int D, int UV = 4, int UK = 2>
 __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr, int Hkv,
                                      const T* __restrict__ ks, const T* __restrict__ vs,
                                      T* __restrict__ kf, T* __restrict__ vf, int64_t L,
@@ -58,7 +60,6 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
   constexpr int H = D / 2;
   constexpr int VW = Vec<T>::N;
   constexpr int UPH = H / VW;   // K pair units per head
-  constexpr int UV = 4, UK = 2; // per thread and batch: V chunks, K pair units
   const int delta = tab.delta[e];
   const int64_t row_elems = (int64_t)Hkv * D;
   const int64_t src0 = ((int64_t)tab.src[e] + t0) * row_elems;

@@ -282,18 +282,16 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
                  "s"(entry_base), "s"(blk_base), "s"(Mpad), "s"(Hkv), "s"(fuse_merge), "s"(fx));
   }
   if (x >= bmax) {
-    if constexpr (PASS == 1) {   // extra blocks: S1 for a share of kS1Fold key blocks' rows
-      const int per = (KB + Hkv - 1) / Hkv;
-      for (int j = 0; j < kS1Fold; ++j) {
-        const int xb = (x - bmax) * kS1Fold + j;
-        if (xb >= nbe) break;
-        const int tb = xb * KB;
-        const int nr = min(per, min(KB, tab.len[e] - tb) - kvh * per);
-        if (nr <= 0) continue;
-        if (j > 0) __syncthreads();   // the previous share's angles are retired
-        rerot::rows<uint16_t, D>(tab, e, tb + kvh * per, nr, Hkv, rf.ks, rf.vs, rf.kf, rf.vf, rf.L, th,
-                                 reinterpret_cast<float2*>(Ks));
-      }
+    if constexpr (PASS == 1) {   // extra blocks: S1 for a contiguous share of kS1Fold key blocks' rows
+      constexpr int SPAN = kS1Fold * KB;
+      const int per = (SPAN + Hkv - 1) / Hkv;
+      const int r0 = (x - bmax) * SPAN + kvh * per;
+      const int nr = min(min(per, SPAN - kvh * per), tab.len[e] - r0);
+      // one block per CU here: a thread's whole share of a 32-row span (bf16, d 128, 8 KV heads)
+      // is one batch of loads
+      if (nr > 0)
+        rerot::rows<uint16_t, D, 16, 8>(tab, e, r0, nr, Hkv, rf.ks, rf.vs, rf.kf, rf.vf, rf.L, th,
+                                        reinterpret_cast<float2*>(Ks));
     } else {   // one block per chunk entry picks its anchors
       if (kvh == 0)
         anchor_block(tab.len[e], (int64_t)tab.req[e] * Lctx + tab.dst[e], tab.src[e],
