@@ -2,7 +2,7 @@
 // context token indices from the critical-layer attention distribution; ties follow a stable
 // sort by descending score, Cache-Craft CSDN article §2.2.2, so the lower index wins).
 //
-// One block of 256 threads per selection unit (a whole request, or one chunk of a request when
+// One block of 1024 threads per selection unit (a whole request, or one chunk of a request when
 // per-chunk quotas are given). The block first forms the scores (fixed-point totals over KV heads,
 // or per-head float partials added in a fixed order), then finds the score of the N-th best token
 // exactly with an 8-bit radix select over order-preserving 32-bit keys (leading bytes shared by
@@ -19,7 +19,7 @@
 namespace sra {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
 constexpr int kSelLdsKeys = 12288;   // keys of one selection unit kept in LDS (48 KB)
 constexpr int kSelSub = 8;           // copies of each histogram bin, chosen by lane
 
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
                                                         int* __restrict__ row_pos,
                                                         const int* __restrict__ map, int map_stride) {
   constexpr int NW = kSelThreads / 64;
-  constexpr int KREG = 16;   // keys per thread held in registers (units up to 4096 keys)
+  constexpr int KREG = 4;    // keys per thread held in registers (units up to 4096 keys)
   // one histogram per key byte, kSelSub copies of each bin (lanes of a wave that hit the same bin,
   // common while the leading bytes take few values, spread over the copies)
   __shared__ __attribute__((aligned(16))) uint32_t hist[4][256 * kSelSub];
