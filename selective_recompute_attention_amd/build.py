@@ -21,6 +21,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          # packed fp32 ops stay off for every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # leading scalar and pointer kernel arguments arrive in SGPRs at wave launch (the code
+         # object keeps a load prologue for firmware without the feature)
+         "-mllvm", "-amdgpu-kernarg-preload-count=16",
          "-I", os.path.join(ROOT, "include")]
 
 

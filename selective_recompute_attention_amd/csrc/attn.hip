@@ -286,14 +286,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4
         // the sum takes the same bf16-rounded probabilities the products use, so the output
         // weights stay a convex combination
+        // (a bf16 pair dotted with (1, 1): one v_dot2c_f32_bf16 per pair)
+        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
         float lsum = 0.f;
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
           u32x4 pw;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            pw[k] = pack_bf2(x[8 * mp + 2 * k], x[8 * mp + 2 * k + 1]);
-            lsum += __uint_as_float(pw[k] << 16) + __uint_as_float(pw[k] & 0xffff0000u);
+            // (the pair is taken from a scalar word: a bit cast of a vector element picked the
+            // wrong element here)
+            const uint32_t pk = pack_bf2(x[8 * mp + 2 * k], x[8 * mp + 2 * k + 1]);
+            pw[k] = pk;
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, lsum, false);
           }
           const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
