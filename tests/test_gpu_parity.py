@@ -142,6 +142,12 @@ EDGE = [
                                query_len=4), ("quota", 0.6)),
     ("bf16_single_query_row", dict(dtype="bf16", n_q_heads=2, n_kv_heads=1, head_dim=128, chunk_lens=(17,),
                                    query_len=1), ("pct", 50)),
+    # re-rotation inside scoring pass 1: KV-head shares of 86 rows (256 / 3 rounded up), spans cut by
+    # the chunk's end, a one-token chunk, and five heads with a chunk just past one span
+    ("bf16_hkv3_s1_shares", dict(dtype="bf16", n_q_heads=6, n_kv_heads=3, head_dim=64, chunk_lens=(300, 129, 1),
+                                 orig_pos=(5, 0, 200), query_len=4), ("pct", 12)),
+    ("bf16_hkv5_s1_span", dict(dtype="bf16", n_q_heads=10, n_kv_heads=5, head_dim=128, chunk_lens=(257, 40),
+                               orig_pos=(0, 3), query_len=6), ("pct", 25)),
     ("f32_ragged", dict(dtype="f32", n_q_heads=6, n_kv_heads=3, head_dim=64, chunk_lens=(31, 7, 66),
                         orig_pos=(0, 2, 40), query_len=6), ("pct", 20)),
     ("f32_d128_quota", dict(dtype="f32", n_q_heads=4, n_kv_heads=1, head_dim=128, chunk_lens=(40, 40),
