@@ -353,11 +353,22 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
     std::vector<int> req_blk0(n_req + 1, 0);
     for (const Entry& en : ents) req_blk0[en.req + 1] += en.blocks;
     for (int q = 0; q < n_req; ++q) req_blk0[q + 1] += req_blk0[q];
-    e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int) {
-      return sra::launch_score_prep(D, tab, Lq, Hq, Hkv, p.Mpad, Lctx, qc, qrot, p.qrot_plane,
-                                    first, scale_log2, fx, s->rope_base, st);
-    });
-    if (e != hipSuccess) return hip_fail(e, "score prep launch");
+    // pass 1 prepares the query operand itself when each wave has one query tile and the angle
+    // table fits; otherwise the preparation kernel does
+    sra::QueryRot qr;
+    if (p.Mpad <= 128 && Lq <= sra::kInRotMaxLq) {
+      qr.qc = static_cast<const uint16_t*>(qc);
+      qr.Lq = Lq;
+      qr.Hq = Hq;
+      qr.scale_log2 = scale_log2;
+      qr.on = 1;
+    } else {
+      e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int) {
+        return sra::launch_score_prep(D, tab, Lq, Hq, Hkv, p.Mpad, Lctx, qc, qrot, p.qrot_plane,
+                                      first, scale_log2, fx, s->rope_base, st);
+      });
+      if (e != hipSuccess) return hip_fail(e, "score prep launch");
+    }
     // Pass 2 merges a request's (max, sum) partials itself when they are few; otherwise a wide
     // merge kernel runs between the passes.
     int max_blocks = 0;
@@ -372,7 +383,7 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
       e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int first, int blk_base) {
         return sra::launch_score_pass(pass, D, tab, req_blk0.data(), n_req, Hkv, p.Mpad, Lq * g, Lctx, kc,
                                       qrot, p.qrot_plane, first, blk_base, ml_part, ml_final, fuse_merge,
-                                      fx, anc, rf, st);
+                                      fx, anc, rf, qr, s->rope_base, st);
       });
       if (e != hipSuccess) return hip_fail(e, pass == 1 ? "score pass 1 launch" : "score pass 2 launch");
     }

@@ -252,6 +252,18 @@ hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv
 // holds one work group per CU, so the extra blocks are few and move their share in one batch,
 // beside the scoring blocks in the same round. kf == NULL: none.
 constexpr int kS1Fold = 2;
+// Pass 1 may prepare the query operand itself (instead of the preparation kernel) when every wave
+// has one query tile (Lq * g <= 128) and Lq <= kInRotMaxLq: it rotates the raw critical-layer
+// queries [n_req][Lq][Hq][d] with an LDS angle table and writes the operand for pass 2. on == 0:
+// the operand comes from the preparation kernel.
+constexpr int kInRotMaxLq = 64;
+struct QueryRot {
+  const uint16_t* qc = nullptr;
+  int Lq = 0;
+  int Hq = 0;
+  float scale_log2 = 0.f;
+  int on = 0;
+};
 struct RerotFused {
   const uint16_t* ks = nullptr;
   const uint16_t* vs = nullptr;
@@ -265,7 +277,7 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
                              unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
-                             hipStream_t st);
+                             const QueryRot& qr, double base, hipStream_t st);
 hipError_t launch_score_merge(const int* req_blk0, int n_req, int Hkv, int Mpad, int Mvalid,
                               const float2* ml_part, float2* ml_final, hipStream_t st);
 hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, int Hq, int Hkv,

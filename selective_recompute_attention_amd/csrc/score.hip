@@ -261,8 +261,9 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
                                                     const float2* __restrict__ ml_final,
                                                     int fuse_merge,
                                                     unsigned long long* __restrict__ fx,
-                                                    AnchorOut anc, RerotFused rf, Theta th) {
+                                                    AnchorOut anc, RerotFused rf, QueryRot qr, Theta th) {
   constexpr int NKS = D / 16;
+  constexpr int H = D / 2;
   constexpr int KB = 128;          // keys per block
   constexpr int KST = D + 8;       // LDS row stride (elements)
   constexpr int NKL = KB * (D / 8) / 256;
@@ -270,16 +271,18 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KST];
   __shared__ float colred[4][KB];
   __shared__ float2 mlw[4][32];
+  __shared__ float2 qcs[PASS == 1 ? kInRotMaxLq * H : 1];   // pass 1 with qr.on: cos/sin per (row, i)
   // grid (bmax + extra, Hkv, entries): the entry comes from the grid, so every field of it is
   // one independent scalar load
   const int e = blockIdx.z, kvh = blockIdx.y, x = blockIdx.x;
   const int b0e = tab.blk0[e], nbe = tab.blk0[e + 1] - b0e;
   {   // every argument the block's first loads depend on, fetched as one batch of scalar loads
     const int len_e = tab.len[e], src_e = tab.src[e], req_e = tab.req[e], dst_e = tab.dst[e];
-    const int lo_e = erb.lo[e], hi_e = erb.hi[e];
+    const int lo_e = erb.lo[e], hi_e = erb.hi[e], delta_e = tab.delta[e];
     asm volatile("" ::"s"(b0e), "s"(nbe), "s"(bmax), "s"(len_e), "s"(src_e), "s"(req_e), "s"(dst_e),
                  "s"(lo_e), "s"(hi_e), "s"(kc), "s"(qrot), "s"(ml_part), "s"(ml_final), "s"(plane),
-                 "s"(entry_base), "s"(blk_base), "s"(Mpad), "s"(Hkv), "s"(fuse_merge), "s"(fx));
+                 "s"(entry_base), "s"(blk_base), "s"(Mpad), "s"(Hkv), "s"(fuse_merge), "s"(fx),
+                 "s"(delta_e), "s"(qr.qc), "s"(qr.Lq), "s"(qr.Hq), "s"(qr.on));
   }
   if (x >= bmax) {
     if constexpr (PASS == 1) {   // extra blocks: S1 for a contiguous share of kS1Fold key blocks' rows
@@ -322,7 +325,21 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
   }
   const uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;
   bf16x8 qh[NKS], ql[NKS];
-  if (wave < nqt) load_q<NKS>(qb + (int64_t)(32 * wave + l32) * D, plane, qh, ql);
+  // pass 1 with qr.on (one query tile per wave): the wave's raw query vectors instead, rotated
+  // below; vector v = 32 wave + l32 is (row v / g, head kvh g + v % g), zero past Lq g
+  u32x4 qraw[NKS];
+  int qrow = 0;
+  bool qok = false;
+  if (PASS == 1 && qr.on) {
+    const int g = qr.Hq / Hkv, v = 32 * wave + l32, vc = min(v, qr.Lq * g - 1);
+    qok = v < qr.Lq * g;
+    qrow = vc / g;
+    const uint16_t* src = qr.qc + (((int64_t)req * qr.Lq + qrow) * qr.Hq + kvh * g + vc % g) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(src + 16 * ks);
+  } else if (wave < nqt) {
+    load_q<NKS>(qb + (int64_t)(32 * wave + l32) * D, plane, qh, ql);
+  }
 
   // pass 2: (max, 1/sum) of query vector 32 qt + l32 over the request's blocks; the two half-waves
   // take alternate blocks (batches of MB, clamped loads) and merge in a fixed order
@@ -362,6 +379,26 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
     }
   }
 
+  if (PASS == 1 && qr.on) {
+    // the query rows' angles (L_ctx + i - delta) theta_j: thread t takes frequency j = t % H and
+    // rows t / H, t / H + 256 / H, ...: one float64 sin/cos for its first row and one for the row
+    // step, then the rows by complex multiplication in float64, rounded to float32
+    const int j = threadIdx.x % H;
+    constexpr int RS = 256 / H;
+    const double th_j = th.v[j];
+    const double p0 = (double)Lctx + (double)(threadIdx.x / H) - (double)tab.delta[e];
+    double c, sn, cs, ss;
+    sincos(p0 * th_j, &sn, &c);
+    sincos((double)RS * th_j, &ss, &cs);
+    for (int i = threadIdx.x / H; i < qr.Lq; i += RS) {
+      qcs[i * H + j] = make_float2((float)c, (float)sn);
+      const double cn = c * cs - sn * ss;
+      sn = sn * cs + c * ss;
+      c = cn;
+    }
+    // this block clears its keys' score accumulators (pass 2 adds into them)
+    if (kvh == 0 && (int)threadIdx.x < nk) fx[(int64_t)req * Lctx + tab.dst[e] + t0 + threadIdx.x] = 0ull;
+  }
 #pragma unroll
   for (int i = 0; i < NKL; ++i) {
     const int u = threadIdx.x + 256 * i;
@@ -388,6 +425,46 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
     }
   }
   __syncthreads();
+  if (PASS == 1 && qr.on) {
+    // rotate (pairs d, d + H sit in K-steps ks and ks + NKS/2 of the same lane), fold in
+    // log2(e)/sqrt(d) and split into bf16 hi/lo, as the query preparation kernel does; the first
+    // key block of each (entry, KV head) also writes the operand for pass 2
+#pragma unroll
+    for (int ks = 0; ks < NKS / 2; ++ks) {
+      u32x4 ha, hb, la, lb;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t hw[2][2], lw[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float a = bf2f((qraw[ks][k] >> (16 * t)) & 0xffffu);
+          const float b = bf2f((qraw[ks + NKS / 2][k] >> (16 * t)) & 0xffffu);
+          const float2 cw = qcs[qrow * H + 16 * ks + 8 * hh + 2 * k + t];
+          const float r0 = (a * cw.x - b * cw.y) * qr.scale_log2, r1 = (a * cw.y + b * cw.x) * qr.scale_log2;
+          hw[0][t] = f2bf(r0);
+          hw[1][t] = f2bf(r1);
+          lw[0][t] = f2bf(r0 - bf2f(hw[0][t]));
+          lw[1][t] = f2bf(r1 - bf2f(hw[1][t]));
+        }
+        ha[k] = qok ? hw[0][0] | (hw[0][1] << 16) : 0u;
+        hb[k] = qok ? hw[1][0] | (hw[1][1] << 16) : 0u;
+        la[k] = qok ? lw[0][0] | (lw[0][1] << 16) : 0u;
+        lb[k] = qok ? lw[1][0] | (lw[1][1] << 16) : 0u;
+      }
+      qh[ks] = as_bf16x8(ha);
+      qh[ks + NKS / 2] = as_bf16x8(hb);
+      ql[ks] = as_bf16x8(la);
+      ql[ks + NKS / 2] = as_bf16x8(lb);
+    }
+    if (x == 0 && wave < nqt) {
+      uint16_t* qo = const_cast<uint16_t*>(qb) + (int64_t)(32 * wave + l32) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        *reinterpret_cast<u32x4*>(qo + 16 * ks) = __builtin_bit_cast(u32x4, qh[ks]);
+        *reinterpret_cast<u32x4*>(qo + plane + 16 * ks) = __builtin_bit_cast(u32x4, ql[ks]);
+      }
+    }
+  }
   if constexpr (PASS == 1) {
     if (anc.k > 0 && (int)threadIdx.x < nk) {   // this KV head's share of the key norms
       const uint32_t* row = reinterpret_cast<const uint32_t*>(Ks + threadIdx.x * KST);
@@ -505,7 +582,7 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
                              const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
                              unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
-                             hipStream_t st) {
+                             const QueryRot& qr, double base, hipStream_t st) {
   if (tab.n == 0 || tab.blk0[tab.n] == 0) return hipSuccess;
   (void)n_req;
   EntryReqBlocks erb;
@@ -520,11 +597,11 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
   const int extra = pass == 1 ? (rf.kf ? (bmax + kS1Fold - 1) / kS1Fold : 0) : (anc.k > 0 ? 1 : 0);
   dim3 g(bmax + extra, Hkv, tab.n), b(256);
   const uint16_t* k = (const uint16_t*)kc;
-  const Theta th = rf.kf ? make_theta(D, rf.base) : Theta{};
+  const Theta th = make_theta(D, base);
 #define SRA_PASS(DD, PP)                                                                            \
   k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, erb, bmax, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,  \
                                           entry_base, blk_base, ml_part, ml_final, fuse_merge,      \
-                                          fx, anc, rf, th)
+                                          fx, anc, rf, pass == 1 ? qr : QueryRot{}, th)
   if (D == 128 && pass == 1) SRA_PASS(128, 1);
   else if (D == 128) SRA_PASS(128, 2);
   else if (pass == 1) SRA_PASS(64, 1);
