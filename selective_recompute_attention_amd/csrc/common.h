@@ -274,7 +274,7 @@ struct RerotFused {
 };
 hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
-                             const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
+                             uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
                              unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
                              const QueryRot& qr, double base, hipStream_t st);

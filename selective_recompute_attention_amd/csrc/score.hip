@@ -255,7 +255,7 @@ template <int D, int PASS>
 __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks erb, int bmax, int Hkv, int Mpad,
                                                     int Mvalid, int Lctx,
                                                     const uint16_t* __restrict__ kc,
-                                                    const uint16_t* __restrict__ qrot,
+                                                    uint16_t* __restrict__ qrot,
                                                     int64_t plane, int entry_base, int blk_base,
                                                     float2* __restrict__ ml_part,
                                                     const float2* __restrict__ ml_final,
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
     const int row = u / (D / 8);
     kr[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)min(row, nk - 1) * Hkv * D + 8 * (u % (D / 8)));
   }
-  const uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;
+  uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;   // pass 1 may write it
   bf16x8 qh[NKS], ql[NKS];
   // pass 1 with qr.on (one query tile per wave): the wave's raw query vectors instead, rotated
   // below; vector v = 32 wave + l32 is (row v / g, head kvh g + v % g), zero past Lq g
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
       ql[ks + NKS / 2] = as_bf16x8(lb);
     }
     if (x == 0 && wave < nqt) {
-      uint16_t* qo = const_cast<uint16_t*>(qb) + (int64_t)(32 * wave + l32) * D;
+      uint16_t* qo = qb + (int64_t)(32 * wave + l32) * D;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         *reinterpret_cast<u32x4*>(qo + 16 * ks) = __builtin_bit_cast(u32x4, qh[ks]);
@@ -579,7 +579,7 @@ hipError_t launch_score_prep(int D, const ChunkTab& tab, int Lq, int Hq, int Hkv
 
 hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
-                             const uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
+                             uint16_t* qrot, int64_t plane, int entry_base, int blk_base,
                              float2* ml_part, const float2* ml_final, int fuse_merge,
                              unsigned long long* fx, const AnchorOut& anc, const RerotFused& rf,
                              const QueryRot& qr, double base, hipStream_t st) {
