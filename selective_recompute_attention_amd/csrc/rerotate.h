@@ -5,6 +5,8 @@
 // page, §2.4): a chunk cached at original positions orig + t moves to fused rows n_c + t, so each
 // key pair (x_i, x_{i+d/2}) turns by delta_c * theta_i with delta_c = n_c - orig.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace sra {
@@ -60,6 +62,7 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
   constexpr int H = D / 2;
   constexpr int VW = Vec<T>::N;
   constexpr int UPH = H / VW;   // K pair units per head
+  static_assert(H <= 256, "one frequency per thread");
   const int delta = tab.delta[e];
   const int64_t row_elems = (int64_t)Hkv * D;
   const int64_t src0 = ((int64_t)tab.src[e] + t0) * row_elems;
@@ -68,8 +71,13 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
   const int64_t nK = (int64_t)nr * Hkv * UPH;                             // K pair units
   const v4u* vsrc = reinterpret_cast<const v4u*>(vs + src0);
   v4u* vdst = reinterpret_cast<v4u*>(vf + dst0);
-  bool first = true;
-  for (int64_t bv = 0, bk = 0; bv < nV || bk < nK; bv += 256 * UV, bk += 256 * UK) {
+  // the thread's frequency (indexed, so a memory load) goes out before the data: loads complete in
+  // order, so one issued after them would hold the angles back until all the data has arrived
+  const double th_i = th.v[min((int)threadIdx.x, H - 1)];
+  __builtin_amdgcn_sched_barrier(0);   // keep it ahead of the data loads
+  // one batch: its loads, then (first batch only) the angles while they are in flight, then the
+  // stores
+  auto batch = [&](int64_t bv, int64_t bk, auto first_tag) {
     v4u v[UV], ka[UK], kb[UK];
 #pragma unroll
     for (int i = 0; i < UV; ++i) v[i] = vsrc[min(bv + threadIdx.x + 256 * i, nV - 1)];
@@ -80,11 +88,12 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
       ka[i] = *reinterpret_cast<const v4u*>(a);
       kb[i] = *reinterpret_cast<const v4u*>(a + H);
     }
-    if (first) {   // uniform: the angles once per block, while the loads are in flight
-      if (delta != 0)
-        for (int i = threadIdx.x; i < H; i += 256) cs[i] = rope_cs((double)delta, th.v[i]);
+    if constexpr (decltype(first_tag)::value) {
+      // every thread forms an angle and stores it (threads past d/2 repeat the last frequency
+      // with the same value), so nothing here sits behind a branch that the compiler could move
+      // the frequency load into
+      cs[min((int)threadIdx.x, H - 1)] = rope_cs((double)delta, th_i);
       __syncthreads();
-      first = false;
     }
 #pragma unroll
     for (int i = 0; i < UV; ++i)
@@ -112,7 +121,10 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
         *reinterpret_cast<v4u*>(o + H) = Vec<T>::pack(rb);
       }
     }
-  }
+  };
+  batch(0, 0, std::true_type{});   // nr >= 1: the first batch has work
+  for (int64_t bv = 256 * UV, bk = 256 * UK; bv < nV || bk < nK; bv += 256 * UV, bk += 256 * UK)
+    batch(bv, bk, std::false_type{});
 }
 
 }  // namespace rerot

@@ -114,11 +114,13 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
   }
 }
 
-// Online merge of one (max, sum of exp2(y - max)) pair into a running pair.
+// Online merge of one (max, sum of exp2(y - max)) pair into a running pair. Branch-free: an empty
+// pair (-inf, 0) scales the running sum by exp2(0) = 1 and adds 0, so it leaves the pair's bits as
+// they are; when both maxima are -inf the shift is 0 and the sum stays 0.
 __device__ __forceinline__ void ml_merge(float& M, float& S, float2 p) {
-  if (p.x == -INFINITY) return;
   const float nm = fmaxf(M, p.x);
-  S = S * exp2f(M - nm) + p.y * exp2f(p.x - nm);
+  const float sh = nm == -INFINITY ? 0.f : nm;
+  S = S * exp2f(M - sh) + p.y * exp2f(p.x - sh);
   M = nm;
 }
 
@@ -185,49 +187,74 @@ __device__ __forceinline__ void load_q(const uint16_t* qp, int64_t plane, bf16x8
 // Anchors of chunk entry e (one block): the key-norm totals (per-head sums added in head order) go
 // to LDS, then wave 0 takes k rounds, each picking the best token ranked after the previous pick
 // (larger sum first, lower offset on a tie; float64 sums of squares order like their bit patterns).
+// Chunks of up to 512 tokens keep a lane's totals in registers across the rounds; a round's wave
+// reduction carries (total, offset) only, "nothing found" being (0, INT_MAX), which any token beats
+// (totals are sums of squares, so never below +0).
 // (Scalar arguments only: a reference to the kernel-argument table would copy it to scratch.)
 __device__ __forceinline__ void anchor_block(int len, int64_t base, int src, int64_t out_slot, int Hkv,
                                              const AnchorOut& anc, unsigned long long* tot) {
-  // len <= kAnchorFusedMaxLen (checked by the host); base = the chunk's first context position
-  for (int t = threadIdx.x; t < len; t += blockDim.x) {
-    double sum = 0.0;
+  // len <= kAnchorFusedMaxLen (checked by the host); base = the chunk's first context position.
+  // Two tokens per thread per step, every head's load of both issued before any is added.
+  for (int t0 = threadIdx.x; t0 < len; t0 += 2 * blockDim.x) {
+    const int t1 = t0 + blockDim.x, t1c = min(t1, len - 1);
+    double s0 = 0.0, s1 = 0.0;
     for (int h0 = 0; h0 < Hkv; h0 += 8) {
-      double v[8];   // eight heads' loads at once, added in head order
+      double v0[8], v1[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = anc.ssp[(int64_t)min(h0 + u, Hkv - 1) * anc.stride + base + t];
+      for (int u = 0; u < 8; ++u) {
+        const double* row = anc.ssp + (int64_t)min(h0 + u, Hkv - 1) * anc.stride + base;
+        v0[u] = row[t0];
+        v1[u] = row[t1c];
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (h0 + u < Hkv) sum += v[u];
+        if (h0 + u < Hkv) {
+          s0 += v0[u];
+          s1 += v1[u];
+        }
     }
-    tot[t] = __double_as_longlong(sum);
-    if (anc.norms) anc.norms[(int64_t)src + t] = (float)sqrt(sum);
+    tot[t0] = __double_as_longlong(s0);
+    if (anc.norms) anc.norms[(int64_t)src + t0] = (float)sqrt(s0);
+    if (t1 < len) {
+      tot[t1] = __double_as_longlong(s1);
+      if (anc.norms) anc.norms[(int64_t)src + t1] = (float)sqrt(s1);
+    }
   }
   __syncthreads();
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
+  constexpr int RJ = 8;   // register-held totals per lane
+  const bool in_reg = len <= 64 * RJ;
+  unsigned long long rv[RJ];
+  if (in_reg) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) rv[j] = tot[min(lane + 64 * j, len - 1)];
+  }
   unsigned long long pv = ~0ull;   // previous pick (value, offset); starts above everything
   int pt = -1;
   for (int round = 0; round < anc.k; ++round) {
-    bool have = false;
     unsigned long long bv = 0;
     int bt = INT_MAX;
-    for (int t = lane; t < len; t += 64) {
-      const unsigned long long v = tot[t];
+    auto consider = [&](unsigned long long v, int t) {
       const bool after = v < pv || (v == pv && t > pt);
-      const bool better = after && (!have || v > bv || (v == bv && t < bt));
+      const bool better = after && (v > bv || (v == bv && t < bt));
       bv = better ? v : bv;
       bt = better ? t : bt;
-      have = have || better;
+    };
+    if (in_reg) {
+#pragma unroll
+      for (int j = 0; j < RJ; ++j)
+        if (lane + 64 * j < len) consider(rv[j], lane + 64 * j);
+    } else {
+      for (int t = lane; t < len; t += 64) consider(tot[t], t);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const unsigned long long ov = __shfl_xor(bv, off, 64);
       const int ot = __shfl_xor(bt, off, 64);
-      const bool oh = __shfl_xor((int)have, off, 64) != 0;
-      const bool better = oh && (!have || ov > bv || (ov == bv && ot < bt));
+      const bool better = ov > bv || (ov == bv && ot < bt);
       bv = better ? ov : bv;
       bt = better ? ot : bt;
-      have = have || oh;
     }
     if (lane == 0) anc.rows[out_slot * anc.k + round] = bt;
     pv = bv;
@@ -250,8 +277,11 @@ struct EntryReqBlocks {
 // one query vector per lane column, its 128 keys across the registers of both half-waves).
 // PASS 2 adds sum_v exp2(y - M_v) * invS_v of its KV head to the key's fixed-point score (S = Q K^T:
 // one key per lane column), the four waves' sums added in wave order first.
+// OWN: the pass forms its own inputs. Pass 1 rotates, scales and splits the raw query itself (and
+// writes the operand for pass 2); otherwise it reads the operand that the preparation kernel wrote.
+// Pass 2 merges the request's block partials itself; otherwise it reads the merged pairs.
 
-template <int D, int PASS>
+template <int D, int PASS, bool OWN>
 __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks erb, int bmax, int Hkv, int Mpad,
                                                     int Mvalid, int Lctx,
                                                     const uint16_t* __restrict__ kc,
@@ -259,7 +289,6 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
                                                     int64_t plane, int entry_base, int blk_base,
                                                     float2* __restrict__ ml_part,
                                                     const float2* __restrict__ ml_final,
-                                                    int fuse_merge,
                                                     unsigned long long* __restrict__ fx,
                                                     AnchorOut anc, RerotFused rf, QueryRot qr, Theta th) {
   constexpr int NKS = D / 16;
@@ -271,7 +300,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KB * KST];
   __shared__ float colred[4][KB];
   __shared__ float2 mlw[4][32];
-  __shared__ float2 qcs[PASS == 1 ? kInRotMaxLq * H : 1];   // pass 1 with qr.on: cos/sin per (row, i)
+  __shared__ float2 qcs[PASS == 1 && OWN ? kInRotMaxLq * H : 1];   // cos/sin per (query row, i)
   // grid (bmax + extra, Hkv, entries): the entry comes from the grid, so every field of it is
   // one independent scalar load
   const int e = blockIdx.z, kvh = blockIdx.y, x = blockIdx.x;
@@ -281,8 +310,8 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
     const int lo_e = erb.lo[e], hi_e = erb.hi[e], delta_e = tab.delta[e];
     asm volatile("" ::"s"(b0e), "s"(nbe), "s"(bmax), "s"(len_e), "s"(src_e), "s"(req_e), "s"(dst_e),
                  "s"(lo_e), "s"(hi_e), "s"(kc), "s"(qrot), "s"(ml_part), "s"(ml_final), "s"(plane),
-                 "s"(entry_base), "s"(blk_base), "s"(Mpad), "s"(Hkv), "s"(fuse_merge), "s"(fx),
-                 "s"(delta_e), "s"(qr.qc), "s"(qr.Lq), "s"(qr.Hq), "s"(qr.on));
+                 "s"(entry_base), "s"(blk_base), "s"(Mpad), "s"(Hkv), "s"(fx),
+                 "s"(delta_e), "s"(qr.qc), "s"(qr.Lq), "s"(qr.Hq));
   }
   if (x >= bmax) {
     if constexpr (PASS == 1) {   // extra blocks: S1 for a contiguous share of kS1Fold key blocks' rows
@@ -311,10 +340,17 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
   const int rb0 = erb.lo[e], rb1 = erb.hi[e];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
   const int nqt = Mpad / 32;
+  const int v0 = min(32 * wave + l32, Mpad - 1);   // the wave's first query vector, clamped
 
   // Every global load of the block goes out before any of them is waited on: K rows (dims
   // fastest, 16 bytes per load; clamped rows, zeroed on their way to LDS), the wave's first query
-  // tile and, in pass 2, that tile's first batch of merge inputs.
+  // tile and, in pass 2, that tile's first batch of merge inputs. Pass 1's query angles need one
+  // frequency per thread (an indexed load): it goes first, as loads complete in order.
+  double th_j = 0.0;
+  if constexpr (PASS == 1 && OWN) {
+    th_j = th.v[threadIdx.x % H];
+    __builtin_amdgcn_sched_barrier(0);   // keep it ahead of the data loads
+  }
   u32x4 kr[NKL];
   const uint16_t* kbase = kc + (((int64_t)tab.src[e] + t0) * Hkv + kvh) * D;
 #pragma unroll
@@ -325,29 +361,30 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
   }
   uint16_t* qb = qrot + (int64_t)((entry_base + e) * Hkv + kvh) * Mpad * D + 8 * hh;   // pass 1 may write it
   bf16x8 qh[NKS], ql[NKS];
-  // pass 1 with qr.on (one query tile per wave): the wave's raw query vectors instead, rotated
+  // pass 1 with OWN (one query tile per wave): the wave's raw query vectors instead, rotated
   // below; vector v = 32 wave + l32 is (row v / g, head kvh g + v % g), zero past Lq g
   u32x4 qraw[NKS];
   int qrow = 0;
   bool qok = false;
-  if (PASS == 1 && qr.on) {
+  if constexpr (PASS == 1 && OWN) {
     const int g = qr.Hq / Hkv, v = 32 * wave + l32, vc = min(v, qr.Lq * g - 1);
     qok = v < qr.Lq * g;
     qrow = vc / g;
     const uint16_t* src = qr.qc + (((int64_t)req * qr.Lq + qrow) * qr.Hq + kvh * g + vc % g) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(src + 16 * ks);
-  } else if (wave < nqt) {
-    load_q<NKS>(qb + (int64_t)(32 * wave + l32) * D, plane, qh, ql);
+  } else {   // unconditional (a wave past the last tile loads a valid vector it never uses), so no
+             // value merges across a branch and forces a wait in the middle of the batch
+    load_q<NKS>(qb + (int64_t)v0 * D, plane, qh, ql);
   }
 
   // pass 2: (max, 1/sum) of query vector 32 qt + l32 over the request's blocks; the two half-waves
   // take alternate blocks (batches of MB, clamped loads) and merge in a fixed order
-  auto load_batch = [&](int qt, int b, float2* pm) {
+  auto load_batch = [&](int v, int b, float2* pm) {
     const int b1 = rb1;
 #pragma unroll
     for (int u = 0; u < MB; ++u)
-      pm[u] = ml_part[((int64_t)min(b + 2 * u, b1 - 1) * Hkv + kvh) * Mpad + 32 * qt + l32];
+      pm[u] = ml_part[((int64_t)min(b + 2 * u, b1 - 1) * Hkv + kvh) * Mpad + v];
   };
   auto merge_batch = [&](float& M, float& S, int b, const float2* pm) {
     const int b1 = rb1;
@@ -362,39 +399,41 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
   };
   auto merged_ml = [&](int qt) -> float2 {   // later query tiles
     const int v = 32 * qt + l32;
-    if (!fuse_merge) return ml_final[((int64_t)req * Hkv + kvh) * Mpad + v];
+    if (!OWN) return ml_final[((int64_t)req * Hkv + kvh) * Mpad + v];
     float M = -INFINITY, S = 0.f;
     for (int b = rb0 + hh; b < rb1; b += 2 * MB) {
       float2 pm[MB];
-      load_batch(qt, b, pm);
+      load_batch(v, b, pm);
       merge_batch(M, S, b, pm);
     }
     return finish_ml(M, S, v);
   };
   float2 pm0[MB];   // the first tile's first batch (or its merged pair)
-  if constexpr (PASS == 2) {
-    if (wave < nqt) {
-      if (fuse_merge) load_batch(wave, rb0 + hh, pm0);
-      else pm0[0] = ml_final[((int64_t)req * Hkv + kvh) * Mpad + 32 * wave + l32];
-    }
+  if constexpr (PASS == 2) {   // unconditional too, from the clamped vector
+    if constexpr (OWN) load_batch(v0, rb0 + hh, pm0);
+    else pm0[0] = ml_final[((int64_t)req * Hkv + kvh) * Mpad + v0];
   }
 
-  if (PASS == 1 && qr.on) {
+  if constexpr (PASS == 1 && OWN) {
     // the query rows' angles (L_ctx + i - delta) theta_j: thread t takes frequency j = t % H and
     // rows t / H, t / H + 256 / H, ...: one float64 sin/cos for its first row and one for the row
-    // step, then the rows by complex multiplication in float64, rounded to float32
+    // step, then the rows by complex multiplication in float64, rounded to float32. The first row
+    // is stored by every thread (row t / H < 256 / H is inside the table; one past L_q is never
+    // read), so the frequency load, issued first, is used in straight-line code and the sin/cos
+    // overlaps the data loads' latency.
     const int j = threadIdx.x % H;
     constexpr int RS = 256 / H;
-    const double th_j = th.v[j];
+    static_assert(RS <= kInRotMaxLq, "first rows inside the angle table");
     const double p0 = (double)Lctx + (double)(threadIdx.x / H) - (double)tab.delta[e];
     double c, sn, cs, ss;
     sincos(p0 * th_j, &sn, &c);
     sincos((double)RS * th_j, &ss, &cs);
-    for (int i = threadIdx.x / H; i < qr.Lq; i += RS) {
-      qcs[i * H + j] = make_float2((float)c, (float)sn);
+    qcs[threadIdx.x] = make_float2((float)c, (float)sn);
+    for (int i = threadIdx.x / H + RS; i < qr.Lq; i += RS) {
       const double cn = c * cs - sn * ss;
       sn = sn * cs + c * ss;
       c = cn;
+      qcs[i * H + j] = make_float2((float)c, (float)sn);
     }
     // this block clears its keys' score accumulators (pass 2 adds into them)
     if (kvh == 0 && (int)threadIdx.x < nk) fx[(int64_t)req * Lctx + tab.dst[e] + t0 + threadIdx.x] = 0ull;
@@ -402,30 +441,31 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
 #pragma unroll
   for (int i = 0; i < NKL; ++i) {
     const int u = threadIdx.x + 256 * i;
-    *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) =
-        u / (D / 8) < nk ? kr[i] : u32x4{0u, 0u, 0u, 0u};
+    // masked rather than selected: a select lets the compiler move the row's load behind a branch
+    const uint32_t m = u / (D / 8) < nk ? ~0u : 0u;
+    *reinterpret_cast<u32x4*>(Ks + (u / (D / 8)) * KST + 8 * (u % (D / 8))) = kr[i] & m;
   }
   float2 mlv = make_float2(0.f, 0.f);
   if constexpr (PASS == 2) {
-    if (wave < nqt) {   // the first tile, from the batch loaded above
-      if (fuse_merge) {
-        float M = -INFINITY, S = 0.f;
-        int b = rb0 + hh;
-        if (b < rb1) merge_batch(M, S, b, pm0);
-        for (b += 2 * MB; b < rb1; b += 2 * MB) {
-          float2 pm[MB];
-          load_batch(wave, b, pm);
-          merge_batch(M, S, b, pm);
-        }
-        mlv = finish_ml(M, S, 32 * wave + l32);
-      } else {
-        mlv = pm0[0];
+    // the first tile, from the batch loaded above: every wave merges it in straight-line code
+    // beside the loads (a use behind a branch lets the compiler sink the loads after the waits)
+    if constexpr (OWN) {
+      float M = -INFINITY, S = 0.f;
+      int b = rb0 + hh;
+      merge_batch(M, S, b, pm0);
+      for (b += 2 * MB; b < rb1; b += 2 * MB) {
+        float2 pm[MB];
+        load_batch(v0, b, pm);
+        merge_batch(M, S, b, pm);
       }
-      mlw[wave][l32] = mlv;   // published before the barrier, so the merge is done before the MFMAs
+      mlv = finish_ml(M, S, 32 * wave + l32);
+    } else {
+      mlv = pm0[0];
     }
+    if (wave < nqt) mlw[wave][l32] = mlv;   // before the barrier: the merge is done before the MFMAs
   }
   __syncthreads();
-  if (PASS == 1 && qr.on) {
+  if constexpr (PASS == 1 && OWN) {
     // rotate (pairs d, d + H sit in K-steps ks and ks + NKS/2 of the same lane), fold in
     // log2(e)/sqrt(d) and split into bf16 hi/lo, as the query preparation kernel does; the first
     // key block of each (entry, KV head) also writes the operand for pass 2
@@ -598,14 +638,20 @@ hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* re
   dim3 g(bmax + extra, Hkv, tab.n), b(256);
   const uint16_t* k = (const uint16_t*)kc;
   const Theta th = make_theta(D, base);
-#define SRA_PASS(DD, PP)                                                                            \
-  k_score_pass<DD, PP><<<g, b, 0, st>>>(tab, erb, bmax, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane,  \
-                                          entry_base, blk_base, ml_part, ml_final, fuse_merge,      \
-                                          fx, anc, rf, pass == 1 ? qr : QueryRot{}, th)
-  if (D == 128 && pass == 1) SRA_PASS(128, 1);
-  else if (D == 128) SRA_PASS(128, 2);
-  else if (pass == 1) SRA_PASS(64, 1);
-  else SRA_PASS(64, 2);
+#define SRA_PASS(DD, PP, FF)                                                                        \
+  k_score_pass<DD, PP, FF><<<g, b, 0, st>>>(tab, erb, bmax, Hkv, Mpad, Mvalid, Lctx, k, qrot, plane, \
+                                              entry_base, blk_base, ml_part, ml_final, fx, anc, rf,  \
+                                              pass == 1 ? qr : QueryRot{}, th)
+  // pass 1 forms its own operand when qr.on, pass 2 merges its own partials when fuse_merge
+  const bool own = pass == 1 ? qr.on != 0 : fuse_merge != 0;
+  if (D == 128 && pass == 1 && own) SRA_PASS(128, 1, true);
+  else if (D == 128 && pass == 1) SRA_PASS(128, 1, false);
+  else if (D == 128 && own) SRA_PASS(128, 2, true);
+  else if (D == 128) SRA_PASS(128, 2, false);
+  else if (pass == 1 && own) SRA_PASS(64, 1, true);
+  else if (pass == 1) SRA_PASS(64, 1, false);
+  else if (own) SRA_PASS(64, 2, true);
+  else SRA_PASS(64, 2, false);
 #undef SRA_PASS
   return hipGetLastError();
 }

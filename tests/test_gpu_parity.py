@@ -288,6 +288,10 @@ FUSED_ANCHOR_CASES = {
     "two_requests_ragged_bf16": (lambda: make_custom(dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128,
                                                      chunk_lens=(200, 37, 301), orig_pos=(0, 5, 0), query_len=7,
                                                      n_req=2, seed=11), 6),
+    # chunks past 512 tokens: the selection rounds read the totals from LDS instead of registers
+    "chunks_past_register_bf16": (lambda: make_custom(dtype="bf16", n_q_heads=8, n_kv_heads=4, head_dim=64,
+                                                      chunk_lens=(1000, 513, 64), orig_pos=(0, 0, 9), query_len=4,
+                                                      seed=13), 7),
     "chunk_longer_than_lds_bf16": (lambda: make_custom(dtype="bf16", n_q_heads=2, n_kv_heads=1, head_dim=64,
                                                        chunk_lens=(4500, 100), query_len=3, seed=12), 5),
 }
