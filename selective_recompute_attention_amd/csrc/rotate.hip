@@ -35,7 +35,9 @@ __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int row
 // by log2(e)/sqrt(d) and split into bf16 hi/lo planes in the matrix-operand order of qop_index.
 // Fresh rows are compact (row r) or position-indexed (row p). Rows outside [0, L) write nothing
 // but zero query operands. The first batch of every part is loaded before the angles are formed.
-template <typename T, int D>
+// FULL: kn and qop are both set (bf16), so every first-batch load is unconditional and the
+// angles wait on the frequency load alone.
+template <typename T, int D, bool FULL>
 __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
                                                  const T* __restrict__ qn, const T* __restrict__ kn,
                                                  const T* __restrict__ vn, int fresh_rows,
@@ -57,10 +59,15 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
   const int64_t src0 = ((int64_t)q * fresh_rows + srow) * row_elems;
   const int64_t dst0 = ((int64_t)q * L + (valid ? p : 0)) * row_elems;
   const int nV = (int)(row_elems * (int64_t)sizeof(T) / 16), nK = Hkv * UPH;
-  const bool do_kv = valid && kn;
+  const bool do_kv = valid && (FULL || kn);
+  // the thread's frequency (an indexed load) goes out before the row's data: loads complete in
+  // order, so one issued after them would hold the angles back until all the data has arrived
+  static_assert(H <= NT, "one frequency per thread");
+  const double th_i = th.v[min((int)threadIdx.x, H - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   // first batch: V chunks tid, tid+128; K pair tid; query units tid, tid+128
   u32x4 v0 = {}, v1 = {}, ka = {}, kb = {};
-  if (kn) {
+  if (FULL || kn) {
     const u32x4* vsrc = reinterpret_cast<const u32x4*>(vn + src0);
     v0 = vsrc[min((int)threadIdx.x, nV - 1)];
     v1 = vsrc[min((int)threadIdx.x + NT, nV - 1)];
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
   auto qsrc = [&](int u) { return qn + (((int64_t)q * fresh_rows + srow) * Hq + u / NKS) * D + 16 * ((u % NKS) >> 1) + 8 * (u & 1); };
   u32x4 qx[2] = {}, qy[2] = {};
   if constexpr (sizeof(T) == 2) {
-    if (qop) {
+    if (FULL || qop) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const T* src = qsrc(min((int)threadIdx.x + NT * k, nQ - 1));
@@ -83,12 +90,12 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
       }
     }
   }
-  if (valid) {
-    for (int i = threadIdx.x; i < H; i += NT) {
-      const float2 c = rope_cs((double)p, th.v[i]);
-      cs[i] = c;
-      if (cs_out) cs_out[((int64_t)q * R + r) * H + i] = c;
-    }
+  {   // every thread forms an angle and stores it (threads past d/2 repeat the last frequency with
+      // the same value; an invalid row's angles are never used), so the frequency load stays in
+      // straight-line code and the float64 sin/cos overlaps the data loads
+    const float2 c = rope_cs((double)(valid ? p : 0), th_i);
+    cs[min((int)threadIdx.x, H - 1)] = c;
+    if (valid && cs_out && (int)threadIdx.x < H) cs_out[((int64_t)q * R + r) * H + threadIdx.x] = c;
   }
   __syncthreads();
 
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
     }
   }
   if constexpr (sizeof(T) == 2) {
-    if (qop) {
+    if (FULL || qop) {
       auto q_store = [&](int u, u32x4 wx, u32x4 wy) {
         const int h = u / NKS, ks = (u % NKS) >> 1, hh = u & 1;
         const int d0 = 16 * ks + 8 * hh;
@@ -370,24 +377,18 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(128);
   const Theta th = make_theta(D, base);
-  if (dtype == 0 && D == 128)
-    k_scatter<uint16_t, 128><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const uint16_t*)qn, (const uint16_t*)kn,
-                                               (const uint16_t*)vn, fresh_rows, indexed, row_pos,
-                                               (uint16_t*)kf, (uint16_t*)vf, cs_out, qop, qop_blocks,
-                                               scale_log2, th);
-  else if (dtype == 0 && D == 64)
-    k_scatter<uint16_t, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const uint16_t*)qn, (const uint16_t*)kn,
-                                              (const uint16_t*)vn, fresh_rows, indexed, row_pos,
-                                              (uint16_t*)kf, (uint16_t*)vf, cs_out, qop, qop_blocks,
-                                              scale_log2, th);
-  else if (dtype == 1 && D == 128)
-    k_scatter<float, 128><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
-                                            (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
-                                            (float*)vf, cs_out, nullptr, 0, scale_log2, th);
-  else
-    k_scatter<float, 64><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const float*)qn, (const float*)kn,
-                                           (const float*)vn, fresh_rows, indexed, row_pos, (float*)kf,
-                                           (float*)vf, cs_out, nullptr, 0, scale_log2, th);
+#define SRA_SCATTER(TT, DD, FF)                                                                         \
+  k_scatter<TT, DD, FF><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const TT*)qn, (const TT*)kn, (const TT*)vn,       \
+                                         fresh_rows, indexed, row_pos, (TT*)kf, (TT*)vf, cs_out,         \
+                                         dtype == 0 ? qop : nullptr, qop_blocks, scale_log2, th)
+  const bool full = dtype == 0 && kn && qop;
+  if (dtype == 0 && D == 128 && full) SRA_SCATTER(uint16_t, 128, true);
+  else if (dtype == 0 && D == 128) SRA_SCATTER(uint16_t, 128, false);
+  else if (dtype == 0 && D == 64 && full) SRA_SCATTER(uint16_t, 64, true);
+  else if (dtype == 0 && D == 64) SRA_SCATTER(uint16_t, 64, false);
+  else if (dtype == 1 && D == 128) SRA_SCATTER(float, 128, false);
+  else SRA_SCATTER(float, 64, false);
+#undef SRA_SCATTER
   return hipGetLastError();
 }
 

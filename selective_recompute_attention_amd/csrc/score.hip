@@ -235,24 +235,24 @@ __device__ __forceinline__ void anchor_block(int len, int64_t base, int src, int
   for (int round = 0; round < anc.k; ++round) {
     unsigned long long bv = 0;
     int bt = INT_MAX;
-    auto consider = [&](unsigned long long v, int t) {
-      const bool after = v < pv || (v == pv && t > pt);
-      const bool better = after && (v > bv || (v == bv && t < bt));
+    // bitwise rather than short-circuit logic: the conditions become mask operations, not branches
+    auto consider = [&](unsigned long long v, int t, bool valid) {
+      const bool after = (v < pv) | ((v == pv) & (t > pt));
+      const bool better = valid & after & ((v > bv) | ((v == bv) & (t < bt)));
       bv = better ? v : bv;
       bt = better ? t : bt;
     };
     if (in_reg) {
 #pragma unroll
-      for (int j = 0; j < RJ; ++j)
-        if (lane + 64 * j < len) consider(rv[j], lane + 64 * j);
+      for (int j = 0; j < RJ; ++j) consider(rv[j], lane + 64 * j, lane + 64 * j < len);
     } else {
-      for (int t = lane; t < len; t += 64) consider(tot[t], t);
+      for (int t = lane; t < len; t += 64) consider(tot[t], t, true);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const unsigned long long ov = __shfl_xor(bv, off, 64);
       const int ot = __shfl_xor(bt, off, 64);
-      const bool better = ov > bv || (ov == bv && ot < bt);
+      const bool better = (ov > bv) | ((ov == bv) & (ot < bt));
       bv = better ? ov : bv;
       bt = better ? ot : bt;
     }
