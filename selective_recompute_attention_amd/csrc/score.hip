@@ -116,11 +116,14 @@ __global__ __launch_bounds__(256) void k_score_prep(ChunkTab tab, int Lq, int Hq
 
 // Online merge of one (max, sum of exp2(y - max)) pair into a running pair. Branch-free: an empty
 // pair (-inf, 0) scales the running sum by exp2(0) = 1 and adds 0, so it leaves the pair's bits as
-// they are; when both maxima are -inf the shift is 0 and the sum stays 0.
+// they are; when both maxima are -inf the shift is 0 and the sum stays 0. The bare exp2 flushes
+// results below 2^-126 to zero: one of the two terms has weight exp2(0) = 1 on a sum >= 1 (a
+// non-empty pair counts its own maximum once), and a sum counts fewer than 2^31 keys, so a flushed
+// term (below 2^31 * 2^-126) could not have changed the float32 result.
 __device__ __forceinline__ void ml_merge(float& M, float& S, float2 p) {
   const float nm = fmaxf(M, p.x);
   const float sh = nm == -INFINITY ? 0.f : nm;
-  S = S * exp2f(M - sh) + p.y * exp2f(p.x - sh);
+  S = S * fast_exp2(M - sh) + p.y * fast_exp2(p.x - sh);
   M = nm;
 }
 
@@ -474,22 +477,26 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
       u32x4 ha, hb, la, lb;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t hw[2][2], lw[2][2];
+        float r[2][2];   // [a or b output][element of the pair]
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const float a = bf2f((qraw[ks][k] >> (16 * t)) & 0xffffu);
           const float b = bf2f((qraw[ks + NKS / 2][k] >> (16 * t)) & 0xffffu);
           const float2 cw = qcs[qrow * H + 16 * ks + 8 * hh + 2 * k + t];
-          const float r0 = (a * cw.x - b * cw.y) * qr.scale_log2, r1 = (a * cw.y + b * cw.x) * qr.scale_log2;
-          hw[0][t] = f2bf(r0);
-          hw[1][t] = f2bf(r1);
-          lw[0][t] = f2bf(r0 - bf2f(hw[0][t]));
-          lw[1][t] = f2bf(r1 - bf2f(hw[1][t]));
+          r[0][t] = (a * cw.x - b * cw.y) * qr.scale_log2;
+          r[1][t] = (a * cw.y + b * cw.x) * qr.scale_log2;
         }
-        ha[k] = qok ? hw[0][0] | (hw[0][1] << 16) : 0u;
-        hb[k] = qok ? hw[1][0] | (hw[1][1] << 16) : 0u;
-        la[k] = qok ? lw[0][0] | (lw[0][1] << 16) : 0u;
-        lb[k] = qok ? lw[1][0] | (lw[1][1] << 16) : 0u;
+        // hi = bf16(r), lo = bf16(r - hi), both rounded to nearest even, one pair per conversion
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          hw[o] = pack_bf2(r[o][0], r[o][1]);
+          lw[o] = pack_bf2(r[o][0] - bf2f(hw[o] & 0xffffu), r[o][1] - __uint_as_float(hw[o] & 0xffff0000u));
+        }
+        ha[k] = qok ? hw[0] : 0u;
+        hb[k] = qok ? hw[1] : 0u;
+        la[k] = qok ? lw[0] : 0u;
+        lb[k] = qok ? lw[1] : 0u;
       }
       qh[ks] = as_bf16x8(ha);
       qh[ks + NKS / 2] = as_bf16x8(hb);
