@@ -26,7 +26,12 @@
  *     stream reaches that point. Calls on one stream run in order.
  *   - Storage type: shape->dtype selects bfloat16 (SRA_DTYPE_BF16) or float32
  *     (SRA_DTYPE_F32) for every K/V/Q/output tensor; arithmetic is float32 on the device
- *     (matrix-core products take bf16 operands and accumulate in float32).
+ *     (matrix-core products accumulate in float32). With bfloat16 storage the attention's
+ *     query-key products take fp16 operands: the rotated, scaled query is rounded once to
+ *     fp16 and the keys convert to fp16 exactly, so keys must have magnitude at most 65504
+ *     and the rotated query times log2(e)/sqrt(head_dim) likewise (bfloat16 values beyond
+ *     that are outside the supported range); probability-value products take bf16 operands.
+ *     Scoring and the attention statistics keep a bf16 hi/lo query against exact bf16 keys.
  *   - Rotary embedding: pairs (x_i, x_{i+d/2}) rotate by pos * theta_i,
  *     theta_i = rope_base^(-2i/d); angles are formed in float64.
  *   - Tensor layouts are row-major and token-major: [tokens][heads][head_dim].

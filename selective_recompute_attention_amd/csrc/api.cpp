@@ -654,7 +654,7 @@ int sra_chunk_attention_stats(const sra_shape* shape, int32_t n_req, const void*
   // the query of every context token, rotated at its position and split hi/lo (identity rows)
   e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads, n_req, Lctx, Lctx,
                           q_fresh, nullptr, nullptr, q_rows, 1, nullptr, nullptr, nullptr, nullptr, qop,
-                          p.qop_blocks, attn_scale_log2(shape->head_dim), shape->rope_base, stream);
+                          p.qop_blocks, false, attn_scale_log2(shape->head_dim), shape->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "query operand launch");
   const int per = std::max(1, sra::kMaxEntries / n_chunks);   // requests per launch
   for (int q0 = 0; q0 < n_req; q0 += per) {
@@ -778,7 +778,7 @@ int sra_scatter_kv(const sra_shape* shape, int32_t n_req, const void* k_new, con
     return fail(SRA_E_ALIAS, "fresh rows and fused cache overlap");
   hipError_t e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads,
                                      n_req, R, L, nullptr, k_new, v_new, R, 0, row_pos, k_fused, v_fused,
-                                     nullptr, nullptr, 0, 0.f, shape->rope_base, stream);
+                                     nullptr, nullptr, 0, false, 0.f, shape->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   return ok();
 }
@@ -830,7 +830,7 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
   if (shape->dtype == SRA_DTYPE_BF16)
     e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads, n_req, R, L,
                             q_new, nullptr, nullptr, R, 0, row_pos, nullptr, nullptr, nullptr,
-                            reinterpret_cast<uint16_t*>(wsp(ws, p.qop)), p.qop_blocks,
+                            reinterpret_cast<uint16_t*>(wsp(ws, p.qop)), p.qop_blocks, true,
                             attn_scale_log2(shape->head_dim), shape->rope_base, stream);
   else
     e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, reinterpret_cast<float2*>(wsp(ws, p.cs)),
@@ -984,7 +984,7 @@ int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStre
   hipError_t e = sra::launch_scatter(
       s->dtype, s->head_dim, s->n_q_heads, s->n_kv_heads, n_req, R, L, a->q_fresh, a->k_fresh, a->v_fresh,
       L, 1, a->row_pos, a->k_fused, a->v_fused, bf ? nullptr : reinterpret_cast<float2*>(wsp(ws, p.cs)),
-      bf ? reinterpret_cast<uint16_t*>(wsp(ws, p.qop)) : nullptr, p.qop_blocks, attn_scale_log2(s->head_dim),
+      bf ? reinterpret_cast<uint16_t*>(wsp(ws, p.qop)) : nullptr, p.qop_blocks, true, attn_scale_log2(s->head_dim),
       s->rope_base, stream);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   if ((rc = mark(5)) || (rc = mark(6))) return rc;

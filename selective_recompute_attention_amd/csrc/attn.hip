@@ -5,7 +5,7 @@
 // For recomputed row r at absolute position p = row_pos[r] and query head h (KV head h/g):
 //   q = R(p) q_new[r][h];  out = sum_{j <= p} softmax_j(q . k_j / sqrt(d)) v_j
 //
-// bf16 path, gfx950 matrix cores (v_mfma_f32_32x32x16_bf16):
+// bf16 path, gfx950 matrix cores (v_mfma_f32_32x32x16_f16 for S, v_mfma_f32_32x32x16_bf16 for O):
 //   * A tile is 128 query vectors of one (request, KV head) group: the flattened (row, head in
 //     group) pairs v = r*g + hh, so any group size g packs without padding. Rows are ascending, so
 //     a tile's key range ends at the position of its last row and takes ceil((p_last+1)/64) units
@@ -20,9 +20,12 @@
 //   * Four waves, 32 query vectors each. S^T = K Q^T puts one query vector per lane column, so the
 //     online-softmax row reductions stay in-lane plus one cross-half shuffle, and the probabilities
 //     feed O^T = V^T P^T directly from registers (keys permuted consistently on both operands).
-//   * The query operand comes pre-rotated, pre-scaled by log2(e)/sqrt(d) and split into bf16 hi/lo
-//     planes (rounding the rotated query to one bf16 would move the logits by ~1e-3 relative, the
-//     dominant output error); each wave reads it as consecutive 1 KB blocks.
+//   * The query operand comes pre-rotated, pre-scaled by log2(e)/sqrt(d) and rounded once to fp16
+//     (an 11-bit significand: the logits move by ~1e-4 relative, where one bf16 rounding would move
+//     them by ~1e-3 and dominate the output error); each wave reads it as consecutive 1 KB blocks.
+//     Keys enter LDS as fp16, which holds every bf16 key of magnitude 2^-14 .. 65504 exactly (smaller
+//     ones keep an absolute error below 2^-25; larger ones are outside the supported range), so S
+//     takes one fp16 product per key where a bf16 hi/lo query would take two.
 //   * 64-key tiles of K (row-major, padded) and V (transposed on the way into LDS) are shared by
 //     the four waves; float32 accumulation, exp2 in the log2 domain against a lazily moved
 //     reference maximum; each 32-key half is one online-softmax step. Work groups are numbered with
@@ -37,6 +40,7 @@ namespace sra {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -64,6 +68,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // float pair -> two fp16 (round to nearest even) in one word, and back
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+// the same in one instruction (gfx950's packed conversion; low half from the first operand)
+__device__ __forceinline__ uint32_t cvt_pk_h2(float lo, float hi) {
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 __device__ __forceinline__ float h2f(uint32_t h16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h16); }
 
@@ -173,16 +183,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
     // query operand, K/V prefetch and the row position all go out before the first wait
     const int v = t * 128 + wave * 32 + l32;
-    bf16x8 qhi[NKS], qlo[NKS];
+    f16x8 q16[NKS];
     {
-      // the wave's 32-vector block: a uniform base and 32-bit lane offsets (layout of qop_index)
+      // the wave's 32-vector block, fp16 plane 0: a uniform base and 32-bit lane offsets (layout of
+      // qop_index)
       const char* qb = reinterpret_cast<const char*>(a.qop + qop_index(group, t * 4 + wave, 0, 0, 0, 0, a.qop_blocks, NKS));
       const uint32_t lo = (uint32_t)(l32 * 16 + hh * 8) * 2u;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        qhi[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + ((uint32_t)(ks * 2 + 0) * 1024u + lo)));
-        qlo[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qb + ((uint32_t)(ks * 2 + 1) * 1024u + lo)));
-      }
+      for (int ks = 0; ks < NKS; ++ks)
+        q16[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(qb + ((uint32_t)(ks * 2) * 1024u + lo)));
     }
     prefetch(kbeg, kend);
     const int r = min(v, Mv - 1) / g;
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const int pq = qvalid ? min(p_r, a.L - 1) : -1;
     if (!qvalid) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qhi[ks] = qlo[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      for (int ks = 0; ks < NKS; ++ks) q16[ks] = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
     }
     // smallest position among this wave's query vectors: tiles entirely at or below it need no mask
     const int pmin = (int)wave_reduce(qvalid ? (uint32_t)pq : (uint32_t)INT_MAX,
@@ -209,7 +218,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
         const int uu = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(&Ks[buf][(uu / (D / 8)) * KST + 8 * (uu % (D / 8))]) = kr[i];
+        // keys go into LDS as fp16: every bf16 value of magnitude 2^-14 .. 65504 converts exactly
+        u32x4 kh;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          kh[w] = cvt_pk_h2(__builtin_bit_cast(float, kr[i][w] << 16), __builtin_bit_cast(float, kr[i][w] & 0xffff0000u));
+        *reinterpret_cast<u32x4*>(&Ks[buf][(uu / (D / 8)) * KST + 8 * (uu % (D / 8))]) = kh;
       }
       if (vtask) {
 #pragma unroll
@@ -244,10 +258,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
         sc[st] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 ka =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(Kc + (32 * st + l32) * KST + 16 * ks + 8 * hh));
-          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qhi[ks], sc[st], 0, 0, 0);
-          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qlo[ks], sc[st], 0, 0, 0);
+          const f16x8 ka = __builtin_bit_cast(
+              f16x8, *reinterpret_cast<const u32x4*>(Kc + (32 * st + l32) * KST + 16 * ks + 8 * hh));
+          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, q16[ks], sc[st], 0, 0, 0);
         }
       }
 #pragma unroll

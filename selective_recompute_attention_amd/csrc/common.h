@@ -203,7 +203,7 @@ hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int r
 hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, int L,
                           const void* qn, const void* kn, const void* vn, int fresh_rows,
                           int indexed, const int* row_pos, void* kf, void* vf, float2* cs_out,
-                          uint16_t* qop, int qop_blocks, float scale_log2, double base,
+                          uint16_t* qop, int qop_blocks, bool q16, float scale_log2, double base,
                           hipStream_t st);
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
                              double base, hipStream_t st);

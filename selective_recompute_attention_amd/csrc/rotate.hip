@@ -32,12 +32,14 @@ __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int row
 // One block per (recomputed row r, request) at position p = row_pos[r]: forms the row's angles
 // once, then (each part optional) writes them out, scatters the fresh K/V row to fused row p with
 // K rotated at p, and writes the attention's query operand: every query head rotated at p, scaled
-// by log2(e)/sqrt(d) and split into bf16 hi/lo planes in the matrix-operand order of qop_index.
+// by log2(e)/sqrt(d) and either split into bf16 hi/lo planes (Q16 false: the statistics' exact
+// products) or rounded once to fp16 in plane 0 (Q16 true: the attention's operand), in the
+// matrix-operand order of qop_index.
 // Fresh rows are compact (row r) or position-indexed (row p). Rows outside [0, L) write nothing
 // but zero query operands. The first batch of every part is loaded before the angles are formed.
 // FULL: kn and qop are both set (bf16), so every first-batch load is unconditional and the
 // angles wait on the frequency load alone.
-template <typename T, int D, bool FULL>
+template <typename T, int D, bool FULL, bool Q16>
 __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
                                                  const T* __restrict__ qn, const T* __restrict__ kn,
                                                  const T* __restrict__ vn, int fresh_rows,
@@ -151,15 +153,24 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const float* f = half ? y : x;
-          u32x4 wh, wl;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            wh[k] = pack_bf2(f[2 * k], f[2 * k + 1]);
-            wl[k] = pack_bf2(f[2 * k] - bf2f(wh[k] & 0xffffu), f[2 * k + 1] - bf2f(wh[k] >> 16));
-          }
           const int kss = ks + half * (NKS / 2);
-          *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 0, v & 31, hh, qop_blocks, NKS)) = wh;
-          *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 1, v & 31, hh, qop_blocks, NKS)) = wl;
+          if constexpr (Q16) {
+            u32x4 wq;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              wq[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * k]) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * k + 1]) << 16);
+            *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 0, v & 31, hh, qop_blocks, NKS)) = wq;
+          } else {
+            u32x4 wh, wl;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              wh[k] = pack_bf2(f[2 * k], f[2 * k + 1]);
+              wl[k] = pack_bf2(f[2 * k] - bf2f(wh[k] & 0xffffu), f[2 * k + 1] - bf2f(wh[k] >> 16));
+            }
+            *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 0, v & 31, hh, qop_blocks, NKS)) = wh;
+            *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 1, v & 31, hh, qop_blocks, NKS)) = wl;
+          }
         }
       };
 #pragma unroll
@@ -372,22 +383,24 @@ hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int r
 hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, int L,
                           const void* qn, const void* kn, const void* vn, int fresh_rows,
                           int indexed, const int* row_pos, void* kf, void* vf, float2* cs_out,
-                          uint16_t* qop, int qop_blocks, float scale_log2, double base,
+                          uint16_t* qop, int qop_blocks, bool q16, float scale_log2, double base,
                           hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(128);
   const Theta th = make_theta(D, base);
-#define SRA_SCATTER(TT, DD, FF)                                                                         \
-  k_scatter<TT, DD, FF><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const TT*)qn, (const TT*)kn, (const TT*)vn,       \
+#define SRA_SCATTER(TT, DD, FF, QQ)                                                                     \
+  k_scatter<TT, DD, FF, QQ><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const TT*)qn, (const TT*)kn, (const TT*)vn,       \
                                          fresh_rows, indexed, row_pos, (TT*)kf, (TT*)vf, cs_out,         \
                                          dtype == 0 ? qop : nullptr, qop_blocks, scale_log2, th)
   const bool full = dtype == 0 && kn && qop;
-  if (dtype == 0 && D == 128 && full) SRA_SCATTER(uint16_t, 128, true);
-  else if (dtype == 0 && D == 128) SRA_SCATTER(uint16_t, 128, false);
-  else if (dtype == 0 && D == 64 && full) SRA_SCATTER(uint16_t, 64, true);
-  else if (dtype == 0 && D == 64) SRA_SCATTER(uint16_t, 64, false);
-  else if (dtype == 1 && D == 128) SRA_SCATTER(float, 128, false);
-  else SRA_SCATTER(float, 64, false);
+  if (dtype == 0 && D == 128 && full) SRA_SCATTER(uint16_t, 128, true, true);   // fused layer
+  else if (dtype == 0 && D == 128 && q16) SRA_SCATTER(uint16_t, 128, false, true);
+  else if (dtype == 0 && D == 128) SRA_SCATTER(uint16_t, 128, false, false);
+  else if (dtype == 0 && D == 64 && full) SRA_SCATTER(uint16_t, 64, true, true);
+  else if (dtype == 0 && D == 64 && q16) SRA_SCATTER(uint16_t, 64, false, true);
+  else if (dtype == 0 && D == 64) SRA_SCATTER(uint16_t, 64, false, false);
+  else if (dtype == 1 && D == 128) SRA_SCATTER(float, 128, false, false);
+  else SRA_SCATTER(float, 64, false, false);
 #undef SRA_SCATTER
   return hipGetLastError();
 }
