@@ -330,13 +330,11 @@ def hkvd_filter(dev, row_pos, n_prev: int, n_keep: int) -> np.ndarray:
     among the tokens layer i-1 selected, the given share with the highest KV deviation).
 
     row_pos holds the previous selection (n_prev context positions, ascending) followed by the query
-    rows. The n_keep context rows of highest deviation are kept -- ranked on float32 deviations,
-    the precision the device decides in, ties to the lower row -- in ascending order, followed by
-    the same query rows.
+    rows. The n_keep context rows of highest deviation (float64, ties to the lower row) are kept in
+    ascending order, followed by the same query rows.
     """
     rp = np.asarray(row_pos, dtype=np.int64)
-    d32 = np.asarray(dev, dtype=np.float64)[:n_prev].astype(np.float32).astype(np.float64)
-    keep = select_topn(d32, int(n_keep))
+    keep = select_topn(np.asarray(dev, dtype=np.float64)[:n_prev], int(n_keep))
     return np.concatenate([rp[:n_prev][keep], rp[n_prev:]]).astype(np.int32)
 
 
@@ -357,19 +355,22 @@ def sparse_causal_attn(q_new, row_pos, k_fused, v_fused, dtype: str, base: float
     g = Hq // Hkv
     rp = np.asarray(row_pos, dtype=np.int64)
     rows = range(R) if rows is None else rows
+    # keys and values of one KV head as contiguous [L, d] arrays (a copy, no arithmetic)
+    kh = [np.ascontiguousarray(np.asarray(k_fused, dtype=np.float64)[:, kv, :]) for kv in range(Hkv)]
+    vh = [np.ascontiguousarray(np.asarray(v_fused, dtype=np.float64)[:, kv, :]) for kv in range(Hkv)]
     outs, lses = [], []
     for r in rows:
         p = int(rp[r])
         qr = rope(q[r], p, base)                                  # [Hq, d]
         o = np.empty((Hq, d))
         lse = np.empty(Hq)
-        for h in range(Hq):
-            kv = h // g
-            x = k_fused[:p + 1, kv, :] @ qr[h] / math.sqrt(d)   # [p+1]
-            m = x.max()
+        for kv in range(Hkv):
+            # the g query heads h = kv*g .. kv*g+g-1 of this KV head, one column each
+            x = kh[kv][:p + 1] @ qr[kv * g:(kv + 1) * g].T / math.sqrt(d)   # [p+1, g]
+            m = x.max(axis=0)
             e = np.exp(x - m)
-            o[h] = (e / e.sum()) @ v_fused[:p + 1, kv, :]
-            lse[h] = m + math.log(e.sum())
+            o[kv * g:(kv + 1) * g] = (e / e.sum(axis=0)).T @ vh[kv][:p + 1]
+            lse[kv * g:(kv + 1) * g] = m + np.log(e.sum(axis=0))
         outs.append(o)
         lses.append(lse)
     return np.asarray(outs).reshape(len(outs), Hq, d), np.asarray(lses).reshape(len(lses), Hq)

@@ -7,8 +7,10 @@ Comparison rules (float outputs):
   * scores: 1e-4 relative to the oracle;
   * selected indices: bit-exact, except that swaps are allowed among tokens whose oracle score is
     within 1e-5 relative of the N-th score (per chunk with quotas);
-  * attention output: bfloat16 max |err| <= 1.5e-2 and mean |err| <= 2e-3; float32
-    |err| <= 1e-4 * max(1, |ref|); log-sum-exp: 2e-2 (bf16) / 1e-4 (f32) absolute.
+  * attention output: bfloat16 max |err| <= 1.5e-2 where |ref| < 4, and half a bfloat16 ulp of
+    |ref| plus 5e-3 where |ref| >= 4 (the output's own rounding to bfloat16 reaches 1.56e-2 there);
+    mean |err| <= 2e-3; float32 |err| <= 1e-4 * max(1, |ref|); log-sum-exp: 2e-2 (bf16) / 1e-4 (f32)
+    absolute.
 """
 import sys
 
@@ -90,8 +92,9 @@ def assert_storage_close(gpu_vals: np.ndarray, ref: np.ndarray, dtype: str, what
 
 
 def assert_out_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = "attention output"):
-    """bf16: max |err| <= 1.5e-2 and mean |err| <= 2e-3. Where |ref| >= 4 half a bfloat16 ulp of the
-    stored output alone is 1.56e-2, so there the bound is half an ulp plus 5e-3 of arithmetic error."""
+    """bf16: max |err| <= 1.5e-2 and mean |err| <= 2e-3. Where |ref| >= 4, half a bfloat16 ulp of the
+    stored output alone is 1.56e-2 (a correctly rounded output can miss 1.5e-2 there), so the bound is
+    half an ulp of |ref| plus 5e-3 of arithmetic error: 2.06e-2 on [4, 8), 3.6e-2 on [8, 16)."""
     err = np.abs(gpu - ref)
     if dtype == "bf16":
         bound = np.maximum(1.5e-2, 0.5 * bf16_ulp(ref) + 5e-3)

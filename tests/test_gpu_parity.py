@@ -4,6 +4,8 @@ Small workloads compare every output; the full-size workloads compare every scor
 every fused K/V row, and the attention output of sampled rows (the oracle evaluates rows one by
 one). Tolerances are those stated in tests/gpu_helpers.py.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -53,11 +55,14 @@ def oracle_compare(w, res, layer=0, rows=None, quotas=None, check_scores=True):
         still[Lctx:] = False
         np.testing.assert_array_equal(bits(res["k_fused"][q], dt)[still], O.storage_bits(kf[still], dt))
         assert_storage_close(decode(res["k_fused"][q], dt), kf, dt, f"fused K (request {q})")
-        sel_rows = list(range(R)) if rows is None else rows
+        sel_rows = list(range(R)) if rows is None else (rows(q) if callable(rows) else rows)
         o_ref, lse_ref = O.sparse_causal_attn(lay["q_new"][q][rp], rp, kf, vf, dt, base, rows=sel_rows)
         o_gpu = decode(res["out"][q][sel_rows], dt)
         mx, mean = assert_out_close(o_gpu, o_ref, dt)
         stats["out_max"] = max(stats.get("out_max", 0.0), mx)
+        stats["rows"] = stats.get("rows", 0) + len(sel_rows)
+        if dt == "bf16":   # values past the plain 1.5e-2 (allowed only where |O| >= 4, see assert_out_close)
+            stats["over_1.5e-2"] = stats.get("over_1.5e-2", 0) + int((np.abs(o_gpu - o_ref) > 1.5e-2).sum())
         lse_tol = 2e-2 if dt == "bf16" else 1e-4
         np.testing.assert_allclose(res["lse"][q][sel_rows], lse_ref, rtol=0, atol=lse_tol)
     say(f"    parity stats: {stats}")
@@ -82,12 +87,24 @@ def test_mistral_fused_all_rows():
     oracle_compare(w, res)
 
 
+def wide_rows(res, dtype, Lq, k, top, seed=0):
+    """Rows of request q to check at full size: a seeded spread (sample_rows), every query row, and the
+    `top` rows with the largest GPU |O| (where the output's own bf16 rounding is coarsest)."""
+    def pick(q):
+        R = res["R"]
+        big = np.abs(decode(res["out"][q], dtype)).reshape(R, -1).max(axis=1)
+        rows = set(sample_rows(R, Lq, k, seed=seed + q)) | set(range(R - Lq, R))
+        rows |= set(np.argsort(-big, kind="stable")[:top].tolist())
+        return sorted(rows)
+    return pick
+
+
 def test_yi_batch_of_four_sampled_rows():
     w = make_workload(2)
     N = O.select_count(10, 100, w.cfg.ctx_len)
     say(f"case yi34b_layer_x4req fused N={N}")
     res = run_fused(w, n_select=N)
-    oracle_compare(w, res, rows=sample_rows(res["R"], w.cfg.query_len, 64))
+    oracle_compare(w, res, rows=wide_rows(res, "bf16", w.cfg.query_len, 96, 16))
 
 
 def test_llama70b_tapered_layers():
@@ -96,7 +113,7 @@ def test_llama70b_tapered_layers():
     N0 = O.select_count(14, 70, Lctx)
     say(f"case llama70b_8layers layer 0 (scoring) N={N0}")
     res0 = run_fused(w, 0, n_select=N0)
-    oracle_compare(w, res0, 0, rows=sample_rows(res0["R"], Lq, 40))
+    oracle_compare(w, res0, 0, rows=wide_rows(res0, "bf16", Lq, 128, 16))
     scores = torch.from_numpy(res0["scores"]).cuda()
     prev = set(res0["row_pos"][0][:N0].tolist())
     for l in (5, 7):
@@ -112,14 +129,15 @@ def test_llama70b_tapered_layers():
         assert cur <= prev, "tapered selections must nest"
         prev = cur
         res = run_fused(w, l, score=False, row_pos_in=rp_h)
-        oracle_compare(w, res, l, rows=sample_rows(res["R"], Lq, 32), check_scores=False)
+        # at least 256 spread rows, every query row and the 32 rows of largest |O|
+        oracle_compare(w, res, l, rows=wide_rows(res, "bf16", Lq, 256, 32, seed=l), check_scores=False)
 
 
 def test_llama7b_per_chunk_quotas():
     w = make_workload(4)
     say(f"case llama7b_mha_quota fused N={int(w.quotas.sum())}")
     res = run_fused(w, quotas=w.quotas)
-    oracle_compare(w, res, rows=sample_rows(res["R"], w.cfg.query_len, 40), quotas=w.quotas)
+    oracle_compare(w, res, rows=wide_rows(res, "bf16", w.cfg.query_len, 48, 16), quotas=w.quotas)
 
 
 # ------------------------------------------------------------------------------ edge cases
@@ -157,9 +175,10 @@ EDGE = [
 
 @pytest.mark.parametrize("name,kw,sel", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_cases(name, kw, sel):
-    w = make_custom(select=sel, seed=hash(name) % 1000, **kw)
+    seed = zlib.crc32(name.encode()) % 1000   # fixed per case (str hashes change between processes)
+    w = make_custom(select=sel, seed=seed, **kw)
     Lctx = int(w.chunks[0, :, 1].sum())
-    say(f"case edge {name}")
+    say(f"case edge {name} seed={seed}")
     if sel[0] == "quota":
         res = run_fused(w, quotas=w.quotas)
         oracle_compare(w, res, quotas=w.quotas)

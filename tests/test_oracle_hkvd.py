@@ -82,11 +82,14 @@ def test_hkvd_filter_brute_force_and_ties():
             assert list(got[:n_keep]) == [int(ctx[i]) for i in good[0]]
 
 
-def test_hkvd_filter_decides_in_float32():
-    # equal as float32, different as float64: the lower row wins the tie
+def test_hkvd_filter_ranks_in_float64():
+    # equal as float32, different as float64: the plain definition ranks the larger value first
+    # (the device ranks float32 deviations; the GPU tests allow swaps inside the 1e-5 window)
     dev = np.array([1.0, 1.0 + 1e-12, 0.5])
     rows = np.array([3, 7, 9, 20], dtype=np.int32)
-    assert list(O.hkvd_filter(dev, rows, 3, 1)) == [3, 20]
+    assert list(O.hkvd_filter(dev, rows, 3, 1)) == [7, 20]
+    # an exact tie keeps the lower row
+    assert list(O.hkvd_filter(np.array([2.0, 2.0, 0.5]), rows, 3, 1)) == [3, 20]
 
 
 def _taper_workload():

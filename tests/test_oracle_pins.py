@@ -171,6 +171,30 @@ def test_anchor_brute_force_and_tie_break():
     np.testing.assert_array_equal(O.extract_anchors(k, chunks, 4, "f32"), [[1, 3, 2, 5]])
 
 
+def test_anchor_norm_spans_every_kv_head():
+    # Three KV heads, d = 2. Full-row L2 norms: t0 3, t1 sqrt(13) = 3.61, t2 3.5, t3 sqrt(12) = 3.46,
+    # so the anchors in order are 1, 2, 3, 0. A norm of head 0 alone would rank 0 first, of the last
+    # head alone 2 first, the largest per-head norm 2, 0, 1, 3, and a sum of per-head norms 3 first.
+    k = np.zeros((4, 3, 2), dtype=np.float32)
+    k[0, 0] = (3.0, 0.0)
+    k[1, 0], k[1, 1], k[1, 2] = (1.0, 0.0), (2.0, 2.0), (2.0, 0.0)
+    k[2, 2] = (0.0, 3.5)
+    k[3, :, 0] = 2.0
+    chunks = np.array([[0, 4, 0, 0]], dtype=np.int32)
+    np.testing.assert_array_equal(O.extract_anchors(k, chunks, 4, "f32"), [[1, 2, 3, 0]])
+    np.testing.assert_allclose(O.key_norms(k, "f32"), [3.0, np.sqrt(13.0), 3.5, np.sqrt(12.0)], rtol=1e-15)
+
+
+def test_key_norms_equal_library_norm_of_flattened_rows():
+    # eight KV heads x 128 dims, bf16 with the x4 outliers: numpy's own vector norm of each stored row
+    w = make_workload(1)
+    rows = O.to_f64(w.k_crit[:2048], "bf16").reshape(2048, -1)
+    np.testing.assert_allclose(O.key_norms(w.k_crit[:2048], "bf16"), np.linalg.norm(rows, axis=1), rtol=1e-13)
+    # a per-head norm would differ from it on these rows
+    assert not np.allclose(np.linalg.norm(O.to_f64(w.k_crit[:2048], "bf16")[:, 0, :], axis=1),
+                           O.key_norms(w.k_crit[:2048], "bf16"), rtol=1e-3)
+
+
 def test_anchors_pick_outliers_and_ignore_rotation():
     w = make_workload(1)
     norms = O.key_norms(w.k_crit, "bf16")
