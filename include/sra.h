@@ -28,9 +28,9 @@
  *     (SRA_DTYPE_F32) for every K/V/Q/output tensor; arithmetic is float32 on the device
  *     (matrix-core products accumulate in float32). With bfloat16 storage the attention's
  *     query-key products take fp16 operands: the rotated, scaled query is rounded once to
- *     fp16 and the keys convert to fp16 exactly, so keys must have magnitude at most 65504
- *     and the rotated query times log2(e)/sqrt(head_dim) likewise (bfloat16 values beyond
- *     that are outside the supported range); probability-value products take bf16 operands.
+ *     fp16 and the keys convert to fp16 exactly; a (request, KV head) group whose keys or
+ *     scaled queries lie beyond fp16's range is detected and recomputed exactly in float32
+ *     (see sra_sparse_causal_attn); probability-value products take bf16 operands.
  *     Scoring and the attention statistics keep a bf16 hi/lo query against exact bf16 keys.
  *   - Rotary embedding: pairs (x_i, x_{i+d/2}) rotate by pos * theta_i,
  *     theta_i = rope_base^(-2i/d); angles are formed in float64.
@@ -145,6 +145,10 @@ typedef struct {
      * with q_crit and bfloat16 storage the re-rotation runs inside the scoring launch, so stage
      * 0 is empty and stage 1 covers both). */
     hipEvent_t* stage_events;
+    /* optional out [n_req][Hkv] int32, or NULL: 1 for each (request, KV head) whose attention was
+     * recomputed exactly in float32 because a key or scaled query lay beyond fp16's range (see
+     * sra_sparse_causal_attn), else 0; bfloat16 storage only (float32 leaves it untouched) */
+    int32_t* attn_fallback;
 } sra_layer_args;
 
 /* ------------------------------------------------------------------------ host helpers */
@@ -339,11 +343,18 @@ int sra_hkvd_select(const sra_shape* shape, int32_t n_req, const void* k_fused, 
  * unique, < L. k_fused, v_fused: [n_req][L][Hkv][d]. out: [n_req][R][Hq][d] (storage
  * dtype). lse: [n_req][R][Hq] float32 or NULL. ws: at least
  * sra_workspace_size(shape, n_req, 1, L, R, 1) bytes.
+ * With bfloat16 storage the query-key products take fp16 operands (the rotated query times
+ * log2(e)/sqrt(d) rounded once to fp16, the keys converted exactly). A (request, KV head) group with
+ * a key of magnitude above 65504 or a scaled query at or beyond 65520 has no fp16 operand: that
+ * group is recomputed exactly in float32 from the bf16 inputs (slower, same bounds); its logits must
+ * be finite in float32. fallback: optional out [n_req][Hkv] int32, 1 where a group was recomputed
+ * that way, else 0 (NULL: not reported; with float32 storage nothing falls back and the array is
+ * left untouched).
  * Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_DTYPE, SRA_E_ALIAS, SRA_E_WORKSPACE, SRA_E_HIP. */
 int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_new,
                            const int32_t* row_pos, int32_t R,
                            const void* k_fused, const void* v_fused, int32_t L,
-                           void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* out, float* lse, int32_t* fallback, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------ fused entry */

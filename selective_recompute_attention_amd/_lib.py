@@ -49,6 +49,7 @@ class LayerArgs(ctypes.Structure):
         ("k_fused", ctypes.c_void_p), ("v_fused", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+        ("attn_fallback", ctypes.c_void_p),
     ]
 
 
@@ -81,7 +82,7 @@ _SIGS = {
     "sra_hkvd_select": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int32, _P, _P, _P, _c.c_int32,
                                    _c.c_int32, _c.c_int32, _P, _P, _P]),
     "sra_sparse_causal_attn": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int32, _P, _P,
-                                          _c.c_int32, _P, _P, _P, _c.c_size_t, _P]),
+                                          _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
     "sra_fused_layer": (_c.c_int, [_c.POINTER(LayerArgs), _P, _c.c_size_t, _P]),
     "sra_check_rows": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int32), _P]),
     "sra_pipelined_layers": (_c.c_int, [_c.POINTER(LayerArgs), _c.c_int32, _c.POINTER(_P), _c.POINTER(_P),

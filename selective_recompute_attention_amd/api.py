@@ -176,17 +176,18 @@ def hkvd_select(shape, k_fused, v_fused, k_new, v_new, row_pos_prev, n_prev, n_k
                                 _ptr(dev), _ptr(row_pos_next), _stream(stream)))
 
 
-def sparse_causal_attn(shape, q_new, row_pos, k_fused, v_fused, out, lse, ws, stream=None):
+def sparse_causal_attn(shape, q_new, row_pos, k_fused, v_fused, out, lse, ws, stream=None, fallback=None):
+    """fallback: optional int32 [n_req][Hkv], 1 where a group was recomputed exactly (fp16 range)."""
     n_req, R = row_pos.shape
     check(lib().sra_sparse_causal_attn(ctypes.byref(shape), n_req, _ptr(q_new), _ptr(row_pos), R,
                                        _ptr(k_fused), _ptr(v_fused), k_fused.shape[-3], _ptr(out), _ptr(lse),
-                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                                       _ptr(fallback), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def _layer_args(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, row_pos, k_fused, v_fused,
                 out, lse=None, q_crit=None, k_crit_store=None, n_select=None, quotas=None, scores=None,
                 anchors_k=0, anchor_rows=None, anchor_norms=None, hkvd_prev=None, hkvd_prev_ctx=0,
-                hkvd_dev=None, stage_events=None, store_rows=None):
+                hkvd_dev=None, stage_events=None, store_rows=None, attn_fallback=None):
     """A filled sra_layer_args and the host arrays it points to (keep both alive during the call)."""
     ch = np.asarray(chunks, dtype=np.int32)
     n_req, n_chunks = ch.shape[0], ch.shape[1]
@@ -215,6 +216,7 @@ def _layer_args(shape, *, chunks, k_store, v_store, q_fresh, k_fresh, v_fresh, r
     a.k_fused, a.v_fused, a.out, a.lse = _ptr(k_fused), _ptr(v_fused), _ptr(out), _ptr(lse)
     if stage_events is not None:
         a.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
+    a.attn_fallback = _ptr(attn_fallback)
     return a, (carr, qa)
 
 
@@ -225,7 +227,8 @@ def fused_layer(shape, *, ws, stream=None, **kw):
     [n_req][n_chunks][anchors_k] (int32) and optional anchor_norms [crit_store_rows] (float32);
     hkvd_prev [n_req][hkvd_prev_ctx + Lq] (int32) to select by gradual filtering (the n_select
     previous context rows of highest KV deviation, written to hkvd_dev [n_req][hkvd_prev_ctx]);
-    stage_events: optional ctypes array of 8 hipEvent_t handles."""
+    stage_events: optional ctypes array of 8 hipEvent_t handles; attn_fallback: optional int32
+    [n_req][Hkv] report of groups recomputed exactly (fp16 range)."""
     a, keep = _layer_args(shape, **kw)
     check(lib().sra_fused_layer(ctypes.byref(a), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     del keep

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -108,6 +109,8 @@ int attn_pieces(int n_req, int Hkv) {
 struct Plan {
   // offsets in bytes from the workspace base
   size_t cs = 0;          // rotary table [n_req][R][d/2] float2
+  size_t k16 = 0;         // fp16 copy of the fused keys [n_req][L][Hkv][d] (bf16 attention)
+  size_t flags = 0;       // fp16 overflow flags [n_req][Hkv]
   size_t region = 0;      // start of the union of the score and attention regions
   // score (bf16)
   int Mpad = 0;
@@ -129,6 +132,15 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
   size_t off = 0;
   p.cs = off;  // the float32 attention's angle table
   if (s->dtype == SRA_DTYPE_F32) off = align256(off + (size_t)n_req * R * (D / 2) * sizeof(float2));
+  // the bf16 attention's fp16 keys and overflow flags, outside the union below: the re-rotation
+  // writes them while the scoring still uses its region
+  p.k16 = off;
+  p.flags = off;
+  if (s->dtype == SRA_DTYPE_BF16) {
+    off = align256(off + (size_t)n_req * L * Hkv * D * sizeof(uint16_t));
+    p.flags = off;
+    off = align256(off + (size_t)n_req * Hkv * sizeof(unsigned));
+  }
   p.region = off;
   // score region
   size_t so = off;
@@ -167,6 +179,22 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
 }
 
 char* wsp(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// A distinct id per attention call, never 0: fp16 overflow flags of another call never match it.
+std::atomic<unsigned> g_call_id{0};
+unsigned next_call_id() {
+  unsigned v = ++g_call_id;
+  while (v == 0) v = ++g_call_id;
+  return v;
+}
+sra::F16Shadow shadow_of(const sra_shape* s, void* ws, const Plan& p, unsigned call_id) {
+  sra::F16Shadow sh;
+  if (s->dtype != SRA_DTYPE_BF16) return sh;
+  sh.kh = reinterpret_cast<uint16_t*>(wsp(ws, p.k16));
+  sh.flags = reinterpret_cast<unsigned*>(wsp(ws, p.flags));
+  sh.call_id = call_id;
+  return sh;
+}
 
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SRA_OK;
@@ -228,13 +256,14 @@ std::vector<Entry> chunk_entries(const sra_chunk* ch, int n_req, int n_chunks, i
 
 // ------------------------------------------------------------------------------ stage bodies
 int do_rerotate(const sra_shape* s, int n_req, const void* ks, const void* vs,
-                const sra_chunk* ch, int n_chunks, void* kf, void* vf, int L, hipStream_t st) {
+                const sra_chunk* ch, int n_chunks, void* kf, void* vf, int L, hipStream_t st,
+                const sra::F16Shadow& sh = sra::F16Shadow()) {
   const int D = s->head_dim, Hkv = s->n_kv_heads;
   const int64_t row_bytes = (int64_t)Hkv * D * elem_size(s);
   const int rpb = (int)std::max<int64_t>(1, 32768 / (2 * row_bytes));
   auto ents = chunk_entries(ch, n_req, n_chunks, rpb);
   hipError_t e = for_each_tab(ents, [&](const sra::ChunkTab& tab, int, int) {
-    return sra::launch_rerotate(s->dtype, D, Hkv, tab, rpb, ks, vs, kf, vf, L, s->rope_base, st);
+    return sra::launch_rerotate(s->dtype, D, Hkv, tab, rpb, ks, vs, kf, vf, L, s->rope_base, st, sh);
   });
   if (e != hipSuccess) return hip_fail(e, "re-rotation launch");
   return SRA_OK;
@@ -415,15 +444,25 @@ int do_score_select(const sra_shape* s, int n_req, const void* qc, int Lq, const
 // table (f32) in the workspace.
 int do_attn(const sra_shape* s, int n_req, const void* q, int q_rows, int indexed,
             const int32_t* row_pos, int R, const void* kf, const void* vf, int L, void* out,
-            float* lse, void* ws, const Plan& p, hipStream_t st) {
+            float* lse, void* ws, const Plan& p, hipStream_t st, unsigned call_id = 0,
+            int32_t* fallback = nullptr) {
   const int D = s->head_dim, Hq = s->n_q_heads, Hkv = s->n_kv_heads;
   hipError_t e;
   if (s->dtype == SRA_DTYPE_BF16) {
+    sra::AttnExact ex;
+    ex.q = static_cast<const uint16_t*>(q);
+    ex.q_rows = q_rows;
+    ex.indexed = indexed;
+    ex.flags = reinterpret_cast<const unsigned*>(wsp(ws, p.flags));
+    ex.call_id = call_id;
+    ex.fallback = fallback;
+    ex.base = s->rope_base;
     e = sra::launch_attn_bf16(D, n_req, Hq, Hkv, R, L, reinterpret_cast<const uint16_t*>(wsp(ws, p.qop)),
-                              p.qop_blocks, row_pos, (const uint16_t*)kf, (const uint16_t*)vf,
+                              p.qop_blocks, row_pos, reinterpret_cast<const uint16_t*>(wsp(ws, p.k16)),
+                              (const uint16_t*)kf, (const uint16_t*)vf,
                               (uint16_t*)out, lse, p.pieces, reinterpret_cast<int*>(wsp(ws, p.tilecum)),
                               reinterpret_cast<uint16_t*>(wsp(ws, p.part_o)),
-                              reinterpret_cast<float4*>(wsp(ws, p.part_ml)), st);
+                              reinterpret_cast<float4*>(wsp(ws, p.part_ml)), ex, st);
   } else {
     e = sra::launch_attn_f32(D, n_req, Hq, Hkv, R, L, (const float*)q, q_rows, indexed, row_pos,
                              reinterpret_cast<const float2*>(wsp(ws, p.cs)), (const float*)kf,
@@ -809,8 +848,8 @@ int sra_hkvd_select(const sra_shape* shape, int32_t n_req, const void* k_fused, 
 
 int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_new,
                            const int32_t* row_pos, int32_t R, const void* k_fused,
-                           const void* v_fused, int32_t L, void* out, float* lse, void* ws,
-                           size_t ws_bytes, hipStream_t stream) {
+                           const void* v_fused, int32_t L, void* out, float* lse, int32_t* fallback,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
   int rc;
   if ((rc = check_shape(shape))) return rc;
   if (n_req <= 0 || R < 0 || L <= 0 || R > L) return fail(SRA_E_SHAPE, "need n_req > 0, 0 <= R <= L");
@@ -826,17 +865,26 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
     return fail(SRA_E_ALIAS, "out overlaps an input");
   const Plan p = make_plan(shape, n_req, 1, L, R, 1);
   if ((rc = check_ws(ws, ws_bytes, p.attn_end))) return rc;
+  if (fallback && overlap(fallback, (size_t)n_req * shape->n_kv_heads * sizeof(int32_t), out, ob))
+    return fail(SRA_E_ALIAS, "fallback overlaps out");
+  const unsigned call_id = next_call_id();
+  const sra::F16Shadow sh = shadow_of(shape, ws, p, call_id);
   hipError_t e;
-  if (shape->dtype == SRA_DTYPE_BF16)
-    e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads, n_req, R, L,
-                            q_new, nullptr, nullptr, R, 0, row_pos, nullptr, nullptr, nullptr,
-                            reinterpret_cast<uint16_t*>(wsp(ws, p.qop)), p.qop_blocks, true,
-                            attn_scale_log2(shape->head_dim), shape->rope_base, stream);
-  else
+  if (shape->dtype == SRA_DTYPE_BF16) {
+    // the caller's keys: their fp16 copy first (flagging keys beyond fp16), then the query operand
+    e = sra::launch_k_to_f16(shape->head_dim, shape->n_kv_heads, n_req, L, (const uint16_t*)k_fused, sh, stream);
+    if (e == hipSuccess)
+      e = sra::launch_scatter(shape->dtype, shape->head_dim, shape->n_q_heads, shape->n_kv_heads, n_req, R, L,
+                              q_new, nullptr, nullptr, R, 0, row_pos, nullptr, nullptr, nullptr,
+                              reinterpret_cast<uint16_t*>(wsp(ws, p.qop)), p.qop_blocks, true,
+                              attn_scale_log2(shape->head_dim), shape->rope_base, stream, sh);
+  } else {
     e = sra::launch_rope_table(shape->head_dim, n_req, R, row_pos, reinterpret_cast<float2*>(wsp(ws, p.cs)),
                                shape->rope_base, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "attention row-input launch");
-  if ((rc = do_attn(shape, n_req, q_new, R, 0, row_pos, R, k_fused, v_fused, L, out, lse, ws, p, stream)))
+  if ((rc = do_attn(shape, n_req, q_new, R, 0, row_pos, R, k_fused, v_fused, L, out, lse, ws, p, stream, call_id,
+                    fallback)))
     return rc;
   return ok();
 }
@@ -919,6 +967,8 @@ int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStre
   if ((rc = check_ws(ws, ws_bytes, need))) return rc;
   if (dry) return SRA_OK;
 
+  const unsigned call_id = next_call_id();
+  const sra::F16Shadow sh = shadow_of(s, ws, p, call_id);
   hipEvent_t* ev = a->stage_events;
   auto mark = [&](int i) -> int {
     if (!ev) return SRA_OK;
@@ -937,10 +987,11 @@ int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStre
     rf.vf = static_cast<uint16_t*>(a->v_fused);
     rf.L = L;
     rf.base = s->rope_base;
+    rf.sh = sh;
   }
   if ((rc = mark(0))) return rc;
   if (!s1_in_score && (rc = do_rerotate(s, n_req, a->k_store, a->v_store, a->chunks, a->n_chunks, a->k_fused,
-                                        a->v_fused, L, stream)))
+                                        a->v_fused, L, stream, sh)))
     return rc;
   if ((rc = mark(1)) || (rc = mark(2))) return rc;
   if (hkvd) {   // deviation against the re-rotated reused rows, before the scatter replaces them
@@ -985,12 +1036,13 @@ int fused_layer_impl(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStre
       s->dtype, s->head_dim, s->n_q_heads, s->n_kv_heads, n_req, R, L, a->q_fresh, a->k_fresh, a->v_fresh,
       L, 1, a->row_pos, a->k_fused, a->v_fused, bf ? nullptr : reinterpret_cast<float2*>(wsp(ws, p.cs)),
       bf ? reinterpret_cast<uint16_t*>(wsp(ws, p.qop)) : nullptr, p.qop_blocks, true, attn_scale_log2(s->head_dim),
-      s->rope_base, stream);
+      s->rope_base, stream, sh);
   if (e != hipSuccess) return hip_fail(e, "scatter launch");
   if ((rc = mark(5)) || (rc = mark(6))) return rc;
   if ((rc = do_attn(s, n_req, a->q_fresh, L, 1, a->row_pos, R, a->k_fused, a->v_fused, L, a->out,
-                    a->lse, ws, p, stream)))
+                    a->lse, ws, p, stream, call_id, a->attn_fallback)))
     return rc;
+
   if ((rc = mark(7))) return rc;
   return ok();
 }

@@ -20,17 +20,23 @@
 //   * Four waves, 32 query vectors each. S^T = K Q^T puts one query vector per lane column, so the
 //     online-softmax row reductions stay in-lane plus one cross-half shuffle, and the probabilities
 //     feed O^T = V^T P^T directly from registers (keys permuted consistently on both operands).
-//   * The query operand comes pre-rotated, pre-scaled by log2(e)/sqrt(d) and rounded once to fp16
-//     (an 11-bit significand: the logits move by ~1e-4 relative, where one bf16 rounding would move
-//     them by ~1e-3 and dominate the output error); each wave reads it as consecutive 1 KB blocks.
-//     Keys enter LDS as fp16, which holds every bf16 key of magnitude 2^-14 .. 65504 exactly (smaller
-//     ones keep an absolute error below 2^-25; larger ones are outside the supported range), so S
-//     takes one fp16 product per key where a bf16 hi/lo query would take two.
-//   * 64-key tiles of K (row-major, padded) and V (transposed on the way into LDS) are shared by
-//     the four waves; float32 accumulation, exp2 in the log2 domain against a lazily moved
-//     reference maximum; each 32-key half is one online-softmax step. Work groups are numbered with
-//     the group index fastest, so all work of one KV head lands on one XCD (work groups are dealt
-//     round-robin over the 8 XCDs) and its K/V stay in that XCD's L2.
+//   * Operands of S are fp16: the query comes pre-rotated, pre-scaled by log2(e)/sqrt(d) and rounded
+//     once to fp16 (an 11-bit significand: the logits move by ~1e-4 relative, where one bf16
+//     rounding would move them by ~1e-3 and dominate the output error), the keys come from the fp16
+//     copy that the kernels writing the fused keys keep beside them (every bf16 key of magnitude
+//     2^-14 .. 65504 is exact in fp16). Keys or scaled queries beyond fp16's range flag their group,
+//     and the merge kernel recomputes that group exactly in float32 from the bf16 inputs.
+//   * The S accumulator starts at minus the softmax reference, so the products come out already
+//     relative to it. The reference is the maximum of a segment's first 32 keys; later keys are
+//     exponentiated against it directly, and only when a 32-key block's probability sum exceeds
+//     2^kLazyMax (some logit more than kLazyMax above the reference) does the reference move, with
+//     the accumulator rescaled: no per-block maximum or subtraction in the common case.
+//   * 64-key tiles: K row-major (fp16, padded rows) and V transposed on its way into LDS with the key
+//     order of the probabilities (bits 2 and 3 of the key index swapped), so each P V operand is one
+//     16-byte LDS read; both double-buffered, one barrier per tile, the next tile's rows loaded into
+//     registers a tile ahead. Work groups are numbered with the group index fastest, so all work of
+//     one KV head lands on one XCD (work groups are dealt round-robin over the 8 XCDs) and its K/V
+//     stay in that XCD's L2.
 // f32 path: plain float32 arithmetic, one block per (row, KV head), exact online softmax.
 #include <float.h>
 
@@ -47,20 +53,28 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLazyMax = 8.f;   // log2 headroom of the attention softmax reference
+constexpr float kLazyMax = 16.f;       // log2 headroom of the attention softmax reference
+constexpr float kSumCap = 65536.f;     // 2^kLazyMax: a 32-key block sum above it moves the reference
 
 struct AttnArgs {
   const uint16_t* qop;
   const int* row_pos;
-  const uint16_t* kf;
+  const uint16_t* kh;     // fp16 copy of the fused keys
+  const uint16_t* kf;     // bf16 fused keys (exact recomputation of flagged groups)
   const uint16_t* vf;
   uint16_t* out;
   float* lse;
   int* tilecum;
   uint16_t* part_o;   // fp16, scaled per vector
   float4* part_ml;    // (max, sum, scale, 0) per vector
+  const uint16_t* qx;       // fresh queries before rotation (exact recomputation)
+  const unsigned* flags;    // [n_groups]: call_id where an fp16 operand overflowed
+  int* fallback;            // optional [n_groups] report
+  unsigned call_id;
+  int q_rows, q_indexed;
   int n_req, Hq, Hkv, g, R, L;
   int n_groups, n_tiles, qop_blocks, pieces;
+  Theta th;
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -69,16 +83,34 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
-// the same in one instruction (gfx950's packed conversion; low half from the first operand)
-__device__ __forceinline__ uint32_t cvt_pk_h2(float lo, float hi) {
-  uint32_t r;
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
-}
 __device__ __forceinline__ float h2f(uint32_t h16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h16); }
 
 __device__ __forceinline__ int64_t part_index(const AttnArgs& a, int group, int piece, int slot) {
   return ((int64_t)(group * a.pieces + piece) * 2 + slot) * 128;
+}
+
+// Position of tile-local key k in the transposed V tile: bits 2 and 3 swapped, which lists each
+// lane's eight probabilities of a 16-key step (keys 8s' + 4hh + e, s' and e free) contiguously.
+__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// Probabilities of one 32-key half against the current reference (x already relative to it): bf16
+// operands of the P V products and their sum (the same rounded values, one v_dot2c_f32_bf16 per
+// pair, so the output weights stay a convex combination).
+__device__ __forceinline__ void probs(const f32x16& x, u32x4* pw, float& lsum) {
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // (the pair is taken from a scalar word: a bit cast of a vector element picked the wrong
+      // element here)
+      const uint32_t pk = pack_bf2(fast_exp2(x[8 * mp + 2 * k]), fast_exp2(x[8 * mp + 2 * k + 1]));
+      pw[mp][k] = pk;
+      if (k & 1) s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, s1, false);
+      else s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, s0, false);
+    }
+  lsum = s0 + s1;
 }
 
 template <int D>
@@ -87,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int NDT = D / 32;   // 32-row d tiles of O^T
   constexpr int KT = 64;        // keys per LDS tile (one unit)
   constexpr int KST = D + 8;    // K row stride in LDS (elements): conflict-free 16-byte reads
-  constexpr int VST = KT + 4;   // V^T row stride in LDS (elements): conflict-free 8-byte reads
+  constexpr int VST = KT + 8;   // V^T row stride in LDS (elements): conflict-free 16-byte reads
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KST];   // double-buffered tiles
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VST];
   __shared__ int cum[kAttnMaxTiles + 1];
@@ -143,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   }
 
   // uniform base of this (request, KV head); per-thread byte offsets fit 32 bits (checked by the host)
-  const char* kbase = reinterpret_cast<const char*>(a.kf + ((int64_t)req * a.L * a.Hkv + kvh) * D);
+  const char* kbase = reinterpret_cast<const char*>(a.kh + ((int64_t)req * a.L * a.Hkv + kvh) * D);
   const char* vbase = reinterpret_cast<const char*>(a.vf + ((int64_t)req * a.L * a.Hkv + kvh) * D);
   const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
   // Tile loads. K: 16-byte chunks, dims fastest (coalesced rows). V: each task holds 4 keys x 8
@@ -210,31 +242,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     f32x16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
-    float m_run = -INFINITY, m_ref = 0.f, l_run = 0.f;  // running max, softmax reference, sum
+    float m_ref = 0.f, l_run = 0.f;   // softmax reference (log2 domain) and running sum
+    f32x16 negm = {};                 // -m_ref in every element: the S accumulator's start value
+    bool first = true;                // wave-uniform: the segment's first half sets the reference
 
     // K row-major; V transposed on the way in (word pp of a task: dims 8c+2pp in the low half
-    // and 8c+2pp+1 in the high half, four keys each)
+    // and 8c+2pp+1 in the high half, four keys each, at the keys' permuted position)
+    const int vpos = vt_pos(4 * vkq);
     auto store_tile = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < NKL; ++i) {
         const int uu = threadIdx.x + 256 * i;
-        // keys go into LDS as fp16: every bf16 value of magnitude 2^-14 .. 65504 converts exactly
-        u32x4 kh;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          kh[w] = cvt_pk_h2(__builtin_bit_cast(float, kr[i][w] << 16), __builtin_bit_cast(float, kr[i][w] & 0xffff0000u));
-        *reinterpret_cast<u32x4*>(&Ks[buf][(uu / (D / 8)) * KST + 8 * (uu % (D / 8))]) = kh;
+        *reinterpret_cast<u32x4*>(&Ks[buf][(uu / (D / 8)) * KST + 8 * (uu % (D / 8))]) = kr[i];
       }
       if (vtask) {
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
           u32x2 lo, hi;
-          lo[0] = (vr[0][pp] & 0xffffu) | (vr[1][pp] << 16);
-          lo[1] = (vr[2][pp] & 0xffffu) | (vr[3][pp] << 16);
-          hi[0] = (vr[0][pp] >> 16) | (vr[1][pp] & 0xffff0000u);
-          hi[1] = (vr[2][pp] >> 16) | (vr[3][pp] & 0xffff0000u);
-          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp) * VST + 4 * vkq]) = lo;
-          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp + 1) * VST + 4 * vkq]) = hi;
+          lo[0] = __builtin_amdgcn_perm(vr[1][pp], vr[0][pp], 0x05040100u);
+          lo[1] = __builtin_amdgcn_perm(vr[3][pp], vr[2][pp], 0x05040100u);
+          hi[0] = __builtin_amdgcn_perm(vr[1][pp], vr[0][pp], 0x07060302u);
+          hi[1] = __builtin_amdgcn_perm(vr[3][pp], vr[2][pp], 0x07060302u);
+          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp) * VST + vpos]) = lo;
+          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp + 1) * VST + vpos]) = hi;
         }
       }
     };
@@ -249,23 +279,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       const uint16_t* Kc = Ks[cur];
       const uint16_t* Vc = Vt[cur];
 
-      // S^T[key][q] for the two 32-key halves. The halves then go through softmax and P V one
-      // after the other (an online-softmax step each), so the second half's products are still
-      // running while the first half's softmax is formed.
+      // S^T[key][q] - m_ref for the two 32-key halves. The halves then go through softmax and P V
+      // one after the other, so the second half's products are still running while the first
+      // half's probabilities are formed.
       f32x16 sc[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        sc[st] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           const f16x8 ka = __builtin_bit_cast(
               f16x8, *reinterpret_cast<const u32x4*>(Kc + (32 * st + l32) * KST + 16 * ks + 8 * hh));
-          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, q16[ks], sc[st], 0, 0, 0);
+          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, q16[ks], ks == 0 ? negm : sc[st], 0, 0, 0);
         }
       }
+      // both halves' products started from the reference of the tile's start; when the first half
+      // moves it (the segment's first half, or a rescale), the second half follows by the difference
+      const float m_tile = m_ref;
+      bool moved = false;   // wave-uniform
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x16 x = sc[st];
+        if (moved) {
+          const float dm = m_tile - m_ref;
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) x[rr] += dm;
+        }
         // causal mask by absolute position where the half reaches past the wave's smallest position
         // or the range's end: element rr holds key kt0 + 32 st + 4 hh + (8 (rr / 4) + rr % 4)
         const int klast = kt0 + 32 * st + 31;
@@ -275,55 +313,56 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           for (int rr = 0; rr < 16; ++rr)
             if (8 * (rr >> 2) + (rr & 3) > lim) x[rr] = -INFINITY;
         }
-        // online softmax in the log2 domain against a lazily moved reference m_ref (0 before any
-        // key): the reference follows a lane's maximum only once a logit exceeds it by more than
-        // kLazyMax, so probabilities stay below 2^kLazyMax and the accumulator is rescaled rarely
-        float mt = -INFINITY;
+        if (first) {   // the segment's first half: its maximum becomes the reference (x was the logit)
+          float mt = -INFINITY;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
-        mt = half_max(mt);
-        const bool upd = mt - m_ref > (m_run == -INFINITY ? -INFINITY : kLazyMax);
-        if (__any(upd)) {
-          const float m_new = upd ? mt : m_run;
-          const float r_new = m_new == -INFINITY ? 0.f : m_new;
-          const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_ref - r_new);
+          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
+          mt = half_max(mt);
+          const float r0 = mt == -INFINITY ? 0.f : mt;   // no visible key in the segment: stays 0
+          m_ref = r0;
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            x[rr] -= r0;
+            negm[rr] = -r0;
+          }
+          first = false;
+          moved = true;
+        }
+        u32x4 pw[2];
+        float lsum;
+        probs(x, pw, lsum);
+        if (__any(lsum > kSumCap)) {   // a logit more than kLazyMax above the reference: move it
+          float mt = -INFINITY;
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
+          mt = half_max(mt);
+          const float sh = mt > 0.f ? mt : 0.f;
+          const float alpha = fast_exp2(-sh);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
           l_run *= alpha;
-          m_run = m_new;
-          m_ref = r_new;
-        }
+          m_ref += sh;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) x[rr] = fast_exp2(x[rr] - m_ref);
+          for (int rr = 0; rr < 16; ++rr) {
+            x[rr] -= sh;
+            negm[rr] = -m_ref;
+          }
+          moved = true;
+          probs(x, pw, lsum);
+        }
+        l_run += lsum;
 
-        // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4
-        // the sum takes the same bf16-rounded probabilities the products use, so the output
-        // weights stay a convex combination
-        // (a bf16 pair dotted with (1, 1): one v_dot2c_f32_bf16 per pair)
-        const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-        float lsum = 0.f;
+        // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4,
+        // stored at V^T position 32st + 16mp + 8hh + s
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
-          u32x4 pw;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            // (the pair is taken from a scalar word: a bit cast of a vector element picked the
-            // wrong element here)
-            const uint32_t pk = pack_bf2(x[8 * mp + 2 * k], x[8 * mp + 2 * k + 1]);
-            pw[k] = pk;
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, lsum, false);
-          }
-          const bf16x8 pb = as_bf16x8(pw);
+          const bf16x8 pb = as_bf16x8(pw[mp]);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const uint16_t* vrow = Vc + (32 * dt + l32) * VST + 32 * st + 16 * mp + 4 * hh;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-            const u32x4 vw = {lo[0], lo[1], hi[0], hi[1]};
+            const u32x4 vw = *reinterpret_cast<const u32x4*>(Vc + (32 * dt + l32) * VST + 32 * st + 16 * mp + 8 * hh);
             o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pb, o[dt], 0, 0, 0);
           }
         }
-        l_run += lsum;
       }
 
       if (kt0 + KT < kend) {
@@ -389,8 +428,60 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   }
 }
 
+// Exact float32 attention of one query vector per 32 threads (4 dims each), for a group whose fp16
+// operands overflowed: the fresh query rotated at p with float64 angles, logits over the bf16 keys
+// j <= p summed across the vector's threads, an online softmax with the exact running maximum, and
+// the bf16 values; out and lse as the fast path writes them.
+template <int D>
+__device__ void exact_vector(const AttnArgs& a, int req, int kvh, int v) {
+  constexpr int TPV = D / 4;
+  const int dc = threadIdx.x % TPV;
+  const int r = v / a.g, hq = kvh * a.g + v % a.g;
+  const int p0 = a.row_pos[(int64_t)req * a.R + r];
+  if (p0 < 0) return;   // rows outside the cache are skipped, as by the fast path
+  const int p = min(p0, a.L - 1);
+  const int srow = a.q_indexed ? p : r;
+  const uint16_t* qrow = a.qx + (((int64_t)req * a.q_rows + srow) * a.Hq + hq) * D;
+  const float scale = 1.f / sqrtf((float)D);
+  float qv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * dc + k, i0 = i % (D / 2);
+    const float x = bf2f(qrow[i0]), y = bf2f(qrow[i0 + D / 2]);
+    const float2 c = rope_cs((double)p, a.th.v[i0]);
+    qv[k] = (i < D / 2 ? x * c.x - y * c.y : x * c.y + y * c.x) * scale;
+  }
+  float m = -INFINITY, l = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* kcol = a.kf + ((int64_t)req * a.L * a.Hkv + kvh) * D + 4 * dc;
+  const uint16_t* vcol = a.vf + ((int64_t)req * a.L * a.Hkv + kvh) * D + 4 * dc;
+  const int64_t stride = (int64_t)a.Hkv * D;
+  for (int j = 0; j <= p; ++j) {
+    const u32x2 kw = *reinterpret_cast<const u32x2*>(kcol + j * stride);
+    float x = qv[0] * bf2f(kw[0] & 0xffffu) + qv[1] * bf2f(kw[0] >> 16) + qv[2] * bf2f(kw[1] & 0xffffu) +
+              qv[3] * bf2f(kw[1] >> 16);
+#pragma unroll
+    for (int msk = TPV / 2; msk >= 1; msk >>= 1) x += __shfl_xor(x, msk, TPV);
+    const float mn = fmaxf(m, x);
+    const float c = m == -INFINITY ? 0.f : expf(m - mn), e = expf(x - mn);
+    const u32x2 vw = *reinterpret_cast<const u32x2*>(vcol + j * stride);
+    l = l * c + e;
+    o[0] = o[0] * c + e * bf2f(vw[0] & 0xffffu);
+    o[1] = o[1] * c + e * bf2f(vw[0] >> 16);
+    o[2] = o[2] * c + e * bf2f(vw[1] & 0xffffu);
+    o[3] = o[3] * c + e * bf2f(vw[1] >> 16);
+    m = mn;
+  }
+  const float inv = 1.f / l;
+  u32x2 w;
+  w[0] = pack_bf2(o[0] * inv, o[1] * inv);
+  w[1] = pack_bf2(o[2] * inv, o[3] * inv);
+  *reinterpret_cast<u32x2*>(a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 4 * dc) = w;
+  if (dc == 0 && a.lse) a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = m + logf(l);
+}
+
 // Merge the pieces of every cut tile in key order. One thread per (query vector, 4 dims); the
-// pieces' loads go out in independent batches of eight.
+// pieces' loads go out in independent batches of eight. A group whose fp16 operands overflowed is
+// recomputed exactly here instead (every tile of it, cut or not).
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   constexpr int TPV = D / 4;                 // threads per query vector
@@ -402,14 +493,22 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int req = group / a.Hkv, kvh = group % a.Hkv;
   const int nt = a.n_tiles;
   const int* cum = a.tilecum + (int64_t)req * (nt + 1);
-  // the tile's unit range and the request's total as one batch of loads
+  // the tile's unit range, the request's total and the group's flag as one batch of loads
   int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt], pieces = a.pieces;
-  asm volatile("" : "+s"(c0), "+s"(c1), "+s"(U), "+s"(pieces) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
+  unsigned fl = a.flags[group];
+  asm volatile("" : "+s"(c0), "+s"(c1), "+s"(U), "+s"(pieces), "+s"(fl) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
+  const bool exact = fl == a.call_id;
+  if (tile == 0 && slab == 0 && threadIdx.x == 0 && a.fallback) a.fallback[group] = exact ? 1 : 0;
+  const int g = a.g, Mv = a.R * g;
+  if (exact) {
+    const int v = tile * 128 + slab * VPB + (int)threadIdx.x / TPV;
+    if (v < Mv) exact_vector<D>(a, req, kvh, v);
+    return;
+  }
   if (c1 <= c0) return;
   const int P = attn_pieces_used(U, pieces);
   const int i0 = attn_piece_of(U, P, c0), i1 = attn_piece_of(U, P, c1 - 1);
   if (i0 == i1) return;  // written directly by its only piece
-  const int g = a.g, Mv = a.R * g;
   const int ql = slab * VPB + threadIdx.x / TPV, dc = threadIdx.x % TPV;
   const int v = tile * 128 + ql;
   if (v >= Mv) return;
@@ -572,13 +671,18 @@ __global__ __launch_bounds__(256) void k_attn_f32(int Hq, int Hkv, int R, int L,
 }  // namespace
 
 hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,
-                            int qop_blocks, const int* row_pos, const uint16_t* kf,
+                            int qop_blocks, const int* row_pos, const uint16_t* kh, const uint16_t* kf,
                             const uint16_t* vf, uint16_t* out, float* lse, int pieces,
-                            int* tilecum, uint16_t* part_o, float4* part_ml, hipStream_t st) {
+                            int* tilecum, uint16_t* part_o, float4* part_ml, const AttnExact& ex,
+                            hipStream_t st) {
   if (R == 0 || n_req == 0) return hipSuccess;
+  if (!ex.flags || !ex.q) return hipErrorInvalidValue;
   AttnArgs a;
-  a.qop = qop; a.row_pos = row_pos; a.kf = kf; a.vf = vf; a.out = out; a.lse = lse;
+  a.qop = qop; a.row_pos = row_pos; a.kh = kh; a.kf = kf; a.vf = vf; a.out = out; a.lse = lse;
   a.tilecum = tilecum; a.part_o = part_o; a.part_ml = part_ml;
+  a.qx = ex.q; a.flags = ex.flags; a.fallback = ex.fallback; a.call_id = ex.call_id;
+  a.q_rows = ex.q_rows; a.q_indexed = ex.indexed;
+  a.th = make_theta(D, ex.base);
   a.n_req = n_req; a.Hq = Hq; a.Hkv = Hkv; a.g = Hq / Hkv; a.R = R; a.L = L;
   a.n_groups = n_req * Hkv;
   a.n_tiles = (R * a.g + 127) / 128;

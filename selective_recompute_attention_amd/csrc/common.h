@@ -160,6 +160,30 @@ __device__ __forceinline__ float2 rope_cs(double pos, double theta) {
   return make_float2((float)c, (float)s);
 }
 
+// fp16 copy of the fused keys for the attention's query-key products (bf16 storage only). Kernels that
+// write fused K rows (re-rotation, scatter, the attention entry's conversion) also write each row's
+// fp16 value to kh (same [n_req][L][Hkv][d] layout); a bf16 key of magnitude above 65504 has no fp16
+// value, so its writer sets flags[req * Hkv + kv_head] = call_id, and so does the scatter for a scaled
+// query beyond fp16. The attention recomputes a flagged (request, KV head) group exactly in float32.
+// call_id differs between calls, so stale flags of another call never match (a graph replay reuses its
+// call's id: a flag it left makes a later replay recompute that group too, which is still exact).
+struct F16Shadow {
+  uint16_t* kh = nullptr;
+  unsigned* flags = nullptr;
+  unsigned call_id = 0;
+};
+// fp16 of the two bf16 values of word w (exact for magnitudes 2^-14 .. 65504; beyond 65504 infinity),
+// with the larger magnitude of the two folded into amax.
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t w, float& amax) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+  amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Largest finite fp16 magnitude; values at or above 65520 round to infinity.
+constexpr float kF16Max = 65504.f;
+
 // Prepared query operand of the bf16 attention (written by the row kernel, read by the attention).
 // Query vectors of one (request, KV head) group are numbered v = r * g + (h % g) and cut into
 // blocks of 32. For block b, 16-dimension step ks and plane (0: hi = bf16(x), 1: lo = bf16(x - hi))
@@ -195,7 +219,11 @@ __host__ __device__ __forceinline__ int attn_piece_of(int U, int P, int u) {
 namespace sra {
 hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
                            const void* ks, const void* vs, void* kf, void* vf, int64_t L,
-                           double base, hipStream_t st);
+                           double base, hipStream_t st, const F16Shadow& sh = F16Shadow());
+// fp16 copy of n_rows fused K rows of every request ([n_req][L][Hkv][D] bf16 -> sh.kh), with the
+// overflow flags of sh.
+hipError_t launch_k_to_f16(int D, int Hkv, int n_req, int L, const uint16_t* kf, const F16Shadow& sh,
+                           hipStream_t st);
 // Per recomputed row (row_pos[r] = p in [0, L); row_pos NULL: p = r): the row's cos/sin table (cs_out, optional), the
 // fresh K/V scatter (kn/vn optional) and, for bf16, the attention's prepared query operand (qn/qop
 // optional; rows outside [0, L) get zeros). Fresh rows are compact (row r) or, when indexed,
@@ -204,7 +232,7 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
                           const void* qn, const void* kn, const void* vn, int fresh_rows,
                           int indexed, const int* row_pos, void* kf, void* vf, float2* cs_out,
                           uint16_t* qop, int qop_blocks, bool q16, float scale_log2, double base,
-                          hipStream_t st);
+                          hipStream_t st, const F16Shadow& sh = F16Shadow());
 hipError_t launch_rope_table(int D, int n_req, int R, const int* row_pos, float2* cs_out,
                              double base, hipStream_t st);
 // Anchor probe prefix rows [0, n_chunks * k) of [n_req][Lp][Hkv][D] probe caches; tab entries
@@ -271,6 +299,7 @@ struct RerotFused {
   uint16_t* vf = nullptr;
   int64_t L = 0;
   double base = 0.0;
+  F16Shadow sh;   // optional fp16 copy of the re-rotated keys
 };
 hipError_t launch_score_pass(int pass, int D, const ChunkTab& tab, const int* req_blk0, int n_req,
                              int Hkv, int Mpad, int Mvalid, int Lctx, const void* kc,
@@ -291,13 +320,25 @@ hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, f
 hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
                          int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
                          const int* map = nullptr, int map_stride = 0);
-// qop: prepared query operand (qop_blocks blocks of 32 vectors per group); tilecum: [n_req][tiles+1]
-// ints; part_o ([..][D] fp16, scaled) / part_ml ((max, sum, scale, 0)): [n_groups][pieces][2][128]
-// partial results.
+// qop: prepared query operand (qop_blocks blocks of 32 vectors per group); kh: fp16 copy of the fused
+// keys; tilecum: [n_req][tiles+1] ints; part_o ([..][D] fp16, scaled) / part_ml ((max, sum, scale, 0)):
+// [n_groups][pieces][2][128] partial results. Groups whose flag equals call_id are recomputed exactly
+// from the fresh queries q ([n_req][q_rows][Hq][D] before rotation, row p when indexed, else row r)
+// and the bf16 K/V; fallback (optional, [n_req][Hkv]) receives 1 for those groups and 0 for the rest.
+struct AttnExact {
+  const uint16_t* q = nullptr;
+  int q_rows = 0;
+  int indexed = 0;
+  const unsigned* flags = nullptr;
+  unsigned call_id = 0;
+  int* fallback = nullptr;
+  double base = 10000.0;
+};
 hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, const uint16_t* qop,
-                            int qop_blocks, const int* row_pos, const uint16_t* kf,
+                            int qop_blocks, const int* row_pos, const uint16_t* kh, const uint16_t* kf,
                             const uint16_t* vf, uint16_t* out, float* lse, int pieces,
-                            int* tilecum, uint16_t* part_o, float4* part_ml, hipStream_t st);
+                            int* tilecum, uint16_t* part_o, float4* part_ml, const AttnExact& ex,
+                            hipStream_t st);
 hipError_t launch_attn_f32(int D, int n_req, int Hq, int Hkv, int R, int L, const float* q,
                            int q_rows, int indexed, const int* row_pos, const float2* cs,
                            const float* kf, const float* vf, float* out, float* lse,

@@ -53,12 +53,14 @@ struct Vec<float> {
 // angles are formed, so the memory latency overlaps the float64 sin/cos; V is stored as is and K
 // rotated, its bits kept when delta = 0. cs is LDS scratch of d/2 float2. UV and UK are a thread's
 // V chunks and K pair units per batch: small where many blocks share a CU, large where one block
-// has a CU (more bytes in flight per round trip).
+// has a CU (more bytes in flight per round trip). With sh.kh set (bf16 storage), every stored K vector
+// is also written as fp16 to the same place of sh.kh, and a key beyond fp16's range flags its
+// (request, KV head).
 template <typename T, int D, int UV = 4, int UK = 2>
 __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr, int Hkv,
                                      const T* __restrict__ ks, const T* __restrict__ vs,
                                      T* __restrict__ kf, T* __restrict__ vf, int64_t L,
-                                     const Theta& th, float2* cs) {
+                                     const Theta& th, float2* cs, const F16Shadow& sh = F16Shadow()) {
   constexpr int H = D / 2;
   constexpr int VW = Vec<T>::N;
   constexpr int UPH = H / VW;   // K pair units per head
@@ -103,11 +105,10 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
       const int64_t u = bk + threadIdx.x + 256 * i;
       if (u >= nK) continue;
       const int i0 = (int)(u % UPH) * VW;
-      T* o = kf + dst0 + (u / UPH) * D + i0;
-      if (delta == 0) {   // rotation by zero is the identity: keep the cached bits
-        *reinterpret_cast<v4u*>(o) = ka[i];
-        *reinterpret_cast<v4u*>(o + H) = kb[i];
-      } else {
+      const int64_t off = dst0 + (u / UPH) * D + i0;
+      T* o = kf + off;
+      v4u wa = ka[i], wb = kb[i];
+      if (delta != 0) {   // rotation by zero is the identity: keep the cached bits
         float fa[VW], fb[VW], ra[VW], rb[VW];
         Vec<T>::unpack(ka[i], fa);
         Vec<T>::unpack(kb[i], fb);
@@ -117,8 +118,24 @@ __device__ __forceinline__ void rows(const ChunkTab& tab, int e, int t0, int nr,
           ra[k] = fa[k] * c - fb[k] * sn;
           rb[k] = fa[k] * sn + fb[k] * c;
         }
-        *reinterpret_cast<v4u*>(o) = Vec<T>::pack(ra);
-        *reinterpret_cast<v4u*>(o + H) = Vec<T>::pack(rb);
+        wa = Vec<T>::pack(ra);
+        wb = Vec<T>::pack(rb);
+      }
+      *reinterpret_cast<v4u*>(o) = wa;
+      *reinterpret_cast<v4u*>(o + H) = wb;
+      if constexpr (sizeof(T) == 2) {
+        if (sh.kh) {
+          float amax = 0.f;
+          v4u ha, hb;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ha[k] = bf2_to_h2(wa[k], amax);
+            hb[k] = bf2_to_h2(wb[k], amax);
+          }
+          *reinterpret_cast<v4u*>(sh.kh + off) = ha;
+          *reinterpret_cast<v4u*>(sh.kh + off + H) = hb;
+          if (amax > kF16Max) sh.flags[(int64_t)tab.req[e] * Hkv + (int)(u / UPH) % Hkv] = sh.call_id;
+        }
       }
     }
   };

@@ -7,6 +7,8 @@
 //
 // Both are pure HBM streams: every thread moves 16-byte vectors, rows are contiguous, angles are
 // formed once per block in float64 and kept in LDS as float32 cos/sin.
+#include <algorithm>
+
 #include "common.h"
 #include "rerotate.h"
 
@@ -22,19 +24,43 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_rerotate(ChunkTab tab, int Hkv, int rows_per_blk,
                                                   const T* __restrict__ ks,
                                                   const T* __restrict__ vs, T* __restrict__ kf,
-                                                  T* __restrict__ vf, int64_t L, Theta th) {
+                                                  T* __restrict__ vf, int64_t L, Theta th, F16Shadow sh) {
   __shared__ float2 cs[D / 2];
   const int e = find_entry(tab, blockIdx.x);
   const int t0 = (blockIdx.x - tab.blk0[e]) * rows_per_blk;
-  rerot::rows<T, D>(tab, e, t0, min(rows_per_blk, tab.len[e] - t0), Hkv, ks, vs, kf, vf, L, th, cs);
+  rerot::rows<T, D>(tab, e, t0, min(rows_per_blk, tab.len[e] - t0), Hkv, ks, vs, kf, vf, L, th, cs, sh);
+}
+
+// fp16 copy of fused bf16 keys for the attention (the standalone attention entry, whose keys come from
+// the caller): n16 16-byte vectors of [n_req][L][Hkv][D], grid-stride; a key beyond fp16's range flags
+// its (request, KV head).
+template <int D>
+__global__ __launch_bounds__(256) void k_to_f16(int64_t n16, int Hkv, int64_t L, const uint16_t* __restrict__ kf,
+                                                F16Shadow sh) {
+  constexpr int VPH = D / 8;   // 16-byte vectors per head row
+  const u32x4* src = reinterpret_cast<const u32x4*>(kf);
+  u32x4* dst = reinterpret_cast<u32x4*>(sh.kh);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const u32x4 w = src[i];
+    float amax = 0.f;
+    u32x4 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h[k] = bf2_to_h2(w[k], amax);
+    dst[i] = h;
+    if (amax > kF16Max) {
+      const int64_t head_row = i / VPH;   // (req, position, KV head)
+      sh.flags[(head_row / (L * Hkv)) * Hkv + head_row % Hkv] = sh.call_id;
+    }
+  }
 }
 
 // One block per (recomputed row r, request) at position p = row_pos[r]: forms the row's angles
 // once, then (each part optional) writes them out, scatters the fresh K/V row to fused row p with
-// K rotated at p, and writes the attention's query operand: every query head rotated at p, scaled
+// K rotated at p (and, with sh.kh, the stored key's fp16 copy for the attention, flagging a key
+// beyond fp16's range), and writes the attention's query operand: every query head rotated at p, scaled
 // by log2(e)/sqrt(d) and either split into bf16 hi/lo planes (Q16 false: the statistics' exact
 // products) or rounded once to fp16 in plane 0 (Q16 true: the attention's operand), in the
-// matrix-operand order of qop_index.
+// matrix-operand order of qop_index (a scaled query beyond fp16's range flags its group).
 // Fresh rows are compact (row r) or position-indexed (row p). Rows outside [0, L) write nothing
 // but zero query operands. The first batch of every part is loaded before the angles are formed.
 // FULL: kn and qop are both set (bf16), so every first-batch load is unconditional and the
@@ -46,7 +72,7 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
                                                  int indexed, const int* __restrict__ row_pos,
                                                  T* __restrict__ kf, T* __restrict__ vf,
                                                  float2* __restrict__ cs_out, uint16_t* __restrict__ qop,
-                                                 int qop_blocks, float scale_log2, Theta th) {
+                                                 int qop_blocks, float scale_log2, Theta th, F16Shadow sh) {
   constexpr int H = D / 2;
   constexpr int NKS = D / 16;
   constexpr int VW = Vec<T>::N;
@@ -113,8 +139,24 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
       ra[k] = fa[k] * c - fb[k] * sn;
       rb[k] = fa[k] * sn + fb[k] * c;
     }
-    *reinterpret_cast<u32x4*>(o) = Vec<T>::pack(ra);
-    *reinterpret_cast<u32x4*>(o + H) = Vec<T>::pack(rb);
+    const u32x4 wa = Vec<T>::pack(ra), wb = Vec<T>::pack(rb);
+    *reinterpret_cast<u32x4*>(o) = wa;
+    *reinterpret_cast<u32x4*>(o + H) = wb;
+    if constexpr (sizeof(T) == 2) {
+      if (sh.kh) {   // the attention's fp16 copy of the stored key
+        float amax = 0.f;
+        u32x4 ha, hb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ha[k] = bf2_to_h2(wa[k], amax);
+          hb[k] = bf2_to_h2(wb[k], amax);
+        }
+        uint16_t* oh = sh.kh + (o - kf);
+        *reinterpret_cast<u32x4*>(oh) = ha;
+        *reinterpret_cast<u32x4*>(oh + H) = hb;
+        if (amax > kF16Max) sh.flags[(int64_t)q * Hkv + u / UPH] = sh.call_id;
+      }
+    }
   };
   if (do_kv) {
     u32x4* vdst = reinterpret_cast<u32x4*>(vf + dst0);
@@ -156,11 +198,16 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
           const int kss = ks + half * (NKS / 2);
           if constexpr (Q16) {
             u32x4 wq;
+            float amax = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < 4; ++k) {
+              amax = fmaxf(amax, fmaxf(fabsf(f[2 * k]), fabsf(f[2 * k + 1])));
               wq[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * k]) |
                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f[2 * k + 1]) << 16);
+            }
             *reinterpret_cast<u32x4*>(qop + qop_index(grp, v >> 5, kss, 0, v & 31, hh, qop_blocks, NKS)) = wq;
+            // a scaled query at or beyond 65520 has no fp16 value (65504 < x < 65520 rounds to 65504)
+            if (sh.flags && amax >= 65520.f) sh.flags[grp] = sh.call_id;
           } else {
             u32x4 wh, wl;
 #pragma unroll
@@ -360,23 +407,33 @@ __global__ void k_check_rows(const int* __restrict__ row_pos, int n_req, int R, 
 
 hipError_t launch_rerotate(int dtype, int D, int Hkv, const ChunkTab& tab, int rows_per_blk,
                            const void* ks, const void* vs, void* kf, void* vf, int64_t L,
-                           double base, hipStream_t st) {
+                           double base, hipStream_t st, const F16Shadow& sh) {
   const int nblk = tab.blk0[tab.n];
   if (nblk == 0) return hipSuccess;
   dim3 g(nblk), b(256);
   const Theta th = make_theta(D, base);
   if (dtype == 0 && D == 128)
     k_rerotate<uint16_t, 128><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const uint16_t*)ks,
-                                                (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, th);
+                                                (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, th, sh);
   else if (dtype == 0 && D == 64)
     k_rerotate<uint16_t, 64><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const uint16_t*)ks,
-                                               (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, th);
+                                               (const uint16_t*)vs, (uint16_t*)kf, (uint16_t*)vf, L, th, sh);
   else if (dtype == 1 && D == 128)
     k_rerotate<float, 128><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const float*)ks,
-                                             (const float*)vs, (float*)kf, (float*)vf, L, th);
+                                             (const float*)vs, (float*)kf, (float*)vf, L, th, F16Shadow());
   else
     k_rerotate<float, 64><<<g, b, 0, st>>>(tab, Hkv, rows_per_blk, (const float*)ks,
-                                            (const float*)vs, (float*)kf, (float*)vf, L, th);
+                                            (const float*)vs, (float*)kf, (float*)vf, L, th, F16Shadow());
+  return hipGetLastError();
+}
+
+hipError_t launch_k_to_f16(int D, int Hkv, int n_req, int L, const uint16_t* kf, const F16Shadow& sh,
+                           hipStream_t st) {
+  const int64_t n16 = (int64_t)n_req * L * Hkv * D / 8;
+  if (n16 == 0) return hipSuccess;
+  const unsigned nblk = (unsigned)std::min<int64_t>((n16 + 255) / 256, 4096);
+  if (D == 128) k_to_f16<128><<<dim3(nblk), dim3(256), 0, st>>>(n16, Hkv, L, kf, sh);
+  else k_to_f16<64><<<dim3(nblk), dim3(256), 0, st>>>(n16, Hkv, L, kf, sh);
   return hipGetLastError();
 }
 
@@ -384,19 +441,22 @@ hipError_t launch_scatter(int dtype, int D, int Hq, int Hkv, int n_req, int R, i
                           const void* qn, const void* kn, const void* vn, int fresh_rows,
                           int indexed, const int* row_pos, void* kf, void* vf, float2* cs_out,
                           uint16_t* qop, int qop_blocks, bool q16, float scale_log2, double base,
-                          hipStream_t st) {
+                          hipStream_t st, const F16Shadow& sh) {
   if (R == 0 || n_req == 0) return hipSuccess;
   dim3 g(R, n_req), b(128);
   const Theta th = make_theta(D, base);
 #define SRA_SCATTER(TT, DD, FF, QQ)                                                                     \
   k_scatter<TT, DD, FF, QQ><<<g, b, 0, st>>>(Hq, Hkv, R, L, (const TT*)qn, (const TT*)kn, (const TT*)vn,       \
                                          fresh_rows, indexed, row_pos, (TT*)kf, (TT*)vf, cs_out,         \
-                                         dtype == 0 ? qop : nullptr, qop_blocks, scale_log2, th)
+                                         dtype == 0 ? qop : nullptr, qop_blocks, scale_log2, th,       \
+                                         dtype == 0 ? sh : F16Shadow())
   const bool full = dtype == 0 && kn && qop;
-  if (dtype == 0 && D == 128 && full) SRA_SCATTER(uint16_t, 128, true, true);   // fused layer
+  if (dtype == 0 && D == 128 && full && q16) SRA_SCATTER(uint16_t, 128, true, true);   // fused layer
+  else if (dtype == 0 && D == 128 && full) SRA_SCATTER(uint16_t, 128, true, false);
   else if (dtype == 0 && D == 128 && q16) SRA_SCATTER(uint16_t, 128, false, true);
   else if (dtype == 0 && D == 128) SRA_SCATTER(uint16_t, 128, false, false);
-  else if (dtype == 0 && D == 64 && full) SRA_SCATTER(uint16_t, 64, true, true);
+  else if (dtype == 0 && D == 64 && full && q16) SRA_SCATTER(uint16_t, 64, true, true);
+  else if (dtype == 0 && D == 64 && full) SRA_SCATTER(uint16_t, 64, true, false);
   else if (dtype == 0 && D == 64 && q16) SRA_SCATTER(uint16_t, 64, false, true);
   else if (dtype == 0 && D == 64) SRA_SCATTER(uint16_t, 64, false, false);
   else if (dtype == 1 && D == 128) SRA_SCATTER(float, 128, false, false);

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void k_score_pass(ChunkTab tab, EntryReqBlocks
       // is one batch of loads
       if (nr > 0)
         rerot::rows<uint16_t, D, 16, 8>(tab, e, r0, nr, Hkv, rf.ks, rf.vs, rf.kf, rf.vf, rf.L, th,
-                                        reinterpret_cast<float2*>(Ks));
+                                        reinterpret_cast<float2*>(Ks), rf.sh);
     } else {   // one block per chunk entry picks its anchors
       if (kvh == 0)
         anchor_block(tab.len[e], (int64_t)tab.req[e] * Lctx + tab.dst[e], tab.src[e],

@@ -157,8 +157,10 @@ def sample_rows(R: int, Lq: int, k: int, seed: int = 0) -> list:
     return sorted(base | {rest[i] for i in pick})
 
 
-def run_fused(w, layer: int = 0, *, score: bool = True, row_pos_in=None, n_select=None, quotas=None):
-    """Runs sra_fused_layer for all requests of workload w; returns host arrays."""
+def run_fused(w, layer: int = 0, *, score: bool = True, row_pos_in=None, n_select=None, quotas=None,
+              fallback: bool = False):
+    """Runs sra_fused_layer for all requests of workload w; returns host arrays (with fallback, also
+    the [n_req][Hkv] report of groups recomputed exactly because of fp16's range)."""
     cfg = w.cfg
     dt = cfg.dtype
     lay = w.layer(layer)
@@ -188,8 +190,12 @@ def run_fused(w, layer: int = 0, *, score: bool = True, row_pos_in=None, n_selec
         row_pos = torch.from_numpy(np.ascontiguousarray(row_pos_in, dtype=np.int32)).cuda()
     ws = workspace(shape, n_req, n_chunks, L, R, Lq)
     kw = {}
+    fb = None
+    if fallback:
+        fb = torch.full((n_req, Hkv), -1, dtype=torch.int32, device="cuda")
+        kw["attn_fallback"] = fb
     if score:
-        kw = dict(q_crit=dev(w.q_crit, dt), k_crit_store=dev(w.k_crit, dt), n_select=n_select,
+        kw.update(q_crit=dev(w.q_crit, dt), k_crit_store=dev(w.k_crit, dt), n_select=n_select,
                   quotas=quotas, scores=scores)
     sra.fused_layer(shape, chunks=w.chunks, k_store=t["k_store"], v_store=t["v_store"], q_fresh=t["q_new"],
                     k_fresh=t["k_new"], v_fresh=t["v_new"], row_pos=row_pos, k_fused=kf, v_fused=vf, out=out,
@@ -199,4 +205,6 @@ def run_fused(w, layer: int = 0, *, score: bool = True, row_pos_in=None, n_selec
            "row_pos": row_pos.cpu().numpy(), "N": N, "R": R, "L": L, "Lctx": Lctx}
     if score:
         res["scores"] = scores.cpu().numpy()
+    if fb is not None:
+        res["fallback"] = fb.cpu().numpy()
     return res

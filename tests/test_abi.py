@@ -134,11 +134,13 @@ def test_attention_and_scatter_host_errors():
     lib = L.lib()
     s = shape()
     assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 10, FAKE[2], FAKE[3], 20, FAKE[4],
-                                      None, None, 0, None) == L.SRA_E_WORKSPACE
+                                      None, None, None, 0, None) == L.SRA_E_WORKSPACE
     assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 30, FAKE[2], FAKE[3], 20, FAKE[4],
-                                      None, FAKE[5], 1 << 30, None) == L.SRA_E_SHAPE       # R > L
+                                      None, None, FAKE[5], 1 << 30, None) == L.SRA_E_SHAPE       # R > L
     assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 10, FAKE[2], FAKE[3], 20, FAKE[2],
-                                      None, FAKE[5], 1 << 30, None) == L.SRA_E_ALIAS       # out is k_fused
+                                      None, None, FAKE[5], 1 << 30, None) == L.SRA_E_ALIAS       # out is k_fused
+    assert lib.sra_sparse_causal_attn(ctypes.byref(s), 1, FAKE[0], FAKE[1], 10, FAKE[2], FAKE[3], 20, FAKE[4],
+                                      None, FAKE[4], FAKE[5], 1 << 30, None) == L.SRA_E_ALIAS    # fallback is out
     assert lib.sra_scatter_kv(ctypes.byref(s), 1, FAKE[0], FAKE[1], None, 4, FAKE[2], FAKE[3], 20,
                               None) == L.SRA_E_NULL
     assert lib.sra_scatter_kv(ctypes.byref(s), 1, FAKE[0], FAKE[1], FAKE[6], 4, FAKE[0], FAKE[3], 20,

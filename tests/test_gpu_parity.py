@@ -414,3 +414,72 @@ def test_check_rows_reports_bad_rows():
         with pytest.raises(sra.SRAError) as e:
             sra.check_rows(torch.tensor(bad, dtype=torch.int32, device="cuda"), 10)
         assert e.value.status == 7 and f"row_pos[{idx}]" in str(e.value)
+
+
+# ------------------------------------------------------------------------------ fp16 operand range
+
+def test_fp16_range_fallback_matches_oracle():
+    """Keys of magnitude 1e5 have no fp16 value: their (request, KV head) group is recomputed exactly in
+    float32, reported as 1 in the fallback array, and the outputs still match the oracle (the other
+    group stays on the fp16 path and reports 0)."""
+    w = make_custom(dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128, chunk_lens=(100, 60), orig_pos=(0, 9),
+                    query_len=6, seed=41, select=("pct", 25))
+    lay = w.layer(0)
+    big = np.array([1e5, -1e5, 1.5e5], dtype=np.float32)
+    bits = O.storage_bits(O.bf16_round(big.astype(np.float64)), "bf16")
+    # KV head 1 only: two cached keys and one fresh query-row key
+    lay["k_store"][10, 1, 3] = bits[0]
+    lay["k_store"][130, 1, 70] = bits[1]
+    Lctx = int(w.chunks[0, :, 1].sum())
+    lay["k_new"][0, Lctx + 2, 1, 5] = bits[2]
+    N = O.select_count(25, 100, Lctx)
+    say(f"case fp16 range: keys {big.tolist()} on KV head 1, N={N}")
+    res = run_fused(w, n_select=N, fallback=True)
+    say(f"    fallback report {res['fallback'].tolist()}")
+    np.testing.assert_array_equal(res["fallback"], [[0, 1]])
+    stats = oracle_compare(w, res)
+    say(f"    fallback {res['fallback'].tolist()}, out max {stats['out_max']:.3g}")
+
+
+def test_fp16_range_query_fallback_standalone():
+    """A rotated query whose scaled value reaches fp16's infinity (|q| ~ 6e5) flags its group in the
+    standalone attention entry; the group is recomputed exactly and matches the oracle (log-sum-exp
+    within 2e-2 + 1e-6 |lse|: float32 logits of magnitude ~1e5 carry ~1e-6 relative error)."""
+    w = _custom_inputs("bf16")
+    cfg, dt, base = w.cfg, "bf16", w.cfg.rope_base
+    lay = w.layer(0)
+    n_req = w.chunks.shape[0]
+    Lctx, Lq = 193, 6
+    L = Lctx + Lq
+    shape = shape_of(cfg)
+    Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    rng = np.random.default_rng(3)
+    rows = np.stack([O.row_positions(np.sort(rng.choice(Lctx, 40, replace=False)), Lctx, Lq) for _ in range(n_req)])
+    R = rows.shape[1]
+    kf_ref, vf_ref = [], []
+    for q in range(n_req):
+        kf, vf = O.fuse_rerotate(lay["k_store"], lay["v_store"], w.chunks[q], L, dt, base)
+        kf, vf = O.scatter_kv(kf, vf, lay["k_new"][q][rows[q]], lay["v_new"][q][rows[q]], rows[q], dt, base)
+        kf_ref.append(kf)
+        vf_ref.append(vf)
+    qn = np.stack([lay["q_new"][q][rows[q]] for q in range(n_req)]).copy()
+    # request 1, row 7, query head 5 (KV head 1): every element 6e5
+    qn[1, 7, 5, :] = O.storage_bits(O.bf16_round(np.full(D, 6e5)), "bf16")
+    say("case fp16 range: scaled query beyond 65520 in request 1, KV head 1")
+    kd = dev(np.stack([O.storage_bits(k, dt) for k in kf_ref]), dt)
+    vd = dev(np.stack([O.storage_bits(v, dt) for v in vf_ref]), dt)
+    out = empty((n_req, R, Hq, D), dt)
+    lse = torch.empty((n_req, R, Hq), dtype=torch.float32, device="cuda")
+    fb = torch.full((n_req, Hkv), -1, dtype=torch.int32, device="cuda")
+    ws = workspace(shape, n_req, 1, L, R, 1)
+    sra.sparse_causal_attn(shape, dev(qn, dt), torch.from_numpy(rows.astype(np.int32)).cuda(), kd, vd, out, lse, ws,
+                           fallback=fb)
+    torch.cuda.synchronize()
+    say(f"    fallback report {fb.cpu().numpy().tolist()}")
+    np.testing.assert_array_equal(fb.cpu().numpy(), [[0, 0], [0, 1]])
+    o_h, l_h = host(out), lse.cpu().numpy()
+    for q in range(n_req):
+        o_ref, l_ref = O.sparse_causal_attn(qn[q], rows[q], kf_ref[q], vf_ref[q], dt, base)
+        mx, _ = assert_out_close(decode(o_h[q], dt), o_ref, dt)
+        assert np.all(np.abs(l_h[q] - l_ref) <= 2e-2 + 1e-6 * np.abs(l_ref)), "log-sum-exp"
+        say(f"    request {q}: out max err {mx:.3g}, largest |lse| {np.abs(l_ref).max():.3g}")
