@@ -371,6 +371,18 @@ int sra_sparse_causal_attn(const sra_shape* shape, int32_t n_req, const void* q_
  * Errors: as the stage calls. */
 int sra_fused_layer(const sra_layer_args* args, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* sra_fused_layer without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * scratch is a 64 MiB device array inside the library, one copy per GPU (its address taken once
+ * per device on the first call there), held until the process ends. Nothing is allocated by the
+ * call. Layers needing more scratch than 64 MiB (sra_workspace_size; the Mistral-7B-shaped layer
+ * needs about 46 MiB) are rejected with SRA_E_LIMIT before anything is enqueued. Every call on one
+ * GPU shares that GPU's scratch, which keeps the last call's contents: calls that overlap on one GPU
+ * (on different streams, or from different threads) race and must be ordered by the caller.
+ * Results are identical to sra_fused_layer's for the same arguments.
+ * Errors: as sra_fused_layer; SRA_E_LIMIT (scratch too small, device index above 63). */
+int sra_fused_layer_static(const sra_layer_args* args, hipStream_t stream);
+
 /* Layer-pipelined reconstruction (QCFuse summary (zh) §2.A: while the GPU rebuilds layer i's
  * selected tokens, layer i+1's KV cache is prefetched; KVCache reuse 01 §1.3.5: layer i's
  * recompute runs in parallel with loading layer i+1's cache, and adds no latency when loading

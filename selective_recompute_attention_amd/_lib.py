@@ -84,6 +84,7 @@ _SIGS = {
     "sra_sparse_causal_attn": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int32, _P, _P,
                                           _c.c_int32, _P, _P, _P, _P, _c.c_size_t, _P]),
     "sra_fused_layer": (_c.c_int, [_c.POINTER(LayerArgs), _P, _c.c_size_t, _P]),
+    "sra_fused_layer_static": (_c.c_int, [_c.POINTER(LayerArgs), _P]),
     "sra_check_rows": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int32), _P]),
     "sra_pipelined_layers": (_c.c_int, [_c.POINTER(LayerArgs), _c.c_int32, _c.POINTER(_P), _c.POINTER(_P),
                                         _c.c_size_t, _c.POINTER(_P), _c.POINTER(_P), _c.c_int32, _c.POINTER(_P),

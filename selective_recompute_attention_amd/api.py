@@ -15,6 +15,7 @@ from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, che
 __all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors", "anchor_prefix",
            "stats_workspace_size", "chunk_attention_stats", "prefix_overlap", "cachecraft_count",
            "score_select", "select_topn", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
+           "fused_layer_static",
            "pipelined_layers", "create_events", "destroy_events", "check_rows", "chunk_array", "SRAError"]
 
 
@@ -231,6 +232,14 @@ def fused_layer(shape, *, ws, stream=None, **kw):
     [n_req][Hkv] report of groups recomputed exactly (fp16 range)."""
     a, keep = _layer_args(shape, **kw)
     check(lib().sra_fused_layer(ctypes.byref(a), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    del keep
+
+
+def fused_layer_static(shape, *, stream=None, **kw):
+    """One layer (sra_fused_layer_static): as fused_layer, with the library's static scratch instead of
+    a workspace (no device allocation; calls on one GPU must not overlap)."""
+    a, keep = _layer_args(shape, **kw)
+    check(lib().sra_fused_layer_static(ctypes.byref(a), _stream(stream)))
     del keep
 
 

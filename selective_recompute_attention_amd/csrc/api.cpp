@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1053,6 +1054,56 @@ extern "C" {
 
 int sra_fused_layer(const sra_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   return fused_layer_impl(a, ws, ws_bytes, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of sra_fused_layer_static: a file-scope device array, one copy per GPU held until the
+// process ends. Host code never uses its name as an address: each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SRA_E_LIMIT, "device %d: the static scratch serves devices 0..%d", dev,
+                                                 kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SRA_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sra_fused_layer_static(const sra_layer_args* a, hipStream_t stream) {
+  int rc;
+  void* ws = nullptr;
+  if ((rc = static_scratch(&ws))) return rc;
+  // every argument check first (the scratch stands in for a workspace of unbounded size), then the
+  // workspace this layer needs against the scratch
+  if ((rc = fused_layer_impl(a, ws, std::numeric_limits<size_t>::max(), stream, true))) return rc;
+  const Plan p = make_plan(&a->shape, a->n_req, a->n_chunks, a->total_len, a->n_rows, a->query_len);
+  const size_t need = a->q_crit ? p.total : p.attn_end;
+  if (need > kStaticScratchBytes)
+    return fail(SRA_E_LIMIT, "this layer needs %zu bytes of scratch; the static scratch holds %zu (use sra_fused_layer "
+                "with a workspace)", need, kStaticScratchBytes);
+  return fused_layer_impl(a, ws, kStaticScratchBytes, stream, false);
 }
 
 int sra_pipelined_layers(const sra_layer_args* layers, int32_t n_layers, const void* const* host_k,
