@@ -7,7 +7,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsra.so")
+# SRA_LIB_PATH selects another build of the same library (the host-sanitized one, for instance)
+LIB_PATH = os.environ.get("SRA_LIB_PATH") or os.path.join(_PKG, "libsra.so")
 
 SRA_OK = 0
 SRA_E_NULL = 1

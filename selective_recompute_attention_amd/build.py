@@ -1,8 +1,16 @@
 """Builds libsra.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m selective_recompute_attention_amd.build [-v]
+    python -m selective_recompute_attention_amd.build [-v] [--sanitize]
 
 Every source is compiled on each call (objects go to _build/ at the repository root).
+
+--sanitize builds a host-checked copy instead, _build/libsra_asan.so: the host pass of every source
+(the C ABI's argument checks, planning and launch code) is compiled with AddressSanitizer and
+UndefinedBehaviorSanitizer, the device code as usual. It is for CPU runs of the ABI tests with the
+sanitizer runtimes preloaded (SRA_LIB_PATH selects the library the binding loads):
+
+    LD_PRELOAD=$(hipcc --print-file-name=libclang_rt.asan-x86_64.so) ASAN_OPTIONS=detect_leaks=0 \
+        SRA_LIB_PATH=_build/libsra_asan.so python -m pytest tests/test_abi.py
 """
 import os
 import subprocess
@@ -27,9 +35,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# host pass only: each option behind -Xarch_host, so no device code is built with a sanitizer
+SANITIZE = [f for opt in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+                          "-fno-omit-frame-pointer", "-g") for f in ("-Xarch_host", opt)]
+
+
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    obj_dir = os.path.join(OBJ, "asan") if sanitize else OBJ
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(SANITIZE if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -43,20 +57,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    os.makedirs(os.path.join(OBJ, "asan") if sanitize else OBJ, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
+    lib = os.path.join(OBJ, "libsra_asan.so") if sanitize else LIB
+    tmp = lib + ".tmp"
+    # a sanitized library leaves the runtimes' symbols to the preloaded sanitizer runtime
+    extra = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-shared-libasan"] if sanitize else []
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
