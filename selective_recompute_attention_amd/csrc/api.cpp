@@ -639,6 +639,8 @@ int sra_anchor_prefix(const sra_shape* shape, int32_t n_req, const void* k_store
   return ok();
 }
 
+}  // extern "C"
+
 namespace {
 struct StatsPlan {
   int n_tiles = 0, qop_blocks = 0;
@@ -656,6 +658,8 @@ StatsPlan stats_plan(const sra_shape* s, int n_req, int Lctx, int n_chunks) {
   return p;
 }
 }  // namespace
+
+extern "C" {
 
 size_t sra_stats_workspace_size(const sra_shape* shape, int32_t n_req, int32_t ctx_len, int32_t n_chunks) {
   if (!shape || check_shape(shape) != SRA_OK || n_req <= 0 || ctx_len <= 0 || n_chunks <= 0) return 0;
@@ -1187,7 +1191,8 @@ int sra_check_rows(const int32_t* row_pos, int32_t n_req, int32_t R, int32_t L, 
   if (e == hipSuccess) e = sra::launch_check_rows(row_pos, n_req, R, L, d_bad, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(&h_bad, d_bad, sizeof(int), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  hipFree(d_bad);
+  const hipError_t ef = hipFree(d_bad);
+  if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return hip_fail(e, "row check");
   if (h_bad != std::numeric_limits<int>::max()) {
     if (first_bad) *first_bad = h_bad;

@@ -29,16 +29,23 @@
 //   * The S accumulator starts at minus the softmax reference, so the products come out already
 //     relative to it. The reference is the maximum of a segment's first 32 keys; later keys are
 //     exponentiated against it directly, and only when a 32-key block's probability sum exceeds
-//     2^kLazyMax (some logit more than kLazyMax above the reference) does the reference move, with
+//     kSumCap = 2^16 (some logit more than 16 above the reference, log2 domain) does the reference move, with
 //     the accumulator rescaled: no per-block maximum or subtraction in the common case.
-//   * 64-key tiles: K row-major (fp16, padded rows) and V transposed on its way into LDS with the key
-//     order of the probabilities (bits 2 and 3 of the key index swapped), so each P V operand is one
-//     16-byte LDS read; both double-buffered, one barrier per tile, the next tile's rows loaded into
-//     registers a tile ahead. Work groups are numbered with the group index fastest, so all work of
-//     one KV head lands on one XCD (work groups are dealt round-robin over the 8 XCDs) and its K/V
-//     stay in that XCD's L2.
+//   * Software pipeline in steps of 32 keys, the same in every wave: step j issues the products of
+//     S_{j+1} on the matrix cores interleaved with the exponentials of S_j on the vector units, then
+//     O += V_j^T P_j. Register use allows two waves per SIMD, which fill each other's stalls.
+//   * K and V tiles go straight from global memory into four-slot LDS rings (direct loads, no
+//     registers), issued three steps ahead; an explicit count of outstanding loads and one LDS-only
+//     barrier per step publish a tile, so later loads stay in flight across the barrier. K slots are
+//     [16-row block][chunk][row % 16] (each S operand read is a lane base plus a constant and hits 16
+//     consecutive slots); V slots are row-major with chunks swizzled by key, and each P V operand is
+//     two transposing LDS reads (ds_read_b64_tr_b16) whose key order matches the probabilities'.
+//   * Work groups are numbered with the group index fastest, so all work of one KV head lands on one
+//     XCD (work groups are dealt round-robin over the 8 XCDs) and its K/V stay in that XCD's L2.
 // f32 path: plain float32 arithmetic, one block per (row, KV head), exact online softmax.
 #include <float.h>
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -46,6 +53,7 @@ namespace sra {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -53,8 +61,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLazyMax = 16.f;       // log2 headroom of the attention softmax reference
-constexpr float kSumCap = 65536.f;     // 2^kLazyMax: a 32-key block sum above it moves the reference
+constexpr float kSumCap = 65536.f;     // 2^16: a 32-key block sum above it moves the softmax reference
 
 struct AttnArgs {
   const uint16_t* qop;
@@ -79,6 +86,20 @@ struct AttnArgs {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Wait until at most N vector memory operations of this wave are outstanding (s_waitcnt with the
+// export and LDS counters left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Work-group barrier that waits for this wave's LDS operations only. Tiles that direct loads write into
+// LDS are published by an explicit vmcnt wait before it, so loads of later tiles stay in flight across
+// the barrier (a __syncthreads() fence would wait for all of them). The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // float pair -> two fp16 (round to nearest even) in one word, and back
 __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
@@ -88,10 +109,6 @@ __device__ __forceinline__ float h2f(uint32_t h16) { return (float)__builtin_bit
 __device__ __forceinline__ int64_t part_index(const AttnArgs& a, int group, int piece, int slot) {
   return ((int64_t)(group * a.pieces + piece) * 2 + slot) * 128;
 }
-
-// Position of tile-local key k in the transposed V tile: bits 2 and 3 swapped, which lists each
-// lane's eight probabilities of a 16-key step (keys 8s' + 4hh + e, s' and e free) contiguously.
-__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // Probabilities of one 32-key half against the current reference (x already relative to it): bf16
 // operands of the P V products and their sum (the same rounded values, one v_dot2c_f32_bf16 per
@@ -113,15 +130,40 @@ __device__ __forceinline__ void probs(const f32x16& x, u32x4* pw, float& lsum) {
   lsum = s0 + s1;
 }
 
+// Tile-local row and 16-byte chunk (as a byte offset) that lane `lane` of direct load instruction n
+// brings into an LDS ring slot (instruction n fills the slot's n-th kilobyte, lane l at byte 16 l).
+// K slots are [16-row block][chunk][row % 16]; V slots are row-major with chunk c of row k at slot
+// c ^ ((k % (D / 32)) << 2).
+template <int D>
+__device__ __forceinline__ int ring_k_row(int n, int lane) { return 16 * (n / (D / 32)) + (lane & 15); }
+template <int D>
+__device__ __forceinline__ uint32_t ring_k_chunk(int n, int lane) {
+  return 16u * (uint32_t)(4 * (n % (D / 32)) + (lane >> 4));
+}
+template <int D>
+__device__ __forceinline__ int ring_v_row(int n, int lane) { return (512 / D) * n + lane / (D / 8); }
+template <int D>
+__device__ __forceinline__ uint32_t ring_v_chunk(int n, int lane) {
+  return 16u * ((uint32_t)(lane % (D / 8)) ^ ((uint32_t)(ring_v_row<D>(n, lane) % (D / 32)) << 2));
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int NKS = D / 16;   // K-steps of S^T = K Q^T
   constexpr int NDT = D / 32;   // 32-row d tiles of O^T
-  constexpr int KT = 64;        // keys per LDS tile (one unit)
-  constexpr int KST = D + 8;    // K row stride in LDS (elements): conflict-free 16-byte reads
-  constexpr int VST = KT + 8;   // V^T row stride in LDS (elements): conflict-free 16-byte reads
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KST];   // double-buffered tiles
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VST];
+  constexpr int KT = 64;              // keys per work unit (the granularity of the split)
+  constexpr int ST = 32;              // keys per pipeline step
+  constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  constexpr int RB = D * 2;           // bytes per key row in LDS (rows unpadded, chunks swizzled)
+  constexpr int TB = ST * RB;         // bytes per step tile
+  constexpr int RPI = 64 / CPR;       // rows per direct load instruction (64 lanes x 16 bytes)
+  constexpr int NIW = ST / RPI / 4;   // direct load instructions per wave per tile
+  static_assert(NIW >= 1 && NIW * 4 * RPI == ST, "a step tile splits evenly over the four waves");
+  // four-deep rings of step tiles, filled straight from global memory (one array per slot)
+  __shared__ __attribute__((aligned(1024))) unsigned char K0s[TB], K1s[TB], K2s[TB], K3s[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0s[TB], V1s[TB], V2s[TB], V3s[TB];
+  unsigned char* const Kring[4] = {K0s, K1s, K2s, K3s};
+  unsigned char* const Vring[4] = {V0s, V1s, V2s, V3s};
   __shared__ int cum[kAttnMaxTiles + 1];
   __shared__ int wsum[4];
 
@@ -178,30 +220,37 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.kh + ((int64_t)req * a.L * a.Hkv + kvh) * D);
   const char* vbase = reinterpret_cast<const char*>(a.vf + ((int64_t)req * a.L * a.Hkv + kvh) * D);
   const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
-  // Tile loads. K: 16-byte chunks, dims fastest (coalesced rows). V: each task holds 4 keys x 8
-  // dims and writes them transposed; key quads vary fastest across lanes, so the 16 lanes an LDS
-  // write serves together hit 16 distinct bank pairs. The next tile's loads are issued into
-  // registers before the current tile is computed, hiding the global-memory latency.
-  constexpr int NKL = KT * (D / 8) / 256;           // K chunks per thread
-  const bool vtask = threadIdx.x < (KT / 4) * (D / 8);
-  const int vkq = threadIdx.x % (KT / 4), vc = threadIdx.x / (KT / 4);
-  u32x4 kr[NKL], vr[4];
-  auto prefetch = [&](int kt0, int kend) {
-    // unconditional loads of clamped rows (kt0 < kend): rows past the range repeat row kend - 1,
-    // whose keys the mask removes (probability 0 on finite values). Nothing reads the registers
-    // until the tile is stored, so no load waits for another.
+  // Tiles move straight from global memory into the LDS rings (16 bytes per lane, no registers), a
+  // four-tile ring each for K and V; direct load instruction n of a tile fills its n-th kilobyte (lane l
+  // at byte 16 l).
+  //  * K: [16-row block][chunk][row % 16], 16 bytes each. Instruction n holds row block n / (CPR / 4) and
+  //    chunks 4 (n % (CPR / 4)) .. + 3 (lane l: row 16 block + l % 16, chunk 4 (n % (CPR / 4)) + l / 16).
+  //    The S operand read of lane (l32, hh), row l32 and chunk 2 ks + hh, is a lane base plus 512 ks,
+  //    and any 16 lanes read 16 consecutive slots.
+  //  * V: row-major (instruction n: rows RPI n .., lane l: row RPI n + l / CPR), 16-byte chunk c of row k
+  //    at slot c ^ ((k % NDT) << 2): the transposing P V operand reads of any 32 lanes hit distinct
+  //    8-byte bank pairs, and the key block stays a compile-time offset.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t kvo[NIW], vvo[NIW];     // byte offsets of the lane's loads from the tile's first row
 #pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-      const int u = threadIdx.x + 256 * i;
-      const uint32_t j = (uint32_t)min(kt0 + u / (D / 8), kend - 1);
-      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (j * row_bytes + 16u * (uint32_t)(u % (D / 8))));
-    }
+  for (int i = 0; i < NIW; ++i) {
+    kvo[i] = (uint32_t)ring_k_row<D>(NIW * wv + i, lane) * row_bytes + ring_k_chunk<D>(NIW * wv + i, lane);
+    vvo[i] = (uint32_t)ring_v_row<D>(NIW * wv + i, lane) * row_bytes + ring_v_chunk<D>(NIW * wv + i, lane);
+  }
+  // operand read offsets: S (row l32, chunk 2 ks + hh: + 512 ks) and the transposing V reads (lane as
+  // address source: key 4 hh + (l32 % 16) / 4 of an 8-key block, dims 32 dt + 16 (l32 / 16) + 4 (l32 % 4))
+  const uint32_t kofs = (uint32_t)((l32 >> 4) * (CPR * 256) + hh * 256 + (l32 & 15) * 16);
+  uint32_t vofs[NDT];
+  {
+    const uint32_t kl = 4 * hh + ((l32 & 15) >> 2), c01 = 2 * (l32 >> 4) + ((l32 & 3) >> 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t j = (uint32_t)min(kt0 + 4 * vkq + i, kend - 1);
-      vr[i] = *reinterpret_cast<const u32x4*>(vbase + (j * row_bytes + 16u * (uint32_t)(vtask ? vc : 0)));
-    }
-  };
+    for (int dt = 0; dt < NDT; ++dt)
+      vofs[dt] = kl * RB + 16u * (4u * ((uint32_t)dt ^ ((uint32_t)(l32 >> 2) & (NDT - 1))) + c01) + 8u * (l32 & 1);
+  }
+  // buffer resources over this (request, KV head)'s rows: row r at byte r * row_bytes
+  const int nrec = (int)((uint32_t)(a.L - 1) * row_bytes + RB);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, nrec, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, nrec, 0x00020000);
 
   int slot = 0;
   for (int u = u0; u < u1; ++t) {
@@ -211,9 +260,39 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const bool direct = (u == c0 && se == c1);
     // keys stop at the tile's last position: rows past it are never read
     const int maxkey = min(rp[min(t * 128 + 127, Mv - 1) / g], a.L - 1);
-    const int kbeg = KT * (u - c0), kend = min(KT * (se - c0), maxkey + 1);
+    const int kbeg = KT * (u - c0), kend = min(KT * (se - c0), maxkey + 1);   // kbeg < kend
+    const int nst = (kend - kbeg + ST - 1) / ST;   // pipeline steps
 
-    // query operand, K/V prefetch and the row position all go out before the first wait
+    // Step tile x of the segment into ring slot b. In a tile that reaches past the range, rows repeat
+    // row kend - 1, whose keys the mask removes (probability 0 on finite values).
+    auto issue = [&](__amdgpu_buffer_rsrc_t rs, unsigned char* ring, const uint32_t* vo, bool is_v, int x) {
+      int rl[NIW];   // tile-local rows of the lane's loads
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) rl[i] = is_v ? ring_v_row<D>(NIW * wv + i, lane) : ring_k_row<D>(NIW * wv + i, lane);
+      const int kt = kbeg + ST * x;
+      typedef __attribute__((address_space(3))) void lds_t;
+      // the destination is laundered through an empty asm: the compiler then does not tie the load to
+      // the slot's array and adds no wait of its own before reads of it (the waits here are explicit)
+      __attribute__((address_space(3))) unsigned char* dst = (__attribute__((address_space(3))) unsigned char*)ring;
+      asm volatile("" : "+s"(dst));
+      if (kt + ST <= kend) {
+#pragma unroll
+        for (int i = 0; i < NIW; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (lds_t*)(dst + 1024 * (NIW * wv + i)), 16, vo[i],
+              kt * (int)row_bytes, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NIW; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (lds_t*)(dst + 1024 * (NIW * wv + i)), 16,
+              vo[i] + (uint32_t)(min(kt + rl[i], kend - 1) - rl[i]) * row_bytes, 0, 0, 0);
+      }
+    };
+    auto issue_k = [&](int x, int b) { issue(rk, Kring[b], kvo, false, x); };
+    auto issue_v = [&](int x, int b) { issue(rv, Vring[b], vvo, true, x); };
+
+    // query operand and the first tiles' loads go out before the first wait
     const int v = t * 128 + wave * 32 + l32;
     f16x8 q16[NKS];
     {
@@ -225,17 +304,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       for (int ks = 0; ks < NKS; ++ks)
         q16[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(qb + ((uint32_t)(ks * 2) * 1024u + lo)));
     }
-    prefetch(kbeg, kend);
     const int r = min(v, Mv - 1) / g;
     const int hq = kvh * g + v % g;
     const int p_r = rp[r];
+    // K_0, K_1, V_0 first; then what the steps -2 and -1 would have issued (K_2, V_1 and K_3, V_2). All
+    // ring slots are free: the previous segment ended with a barrier. (The loads above are issued first:
+    // a wait for them then does not wait for the tiles.)
+    issue_k(0, 0);
+    issue_k(1, 1);
+    issue_v(0, 0);
+    issue_k(2, 2);
+    issue_v(1, 1);
+    issue_k(3, 3);
+    issue_v(2, 2);
     const bool qvalid = v < Mv && p_r >= 0;  // negative positions are skipped
     const int pq = qvalid ? min(p_r, a.L - 1) : -1;
     if (!qvalid) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) q16[ks] = __builtin_bit_cast(f16x8, u32x4{0u, 0u, 0u, 0u});
     }
-    // smallest position among this wave's query vectors: tiles entirely at or below it need no mask
+    // smallest position among this wave's query vectors: steps entirely at or below it need no mask
     const int pmin = (int)wave_reduce(qvalid ? (uint32_t)pq : (uint32_t)INT_MAX,
                                       [](uint32_t x, uint32_t y) { return x < y ? x : y; });
 
@@ -243,135 +331,136 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x16{};
     float m_ref = 0.f, l_run = 0.f;   // softmax reference (log2 domain) and running sum
-    f32x16 negm = {};                 // -m_ref in every element: the S accumulator's start value
-    bool first = true;                // wave-uniform: the segment's first half sets the reference
+    f32x16 negm;                      // -m_ref in every element: the S accumulator's start value
 
-    // K row-major; V transposed on the way in (word pp of a task: dims 8c+2pp in the low half
-    // and 8c+2pp+1 in the high half, four keys each, at the keys' permuted position)
-    const int vpos = vt_pos(4 * vkq);
-    auto store_tile = [&](int buf) {
+    // causal mask by absolute position where step j reaches past the wave's smallest position or the
+    // range's end: element rr holds key kbeg + 32 j + 4 hh + 8 (rr / 4) + rr % 4
+    auto mask = [&](int j, f32x16& x) {
+      const int kt = kbeg + ST * j;
+      if (!(kt + ST - 1 < kend && kt + ST - 1 <= pmin)) {
+        const int lim = min(kend - 1, pq) - (kt + 4 * hh);
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) {
-        const int uu = threadIdx.x + 256 * i;
-        *reinterpret_cast<u32x4*>(&Ks[buf][(uu / (D / 8)) * KST + 8 * (uu % (D / 8))]) = kr[i];
-      }
-      if (vtask) {
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          u32x2 lo, hi;
-          lo[0] = __builtin_amdgcn_perm(vr[1][pp], vr[0][pp], 0x05040100u);
-          lo[1] = __builtin_amdgcn_perm(vr[3][pp], vr[2][pp], 0x05040100u);
-          hi[0] = __builtin_amdgcn_perm(vr[1][pp], vr[0][pp], 0x07060302u);
-          hi[1] = __builtin_amdgcn_perm(vr[3][pp], vr[2][pp], 0x07060302u);
-          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp) * VST + vpos]) = lo;
-          *reinterpret_cast<u32x2*>(&Vt[buf][(8 * vc + 2 * pp + 1) * VST + vpos]) = hi;
-        }
+        for (int rr = 0; rr < 16; ++rr)
+          if (8 * (rr >> 2) + (rr & 3) > lim) x[rr] = -INFINITY;
       }
     };
-    // Both buffers are free here: the previous segment's loop ended with a barrier. Tile t is
-    // computed from buffer t%2 while tile t+1 is written to the other one, so one barrier per tile
-    // both publishes the next tile and retires the current one.
-    store_tile(0);
-    if (kbeg + KT < kend) prefetch(kbeg + KT, kend);
-    __syncthreads();
-    int cur = 0;
-    for (int kt0 = kbeg; kt0 < kend; kt0 += KT) {
-      const uint16_t* Kc = Ks[cur];
-      const uint16_t* Vc = Vt[cur];
-
-      // S^T[key][q] - m_ref for the two 32-key halves. The halves then go through softmax and P V
-      // one after the other, so the second half's products are still running while the first
-      // half's probabilities are formed.
-      f32x16 sc[2];
+    auto s_prod = [&](const unsigned char* Kc, f32x16& acc, bool from_ref) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const f16x8 ka = __builtin_bit_cast(
-              f16x8, *reinterpret_cast<const u32x4*>(Kc + (32 * st + l32) * KST + 16 * ks + 8 * hh));
-          sc[st] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, q16[ks], ks == 0 ? negm : sc[st], 0, 0, 0);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f16x8 ka = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(Kc + kofs + 512 * ks));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, q16[ks], ks == 0 ? (from_ref ? negm : f32x16{}) : acc, 0, 0, 0);
       }
-      // both halves' products started from the reference of the tile's start; when the first half
-      // moves it (the segment's first half, or a rescale), the second half follows by the difference
-      const float m_tile = m_ref;
-      bool moved = false;   // wave-uniform
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x16 x = sc[st];
-        if (moved) {
-          const float dm = m_tile - m_ref;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) x[rr] += dm;
-        }
-        // causal mask by absolute position where the half reaches past the wave's smallest position
-        // or the range's end: element rr holds key kt0 + 32 st + 4 hh + (8 (rr / 4) + rr % 4)
-        const int klast = kt0 + 32 * st + 31;
-        if (!(klast < kend && klast <= pmin)) {
-          const int lim = min(kend - 1, pq) - (kt0 + 32 * st + 4 * hh);
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            if (8 * (rr >> 2) + (rr & 3) > lim) x[rr] = -INFINITY;
-        }
-        if (first) {   // the segment's first half: its maximum becomes the reference (x was the logit)
-          float mt = -INFINITY;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
-          mt = half_max(mt);
-          const float r0 = mt == -INFINITY ? 0.f : mt;   // no visible key in the segment: stays 0
-          m_ref = r0;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            x[rr] -= r0;
-            negm[rr] = -r0;
-          }
-          first = false;
-          moved = true;
-        }
-        u32x4 pw[2];
-        float lsum;
-        probs(x, pw, lsum);
-        if (__any(lsum > kSumCap)) {   // a logit more than kLazyMax above the reference: move it
-          float mt = -INFINITY;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, x[rr]);
-          mt = half_max(mt);
-          const float sh = mt > 0.f ? mt : 0.f;
-          const float alpha = fast_exp2(-sh);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-          l_run *= alpha;
-          m_ref += sh;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            x[rr] -= sh;
-            negm[rr] = -m_ref;
-          }
-          moved = true;
-          probs(x, pw, lsum);
-        }
-        l_run += lsum;
+    };
 
-        // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 32st + 16mp + 8(s/4) + 4hh + s%4,
-        // stored at V^T position 32st + 16mp + 8hh + s
+    // K_0, K_1 and V_0 have landed (their loads are followed by eight per wave at most); S_0 gives the
+    // reference
+    wait_vmcnt<4 * NIW>();
+    lds_barrier();
+    f32x16 sA, sB;
+    s_prod(Kring[0], sA, false);
+    mask(0, sA);
+    {
+      float mt = -INFINITY;
 #pragma unroll
-        for (int mp = 0; mp < 2; ++mp) {
-          const bf16x8 pb = as_bf16x8(pw[mp]);
+      for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, sA[rr]);
+      mt = half_max(mt);
+      m_ref = mt == -INFINITY ? 0.f : mt;   // no visible key in the segment: stays 0
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const u32x4 vw = *reinterpret_cast<const u32x4*>(Vc + (32 * dt + l32) * VST + 32 * st + 16 * mp + 8 * hh);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vw), pb, o[dt], 0, 0, 0);
-          }
-        }
+      for (int rr = 0; rr < 16; ++rr) {
+        sA[rr] -= m_ref;
+        negm[rr] = -m_ref;
       }
-
-      if (kt0 + KT < kend) {
-        store_tile(cur ^ 1);   // its previous tile was retired by the last barrier
-        if (kt0 + 2 * KT < kend) prefetch(kt0 + 2 * KT, kend);
-      }
-      __syncthreads();
-      cur ^= 1;
     }
+    lds_barrier();   // K_0's slot takes K_4 in the first step
+
+    // Step j (ring slot B = j % 4), with S_j complete in sa (relative to the reference): K_{j+4} and
+    // V_{j+3} go out into the slots of K_j and V_{j-1} (both retired by the previous step's barrier);
+    // the matrix cores form S_{j+1} from K_{j+1} into sb while the vector units turn S_j into
+    // probabilities; O += V_j^T P_j; then K_{j+2} and V_{j+1} (issued two steps back) are waited for
+    // and one barrier publishes them.
+    auto step = [&](auto b_tag, const int j, f32x16& sa, f32x16& sb, auto more_tag) {
+      constexpr int B = decltype(b_tag)::value;
+      constexpr bool MORE = decltype(more_tag)::value;   // S_{j+1} exists
+      if constexpr (MORE) {
+        issue_k(j + 4, B);
+        issue_v(j + 3, (B + 3) & 3);
+      }
+      mask(j, sa);
+      u32x4 pw[2];
+      float lsum;
+      if constexpr (MORE) s_prod(Kring[(B + 1) & 3], sb, true);
+      probs(sa, pw, lsum);
+      if (__any(lsum > kSumCap)) {   // a logit more than 16 above the reference: move it
+        float mt = -INFINITY;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mt = fmaxf(mt, sa[rr]);
+        mt = half_max(mt);
+        const float sh = mt > 0.f ? mt : 0.f;
+        const float alpha = fast_exp2(-sh);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        l_run *= alpha;
+        m_ref += sh;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          sa[rr] -= sh;
+          negm[rr] = -m_ref;
+        }
+        if constexpr (MORE) {   // S_{j+1} started from the old reference
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) sb[rr] -= sh;
+        }
+        probs(sa, pw, lsum);
+      }
+      l_run += lsum;
+      // O^T[d][q] += V^T[d][key] P^T[key][q]; hardware k = 8*hh + s <-> key 16mp + 8(s/4) + 4hh + s%4.
+      // Each operand is two transposing reads of four keys.
+      typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+      const __attribute__((address_space(3))) unsigned char* Vc = (const __attribute__((address_space(3))) unsigned char*)Vring[B];
+#pragma unroll
+      for (int mp = 0; mp < 2; ++mp) {
+        const bf16x8 pb = as_bf16x8(pw[mp]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vc + vofs[dt] + (16 * mp) * RB));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vc + vofs[dt] + (16 * mp + 8) * RB));
+          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+        }
+      }
+      if constexpr (MORE) wait_vmcnt<4 * NIW>();
+      lds_barrier();
+    };
+    typedef std::integral_constant<int, 0> B0;
+    typedef std::integral_constant<int, 1> B1;
+    typedef std::integral_constant<int, 2> B2;
+    typedef std::integral_constant<int, 3> B3;
+    int j = 0;
+    for (; j + 4 < nst; j += 4) {   // four steps with a successor each
+      step(B0{}, j, sA, sB, std::true_type{});
+      step(B1{}, j + 1, sB, sA, std::true_type{});
+      step(B2{}, j + 2, sA, sB, std::true_type{});
+      step(B3{}, j + 3, sB, sA, std::true_type{});
+    }
+    // the last one to four steps (j % 4 == 0)
+    if (j + 1 < nst) {
+      step(B0{}, j, sA, sB, std::true_type{});
+      if (j + 2 < nst) {
+        step(B1{}, j + 1, sB, sA, std::true_type{});
+        if (j + 3 < nst) {
+          step(B2{}, j + 2, sA, sB, std::true_type{});
+          step(B3{}, j + 3, sB, sA, std::false_type{});
+        } else {
+          step(B2{}, j + 2, sA, sB, std::false_type{});
+        }
+      } else {
+        step(B1{}, j + 1, sB, sA, std::false_type{});
+      }
+    } else {
+      step(B0{}, j, sA, sB, std::false_type{});
+    }
+    // loads of tiles past the segment may still be landing in the rings: none outlives the segment
+    wait_vmcnt<0>();
 
     const float l_tot = half_sum(l_run);
     // the lane's store offsets are formed here from an opaque copy of the lane index, so that the
