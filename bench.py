@@ -81,6 +81,27 @@ class Hip:
         return float(ms.value)
 
 
+def hbm_copy_gbs():
+    """Read+write bandwidth of a plain 1 GiB device copy (torch), timed with events: the practical
+    ceiling of a streaming kernel on this GPU, reported beside the stages' figures."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    e1.synchronize()
+    gbs = 2.0 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def copy_probe():
     import torch
     n = 256 << 20
@@ -230,7 +251,21 @@ class FusedStep:
         return 2.0 * self.Lq * self.Hq * self.D * self.Lctx * self.n_req
 
     def s3_bytes(self, l):
+        """Fresh K and V of the layer's rows read, the fused rows written."""
         return 4 * self.kv_row_bytes() * self.n_req * (self.counts[l] + self.Lq)
+
+    def s1_launch_bytes(self):
+        """Everything the re-rotation launch moves: the algorithmic bytes plus the fp16 copy of every
+        fused key row that the attention reads its S operand from."""
+        return self.s1_bytes() + self.kv_row_bytes() * self.n_req * self.Lctx
+
+    def s3_launch_bytes(self, l):
+        """Everything the scatter launch moves: fresh K/V read and fused K/V written, the fp16 key copy
+        of the rows, and each row's fresh query read and written back as the attention's fp16 query
+        operand (rotated and scaled in the same launch)."""
+        rows = self.n_req * (self.counts[l] + self.Lq)
+        q_row = self.Hq * self.D * 2
+        return rows * (5 * self.kv_row_bytes() + 2 * q_row)
 
     def measure(self, hip, sp, steps, warmup):
         """Wall clock of `steps` steps (synchronised on both sides), then a separate pass with stage
@@ -284,9 +319,20 @@ class FusedStep:
         res["s2_gflop"] = self.s2_flops() / 1e9
         res["rerotate_score_hbm_gbs"] = (s1 + self.s2_bytes()) / (s12_0 * 1e-3) / 1e9
         s3b = [self.s3_bytes(l) for l in range(self.n_layers)]
-        res["s3_hbm_gbs"] = float(np.sum(s3b)) / (float(np.sum(st["s3"])) * 1e-3) / 1e9
-        res["s3_note"] = ("S3 bytes = fresh K/V read + fused rows written; the same launch also reads the rows' "
-                          "fresh Q and writes the attention's query operand")
+        s3l = [self.s3_launch_bytes(l) for l in range(self.n_layers)]
+        t3 = float(np.sum(st["s3"])) * 1e-3
+        res["s3_hbm_gbs"] = float(np.sum(s3b)) / t3 / 1e9
+        res["s3_launch_hbm_gbs"] = float(np.sum(s3l)) / t3 / 1e9
+        res["s3_bytes"] = s3b
+        res["s3_launch_bytes"] = s3l
+        if later:
+            res["s1_launch_hbm_gbs"] = self.s1_launch_bytes() / (float(np.mean(later)) * 1e-3) / 1e9
+        res["s1_launch_bytes_per_layer"] = self.s1_launch_bytes()
+        # the scoring alone at layer 0: the layer-0 span less a standalone re-rotation
+        if later:
+            t2 = s12_0 - float(np.mean(later))
+            res["s2_ms_est"] = t2
+            res["s2_tflops"] = self.s2_flops() / (t2 * 1e-3) / 1e12
         self.rps = rps
         return res
 
@@ -491,7 +537,8 @@ def stats_leg(sra, fs, hip, sp):
 
 def summary(res):
     keep = ["ms_per_step", "rows", "rows_per_s", "attn_tflops", "attn_mfma_frac", "s1_hbm_gbs",
-            "rerotate_score_hbm_gbs", "s3_hbm_gbs", "stage_ms", "layer0_rerotate_score_select_ms"]
+            "s1_launch_hbm_gbs", "rerotate_score_hbm_gbs", "s3_hbm_gbs", "s3_launch_hbm_gbs", "s2_tflops",
+            "stage_ms", "layer0_rerotate_score_select_ms"]
     return {k: res[k] for k in keep if k in res}
 
 
@@ -651,9 +698,24 @@ def main():
         "s1_hbm_gbs": res.get("s1_hbm_gbs"),
         "rerotate_score_hbm_gbs": res["rerotate_score_hbm_gbs"],
         "s3_hbm_gbs": res["s3_hbm_gbs"],
+        "streaming_stages": {
+            "hbm_peak_gbs": HBM_PEAK_GBS,
+            "plain_copy_gbs": hbm_copy_gbs(),
+            "s1": {"ms": float(np.mean(res["stage_ms"]["s1"][1:])) if fs.n_layers > 1 else None,
+                   "algorithmic_bytes": res["s1_bytes_per_layer"], "launch_bytes": res["s1_launch_bytes_per_layer"],
+                   "algorithmic_gbs": res.get("s1_hbm_gbs"), "launch_gbs": res.get("s1_launch_hbm_gbs")},
+            "s3": {"ms": res["stage_ms"]["s3"], "algorithmic_bytes": res["s3_bytes"],
+                   "launch_bytes": res["s3_launch_bytes"], "algorithmic_gbs": res["s3_hbm_gbs"],
+                   "launch_gbs": res["s3_launch_hbm_gbs"]},
+            "s2_layer0": {"ms_est": res.get("s2_ms_est"), "gflop": res["s2_gflop"], "tflops": res.get("s2_tflops"),
+                          "note": "compute-bound (two passes over the critical layer's K with float32-exact "
+                                  "products); its time is the layer-0 span less a standalone re-rotation"},
+            "note": "algorithmic bytes: what the method reads and writes (stored K/V, fused K/V, fresh K/V); "
+                    "launch bytes add what the launch also moves for the attention (the fp16 key copy, and in "
+                    "S3 the rows' fresh Q read and fp16 query operand written); plain_copy_gbs is a device "
+                    "copy of 1 GiB timed here, the practical ceiling of a read+write stream"},
         "algorithmic": {"s1_bytes_per_layer": res["s1_bytes_per_layer"], "s2_bytes": res["s2_bytes"],
-                        "s2_gflop": res["s2_gflop"], "attn_flops_per_layer": flops,
-                        "s3_note": res["s3_note"]},
+                        "s2_gflop": res["s2_gflop"], "attn_flops_per_layer": flops},
     }
     if not args.no_legs:
         legs = {}
