@@ -20,8 +20,9 @@ namespace sra {
 namespace {
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelLdsKeys = 12288;   // keys of one selection unit kept in LDS (48 KB)
-constexpr int kSelSub = 8;           // copies of each histogram bin, chosen by lane
+constexpr int kSelLdsKeys = 32768;   // keys of one selection unit kept in LDS (128 KB of the 160 KB)
+constexpr int kSelSub = 4;           // copies of each histogram bin, chosen by lane (a multiple of 4)
+static_assert(kSelSub % 4 == 0 && 4 * 256 * kSelSub % (4 * kSelThreads) == 0, "histogram layout");
 
 enum SelSrc { kFromFixed = 0, kFromParts = 1, kFromScores = 2 };
 
@@ -186,14 +187,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
         }
         __syncthreads();
         if (wave == 0) {
-          // lane l holds bins 255-4l .. 252-4l (descending): the 32 copies of bins 252-4l .. 255-4l
-          // are contiguous, eight 16-byte reads
+          // lane l holds bins 255-4l .. 252-4l (descending): the 4 kSelSub copies of bins 252-4l ..
+          // 255-4l are contiguous, kSelSub 16-byte reads
+          constexpr int QB = kSelSub / 4;   // 16-byte reads per bin
           const uint4* hp = reinterpret_cast<const uint4*>(h + (252 - 4 * lane) * kSelSub);
           uint32_t c[4], tot = 0;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {   // bin 255 - 4 lane - k
-            const uint4 a = hp[2 * (3 - k)], b = hp[2 * (3 - k) + 1];
-            c[k] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+            c[k] = 0;
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+              const uint4 a = hp[QB * (3 - k) + q];
+              c[k] += (a.x + a.y) + (a.z + a.w);
+            }
             tot += c[k];
           }
           const uint32_t incl = wave_incl_sum(tot);
