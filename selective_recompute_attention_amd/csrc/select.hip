@@ -139,13 +139,23 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
     }
   } else {
     clear_hist();
-    for (int j = threadIdx.x; j < len; j += kSelThreads) {
-      const float sv = score_at(j);
-      if constexpr (SRC != kFromScores) srow[j] = sv;
-      const uint32_t u = order_key(sv);
-      if (in_lds) kl[j] = u;
-      kand &= u;
-      kor |= u;
+    // batches of eight positions per thread, every load of a batch in flight before any is used
+    constexpr int BT = 8;
+    for (int j0 = threadIdx.x; j0 < len; j0 += kSelThreads * BT) {
+      float sv[BT];
+#pragma unroll
+      for (int u = 0; u < BT; ++u) sv[u] = score_at(min(j0 + kSelThreads * u, len - 1));
+#pragma unroll
+      for (int u = 0; u < BT; ++u) {
+        const int j = j0 + kSelThreads * u;
+        if (j < len) {
+          if constexpr (SRC != kFromScores) srow[j] = sv[u];
+          const uint32_t key = order_key(sv[u]);
+          if (in_lds) kl[j] = key;
+          kand &= key;
+          kor |= key;
+        }
+      }
     }
   }
   // bits shared by every key of the unit (the same barrier publishes the keys in LDS)
