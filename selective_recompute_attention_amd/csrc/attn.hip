@@ -72,6 +72,8 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   int* tilecum;
+  int* merge;       // [n_groups][pieces]: the cut tile a piece merges (its first, when it is the last piece
+                    // over it), or -1
   uint16_t* part_o;   // fp16, scaled per vector
   float4* part_ml;    // (max, sum, scale, 0) per vector
   const uint16_t* qx;       // fresh queries before rotation (exact recomputation)
@@ -204,9 +206,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int P = attn_pieces_used(U, a.pieces);
   if (kvh == 0 && piece == 0)
     for (int t = threadIdx.x; t <= nt; t += 256) a.tilecum[(int64_t)req * (nt + 1) + t] = cum[t];
-  if (piece >= P) return;
+  int* merge = a.merge + (int64_t)group * a.pieces + piece;
+  if (piece >= P) {
+    if (threadIdx.x == 0) *merge = -1;
+    return;
+  }
   const int u0 = attn_piece_start(U, P, piece), u1 = attn_piece_start(U, P, piece + 1);
-  int t = 0;  // last tile with cum[t] <= u0
+  int t = 0;  // last tile with cum[t] <= u0: the tile holding unit u0
   {
     int hi = nt - 1;
     while (t < hi) {
@@ -215,6 +221,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
       else hi = mid - 1;
     }
   }
+  // a piece that starts inside its first tile and reaches that tile's end is the last of the pieces
+  // over it: it is the one whose merge work group combines the tile's partials
+  if (threadIdx.x == 0) *merge = (u0 > cum[t] && u1 >= cum[t + 1]) ? t : -1;
 
   // uniform base of this (request, KV head); per-thread byte offsets fit 32 bits (checked by the host)
   const char* kbase = reinterpret_cast<const char*>(a.kh + ((int64_t)req * a.L * a.Hkv + kvh) * D);
@@ -568,32 +577,40 @@ __device__ void exact_vector(const AttnArgs& a, int req, int kvh, int v) {
   if (dc == 0 && a.lse) a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = m + logf(l);
 }
 
-// Merge the pieces of every cut tile in key order. One thread per (query vector, 4 dims); the
-// pieces' loads go out in independent batches of eight. A group whose fp16 operands overflowed is
-// recomputed exactly here instead (every tile of it, cut or not).
+// Merge the pieces of every cut tile in key order: one work group per (group, piece, slab of query
+// vectors), for the tile whose merge the attention kernel gave that piece (the last piece over a cut
+// tile); work groups of pieces without one exit after a single load. One thread per (query vector,
+// 4 dims); the pieces' loads go out in independent batches of eight. A group whose fp16 operands
+// overflowed is recomputed exactly here instead: work group (piece, slab) takes that slab of the
+// group's tiles piece, piece + pieces, ...
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   constexpr int TPV = D / 4;                 // threads per query vector
   constexpr int VPB = 256 / TPV;             // query vectors per block
   constexpr int B = 8;
   const int slab = blockIdx.x % (128 / VPB);
-  const int gt = blockIdx.x / (128 / VPB);   // group-fastest (group, tile) index
-  const int group = gt % a.n_groups, tile = gt / a.n_groups;
+  const int gp = blockIdx.x / (128 / VPB);   // group-fastest (group, piece) index
+  const int group = gp % a.n_groups, piece = gp / a.n_groups;
   const int req = group / a.Hkv, kvh = group % a.Hkv;
   const int nt = a.n_tiles;
   const int* cum = a.tilecum + (int64_t)req * (nt + 1);
-  // the tile's unit range, the request's total and the group's flag as one batch of loads
-  int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt], pieces = a.pieces;
+  // the piece's merge tile and the group's flag as one batch of loads
+  int tile = a.merge[(int64_t)group * a.pieces + piece];
   unsigned fl = a.flags[group];
-  asm volatile("" : "+s"(c0), "+s"(c1), "+s"(U), "+s"(pieces), "+s"(fl) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
+  asm volatile("" : "+s"(tile), "+s"(fl) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
   const bool exact = fl == a.call_id;
-  if (tile == 0 && slab == 0 && threadIdx.x == 0 && a.fallback) a.fallback[group] = exact ? 1 : 0;
+  if (piece == 0 && slab == 0 && threadIdx.x == 0 && a.fallback) a.fallback[group] = exact ? 1 : 0;
   const int g = a.g, Mv = a.R * g;
   if (exact) {
-    const int v = tile * 128 + slab * VPB + (int)threadIdx.x / TPV;
-    if (v < Mv) exact_vector<D>(a, req, kvh, v);
+    for (int t = piece; t < nt; t += a.pieces) {
+      const int v = t * 128 + slab * VPB + (int)threadIdx.x / TPV;
+      if (v < Mv) exact_vector<D>(a, req, kvh, v);
+    }
     return;
   }
+  if (tile < 0) return;
+  // the tile's unit range and the request's total
+  const int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt], pieces = a.pieces;
   if (c1 <= c0) return;
   const int P = attn_pieces_used(U, pieces);
   const int i0 = attn_piece_of(U, P, c0), i1 = attn_piece_of(U, P, c1 - 1);
@@ -778,12 +795,14 @@ hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, con
   a.qop_blocks = qop_blocks;
   a.pieces = pieces;
   if (a.n_tiles > kAttnMaxTiles || qop_blocks < 4 * a.n_tiles || pieces < 1) return hipErrorInvalidValue;
+  // the pieces' merge tiles follow the tiles' unit prefix sums in the same buffer
+  a.merge = tilecum + (int64_t)n_req * (a.n_tiles + 1);
   const unsigned nblk = (unsigned)(a.n_groups * pieces);
   if (D == 128) k_attn_mfma<128><<<dim3(nblk), dim3(256), 0, st>>>(a);
   else k_attn_mfma<64><<<dim3(nblk), dim3(256), 0, st>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned ncomb = (unsigned)(a.n_groups * a.n_tiles * (D == 128 ? 16 : 8));
+  const unsigned ncomb = (unsigned)(a.n_groups * pieces * (D == 128 ? 16 : 8));
   if (D == 128) k_attn_combine<128><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   else k_attn_combine<64><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   return hipGetLastError();

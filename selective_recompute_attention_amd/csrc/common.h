@@ -321,7 +321,8 @@ hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int np
                          int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
                          const int* map = nullptr, int map_stride = 0);
 // qop: prepared query operand (qop_blocks blocks of 32 vectors per group); kh: fp16 copy of the fused
-// keys; tilecum: [n_req][tiles+1] ints; part_o ([..][D] fp16, scaled) / part_ml ((max, sum, scale, 0)):
+// keys; tilecum: [n_req][tiles+1] ints, then [n_groups][pieces] ints (each piece's merge tile); part_o
+// ([..][D] fp16, scaled) / part_ml ((max, sum, scale, 0)):
 // [n_groups][pieces][2][128] partial results. Groups whose flag equals call_id are recomputed exactly
 // from the fresh queries q ([n_req][q_rows][Hq][D] before rotation, row p when indexed, else row r)
 // and the bf16 K/V; fallback (optional, [n_req][Hkv]) receives 1 for those groups and 0 for the rest.
