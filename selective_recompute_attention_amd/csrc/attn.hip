@@ -577,32 +577,35 @@ __device__ void exact_vector(const AttnArgs& a, int req, int kvh, int v) {
   if (dc == 0 && a.lse) a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = m + logf(l);
 }
 
-// Merge the pieces of every cut tile in key order: one work group per (group, piece, slab of query
-// vectors), for the tile whose merge the attention kernel gave that piece (the last piece over a cut
-// tile); work groups of pieces without one exit after a single load. One thread per (query vector,
-// 4 dims); the pieces' loads go out in independent batches of eight. A group whose fp16 operands
-// overflowed is recomputed exactly here instead: work group (piece, slab) takes that slab of the
-// group's tiles piece, piece + pieces, ...
+// Merge the pieces of every cut tile in key order. One work group per (group, index, slab of query
+// vectors), the index running over the group's tiles when a group has fewer tiles than pieces, else
+// over its pieces: piece i then merges the tile the attention kernel gave it (the cut tile it is the
+// last piece over), and the work groups of pieces without one exit after a single load. One thread
+// per (query vector, 4 dims); the pieces' loads go out in independent batches of eight. A group
+// whose fp16 operands overflowed is recomputed exactly here instead: work group (index, slab) takes
+// that slab of the group's tiles index, index + stride, ... (stride: the index range).
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   constexpr int TPV = D / 4;                 // threads per query vector
   constexpr int VPB = 256 / TPV;             // query vectors per block
   constexpr int B = 8;
   const int slab = blockIdx.x % (128 / VPB);
-  const int gp = blockIdx.x / (128 / VPB);   // group-fastest (group, piece) index
-  const int group = gp % a.n_groups, piece = gp / a.n_groups;
+  const int gi = blockIdx.x / (128 / VPB);   // group-fastest (group, index) index
+  const int group = gi % a.n_groups, idx = gi / a.n_groups;
   const int req = group / a.Hkv, kvh = group % a.Hkv;
   const int nt = a.n_tiles;
+  const bool by_tile = nt <= a.pieces;
   const int* cum = a.tilecum + (int64_t)req * (nt + 1);
-  // the piece's merge tile and the group's flag as one batch of loads
-  int tile = a.merge[(int64_t)group * a.pieces + piece];
+  // the merge tile (by piece) and the group's flag as one batch of loads
+  int tile = by_tile ? idx : a.merge[(int64_t)group * a.pieces + idx];
   unsigned fl = a.flags[group];
   asm volatile("" : "+s"(tile), "+s"(fl) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
   const bool exact = fl == a.call_id;
-  if (piece == 0 && slab == 0 && threadIdx.x == 0 && a.fallback) a.fallback[group] = exact ? 1 : 0;
+  if (idx == 0 && slab == 0 && threadIdx.x == 0 && a.fallback) a.fallback[group] = exact ? 1 : 0;
   const int g = a.g, Mv = a.R * g;
   if (exact) {
-    for (int t = piece; t < nt; t += a.pieces) {
+    const int stride = by_tile ? nt : a.pieces;
+    for (int t = idx; t < nt; t += stride) {
       const int v = t * 128 + slab * VPB + (int)threadIdx.x / TPV;
       if (v < Mv) exact_vector<D>(a, req, kvh, v);
     }
@@ -802,7 +805,7 @@ hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, con
   else k_attn_mfma<64><<<dim3(nblk), dim3(256), 0, st>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned ncomb = (unsigned)(a.n_groups * pieces * (D == 128 ? 16 : 8));
+  const unsigned ncomb = (unsigned)(a.n_groups * min(a.n_tiles, pieces) * (D == 128 ? 16 : 8));
   if (D == 128) k_attn_combine<128><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   else k_attn_combine<64><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   return hipGetLastError();
