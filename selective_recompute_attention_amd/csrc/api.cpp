@@ -169,8 +169,9 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
     p.qop_blocks = 4 * p.n_tiles;
     p.pieces = attn_pieces(n_req, Hkv);
     p.qop = ao; ao = align256(ao + (size_t)groups * p.qop_blocks * 32 * 2 * D * sizeof(uint16_t));
-    // the tiles' unit prefix sums, then each piece's merge tile
-    p.tilecum = ao; ao = align256(ao + ((size_t)n_req * (p.n_tiles + 1) + (size_t)groups * p.pieces) * sizeof(int));
+    // the tiles' unit prefix sums, then each piece's merge record (four ints)
+    p.tilecum = ao;
+    ao = align256(ao + ((size_t)sra::attn_merge_offset(n_req, p.n_tiles) + (size_t)groups * p.pieces * 4) * sizeof(int));
     const int64_t slots = groups * p.pieces * 2 * 128;
     p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(uint16_t));
     p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float4));

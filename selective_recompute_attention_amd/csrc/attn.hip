@@ -72,8 +72,9 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   int* tilecum;
-  int* merge;       // [n_groups][pieces]: the cut tile a piece merges (its first, when it is the last piece
-                    // over it), or -1
+  int4* merge;      // [n_groups][pieces]: the cut tile a piece merges (its first, when it is the last piece
+                    // over it) as (tile, first piece over it, number of pieces, slot of the first piece's
+                    // partial), or tile -1
   uint16_t* part_o;   // fp16, scaled per vector
   float4* part_ml;    // (max, sum, scale, 0) per vector
   const uint16_t* qx;       // fresh queries before rotation (exact recomputation)
@@ -206,9 +207,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int P = attn_pieces_used(U, a.pieces);
   if (kvh == 0 && piece == 0)
     for (int t = threadIdx.x; t <= nt; t += 256) a.tilecum[(int64_t)req * (nt + 1) + t] = cum[t];
-  int* merge = a.merge + (int64_t)group * a.pieces + piece;
+  int4* merge = a.merge + (int64_t)group * a.pieces + piece;
   if (piece >= P) {
-    if (threadIdx.x == 0) *merge = -1;
+    if (threadIdx.x == 0) *merge = make_int4(-1, 0, 0, 0);
     return;
   }
   const int u0 = attn_piece_start(U, P, piece), u1 = attn_piece_start(U, P, piece + 1);
@@ -222,8 +223,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
   }
   // a piece that starts inside its first tile and reaches that tile's end is the last of the pieces
-  // over it: it is the one whose merge work group combines the tile's partials
-  if (threadIdx.x == 0) *merge = (u0 > cum[t] && u1 >= cum[t + 1]) ? t : -1;
+  // over it: it is the one whose merge work group combines the tile's partials. The pieces over the
+  // tile run from the one holding its first unit to this one; the first piece's partial of the tile
+  // is in slot 1 unless the tile is also where that piece starts.
+  if (threadIdx.x == 0) {
+    int4 rec = make_int4(-1, 0, 0, 0);
+    if (u0 > cum[t] && u1 >= cum[t + 1]) {
+      const int i0 = attn_piece_of(U, P, cum[t]);
+      rec = make_int4(t, i0, piece - i0 + 1, attn_piece_start(U, P, i0) < cum[t] ? 1 : 0);
+    }
+    *merge = rec;
+  }
 
   // uniform base of this (request, KV head); per-thread byte offsets fit 32 bits (checked by the host)
   const char* kbase = reinterpret_cast<const char*>(a.kh + ((int64_t)req * a.L * a.Hkv + kvh) * D);
@@ -579,104 +589,113 @@ __device__ void exact_vector(const AttnArgs& a, int req, int kvh, int v) {
 
 // Merge the pieces of every cut tile in key order. One work group per (group, index, slab of query
 // vectors), the index running over the group's tiles when a group has fewer tiles than pieces, else
-// over its pieces: piece i then merges the tile the attention kernel gave it (the cut tile it is the
-// last piece over), and the work groups of pieces without one exit after a single load. One thread
-// per (query vector, 4 dims); the pieces' loads go out in independent batches of eight. A group
-// whose fp16 operands overflowed is recomputed exactly here instead: work group (index, slab) takes
-// that slab of the group's tiles index, index + stride, ... (stride: the index range).
+// over its pieces: piece i then merges the cut tile of the record the attention kernel wrote for it
+// (the tile it is the last piece over, with the range of pieces over it), and the work groups of
+// pieces without one exit after a single load. One thread per (query vector, 8 dims); the pieces'
+// loads go out in independent batches of four. A group whose fp16 operands overflowed is recomputed
+// exactly here instead: work group (index, slab) takes that slab of the group's tiles index,
+// index + stride, ... (stride: the index range).
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
-  constexpr int TPV = D / 4;                 // threads per query vector
-  constexpr int VPB = 256 / TPV;             // query vectors per block
-  constexpr int B = 8;
-  const int slab = blockIdx.x % (128 / VPB);
-  const int gi = blockIdx.x / (128 / VPB);   // group-fastest (group, index) index
+  constexpr int TPV = D / 8;                 // threads per query vector
+  constexpr int VPB = 256 / TPV;             // query vectors per work group
+  constexpr int NSLAB = 128 / VPB;           // slabs per tile
+  constexpr int B = 4;                       // pieces per batch of loads
+  static_assert(B == 4, "the batch's keep-alive below lists four pieces");
+  const int slab = blockIdx.x % NSLAB;
+  const int gi = blockIdx.x / NSLAB;         // group-fastest (group, index) index
   const int group = gi % a.n_groups, idx = gi / a.n_groups;
   const int req = group / a.Hkv, kvh = group % a.Hkv;
   const int nt = a.n_tiles;
   const bool by_tile = nt <= a.pieces;
-  const int* cum = a.tilecum + (int64_t)req * (nt + 1);
-  // the merge tile (by piece) and the group's flag as one batch of loads
-  int tile = by_tile ? idx : a.merge[(int64_t)group * a.pieces + idx];
+  // the merge record (by piece) and the group's flag as one batch of loads
+  int4 rec = by_tile ? make_int4(idx, 0, 0, 0) : a.merge[(int64_t)group * a.pieces + idx];
   unsigned fl = a.flags[group];
-  asm volatile("" : "+s"(tile), "+s"(fl) : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
+  asm volatile("" : "+s"(rec.x), "+s"(rec.y), "+s"(rec.z), "+s"(rec.w), "+s"(fl)
+               : "s"(a.row_pos), "s"(a.part_ml), "s"(a.part_o));
   const bool exact = fl == a.call_id;
   if (idx == 0 && slab == 0 && threadIdx.x == 0 && a.fallback) a.fallback[group] = exact ? 1 : 0;
   const int g = a.g, Mv = a.R * g;
   if (exact) {
+    constexpr int VPE = 256 / (D / 4);   // vectors per pass of exact_vector (4 dims per thread)
     const int stride = by_tile ? nt : a.pieces;
-    for (int t = idx; t < nt; t += stride) {
-      const int v = t * 128 + slab * VPB + (int)threadIdx.x / TPV;
-      if (v < Mv) exact_vector<D>(a, req, kvh, v);
-    }
+    for (int t = idx; t < nt; t += stride)
+      for (int sub = 0; sub < VPB / VPE; ++sub) {
+        const int v = t * 128 + slab * VPB + sub * VPE + (int)threadIdx.x / (D / 4);
+        if (v < Mv) exact_vector<D>(a, req, kvh, v);
+      }
     return;
   }
-  if (tile < 0) return;
-  // the tile's unit range and the request's total
-  const int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt], pieces = a.pieces;
-  if (c1 <= c0) return;
-  const int P = attn_pieces_used(U, pieces);
-  const int i0 = attn_piece_of(U, P, c0), i1 = attn_piece_of(U, P, c1 - 1);
-  if (i0 == i1) return;  // written directly by its only piece
+  int tile = rec.x, i0 = rec.y, n = rec.z, slot0 = rec.w;
+  if (by_tile) {   // the tile's unit range and the request's total give its pieces
+    const int* cum = a.tilecum + (int64_t)req * (nt + 1);
+    const int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt];
+    if (c1 <= c0) return;
+    const int P = attn_pieces_used(U, a.pieces);
+    i0 = attn_piece_of(U, P, c0);
+    n = attn_piece_of(U, P, c1 - 1) - i0 + 1;
+    slot0 = attn_piece_start(U, P, i0) < c0 ? 1 : 0;
+  }
+  if (tile < 0 || n < 2) return;  // no cut tile, or one written directly by its only piece
   const int ql = slab * VPB + threadIdx.x / TPV, dc = threadIdx.x % TPV;
   const int v = tile * 128 + ql;
   if (v >= Mv) return;
   const int r = v / g, hq = kvh * g + v % g;
   // the row's position is loaded with the first batch of pieces and checked at the end
   const int pos_r = a.row_pos[(int64_t)req * a.R + r];
-  // piece i0 ends in this tile: its slot is 1 unless the tile is also where it starts
-  const int slot0 = attn_piece_start(U, P, i0) < c0 ? 1 : 0;
-  const int n = i1 - i0 + 1;
   auto pidx = [&](int k) { return part_index(a, group, i0 + k, k == 0 ? slot0 : 0) + ql; };
-  // online merge over batches of eight pieces; every load of a batch is independent
+  // online merge over batches of four pieces; every load of a batch is independent
   float M = -INFINITY, Ls = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < n; k0 += B) {
     float4 ml[B];
-    u32x2 hv[B];
+    u32x4 hv[B];
 #pragma unroll
     for (int k = 0; k < B; ++k) {   // clamped, unconditional loads: all in flight at once
       const int64_t pi = pidx(min(k0 + k, n - 1));
       ml[k] = a.part_ml[pi];
-      hv[k] = *reinterpret_cast<const u32x2*>(a.part_o + pi * D + 4 * dc);
+      hv[k] = *reinterpret_cast<const u32x4*>(a.part_o + pi * D + 8 * dc);
     }
-    // both halves of the batch are in flight before either is used (a piece skipped below would
-    // otherwise have its values loaded only after that test)
-    asm volatile("" ::"v"(hv[0][0]), "v"(hv[0][1]), "v"(hv[1][0]), "v"(hv[1][1]), "v"(hv[2][0]), "v"(hv[2][1]),
-                 "v"(hv[3][0]), "v"(hv[3][1]), "v"(hv[4][0]), "v"(hv[4][1]), "v"(hv[5][0]), "v"(hv[5][1]),
-                 "v"(hv[6][0]), "v"(hv[6][1]), "v"(hv[7][0]), "v"(hv[7][1]));
-    f32x4 ov[B];
+    // the whole batch is in flight before any of it is used (a piece skipped below would otherwise
+    // have its values loaded only after that test)
+    asm volatile("" ::"v"(hv[0][0]), "v"(hv[0][1]), "v"(hv[0][2]), "v"(hv[0][3]), "v"(hv[1][0]), "v"(hv[1][1]),
+                 "v"(hv[1][2]), "v"(hv[1][3]), "v"(hv[2][0]), "v"(hv[2][1]), "v"(hv[2][2]), "v"(hv[2][3]),
+                 "v"(hv[3][0]), "v"(hv[3][1]), "v"(hv[3][2]), "v"(hv[3][3]));
+    float mb = M;
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       if (k0 + k >= n) ml[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-      ov[k] = f32x4{h2f(hv[k][0] & 0xffffu), h2f(hv[k][0] >> 16), h2f(hv[k][1] & 0xffffu), h2f(hv[k][1] >> 16)} * ml[k].z;
+      mb = fmaxf(mb, ml[k].x);
     }
-    float mb = M;
-#pragma unroll
-    for (int k = 0; k < B; ++k) mb = fmaxf(mb, ml[k].x);
     if (mb == -INFINITY) continue;
     const float sc = exp2f(M - mb);  // 0 while nothing has been merged (M = -inf)
     Ls *= sc;
-    acc *= sc;
+    acc0 *= sc;
+    acc1 *= sc;
 #pragma unroll
     for (int k = 0; k < B; ++k) {
       if (ml[k].x != -INFINITY) {
         const float w = exp2f(ml[k].x - mb);
+        const f32x4 o0 = f32x4{h2f(hv[k][0] & 0xffffu), h2f(hv[k][0] >> 16), h2f(hv[k][1] & 0xffffu), h2f(hv[k][1] >> 16)} * ml[k].z;
+        const f32x4 o1 = f32x4{h2f(hv[k][2] & 0xffffu), h2f(hv[k][2] >> 16), h2f(hv[k][3] & 0xffffu), h2f(hv[k][3] >> 16)} * ml[k].z;
         Ls += ml[k].y * w;
-        acc += w * ov[k];
+        acc0 += w * o0;
+        acc1 += w * o1;
       }
     }
     M = mb;
   }
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  u32x2 w;
-  w[0] = pack_bf2(acc[0] * inv, acc[1] * inv);
-  w[1] = pack_bf2(acc[2] * inv, acc[3] * inv);
+  u32x4 w;
+  w[0] = pack_bf2(acc0[0] * inv, acc0[1] * inv);
+  w[1] = pack_bf2(acc0[2] * inv, acc0[3] * inv);
+  w[2] = pack_bf2(acc1[0] * inv, acc1[1] * inv);
+  w[3] = pack_bf2(acc1[2] * inv, acc1[3] * inv);
   // the merge is finished for every row (the asm keeps it out of the branch), and only then a row
   // outside the cache is dropped: nothing is written for it
-  asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(M), "v"(Ls));
+  asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(M), "v"(Ls));
   if (pos_r < 0) return;
-  *reinterpret_cast<u32x2*>(a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 4 * dc) = w;
+  *reinterpret_cast<u32x4*>(a.out + (((int64_t)req * a.R + r) * a.Hq + hq) * D + 8 * dc) = w;
   if (dc == 0 && a.lse)
     a.lse[((int64_t)req * a.R + r) * a.Hq + hq] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
@@ -798,14 +817,14 @@ hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, con
   a.qop_blocks = qop_blocks;
   a.pieces = pieces;
   if (a.n_tiles > kAttnMaxTiles || qop_blocks < 4 * a.n_tiles || pieces < 1) return hipErrorInvalidValue;
-  // the pieces' merge tiles follow the tiles' unit prefix sums in the same buffer
-  a.merge = tilecum + (int64_t)n_req * (a.n_tiles + 1);
+  // the pieces' merge records follow the tiles' unit prefix sums in the same buffer (16-byte aligned)
+  a.merge = reinterpret_cast<int4*>(tilecum + attn_merge_offset(n_req, a.n_tiles));
   const unsigned nblk = (unsigned)(a.n_groups * pieces);
   if (D == 128) k_attn_mfma<128><<<dim3(nblk), dim3(256), 0, st>>>(a);
   else k_attn_mfma<64><<<dim3(nblk), dim3(256), 0, st>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned ncomb = (unsigned)(a.n_groups * min(a.n_tiles, pieces) * (D == 128 ? 16 : 8));
+  const unsigned ncomb = (unsigned)(a.n_groups * min(a.n_tiles, pieces) * (D == 128 ? 8 : 4));
   if (D == 128) k_attn_combine<128><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   else k_attn_combine<64><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   return hipGetLastError();

@@ -211,6 +211,10 @@ __host__ __device__ __forceinline__ int attn_piece_start(int U, int P, int i) {
 __host__ __device__ __forceinline__ int attn_piece_of(int U, int P, int u) {
   return (int)(((int64_t)(u + 1) * P - 1) / U);
 }
+// ints before the pieces' 16-byte merge records in the attention's tilecum buffer
+__host__ __device__ __forceinline__ int64_t attn_merge_offset(int n_req, int n_tiles) {
+  return ((int64_t)n_req * (n_tiles + 1) + 3) & ~(int64_t)3;
+}
 
 }  // namespace sra
 
@@ -321,7 +325,8 @@ hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int np
                          int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
                          const int* map = nullptr, int map_stride = 0);
 // qop: prepared query operand (qop_blocks blocks of 32 vectors per group); kh: fp16 copy of the fused
-// keys; tilecum: [n_req][tiles+1] ints, then [n_groups][pieces] ints (each piece's merge tile); part_o
+// keys; tilecum: [n_req][tiles+1] ints, then (from int attn_merge_offset) [n_groups][pieces] int4 (each
+// piece's merge record); part_o
 // ([..][D] fp16, scaled) / part_ml ((max, sum, scale, 0)):
 // [n_groups][pieces][2][128] partial results. Groups whose flag equals call_id are recomputed exactly
 // from the fresh queries q ([n_req][q_rows][Hq][D] before rotation, row p when indexed, else row r)
