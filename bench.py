@@ -164,8 +164,10 @@ class FusedStep:
     """Device inputs and outputs of one workload's fusion step, and the step itself.
 
     Layer 0 runs sra_fused_layer with the critical-layer scoring (and the chunks' anchors); a later
-    layer l takes the first N_l of the same ranking (sra_select_topn on the layer-0 scores) and runs
-    sra_fused_layer on those rows. `replicas` copies of every input rotate between steps."""
+    layer l takes the first N_l of the same ranking and runs sra_fused_layer on those rows. The later
+    layers' rows come from one sra_select_topn_nested launch among layer 0's rows, issued before layer
+    1 (the sets nest: each is the Top-N_l of the same scores). `replicas` copies of every input rotate
+    between steps."""
 
     def __init__(self, sra, w, replicas):
         import torch
@@ -220,11 +222,13 @@ class FusedStep:
                                 n_select=None if self.quotas is not None else self.counts[0], quotas=self.quotas,
                                 scores=extra["scores"], anchors_k=cfg.anchors_k, anchor_rows=extra["anchors"], **kw)
             else:
-                if sel_events is not None:
-                    hip.record(ctypes.c_void_p(sel_events[l][0]), sp)
-                sra.select_topn(extra["scores"], self.counts[l], None, None, self.Lq, outs["row_pos"])
-                if sel_events is not None:
-                    hip.record(ctypes.c_void_p(sel_events[l][1]), sp)
+                if l == 1:   # every later layer's rows, in one launch
+                    if sel_events is not None:
+                        hip.record(ctypes.c_void_p(sel_events[l][0]), sp)
+                    sra.select_topn_nested(extra["scores"], layers[0][1]["row_pos"], self.counts[0], self.Lq,
+                                           self.counts[1:], [o["row_pos"] for _, o in layers[1:]])
+                    if sel_events is not None:
+                        hip.record(ctypes.c_void_p(sel_events[l][1]), sp)
                 sra.fused_layer(self.shape, **kw)
 
     # ------------------------------------------------------------------ algorithmic work
@@ -297,7 +301,7 @@ class FusedStep:
             st["s3"].append(float(np.mean([span(i, l, 4, 5) for i in range(n_ev)])))
             st["s4"].append(float(np.mean([span(i, l, 6, 7) for i in range(n_ev)])))
             st["sel"].append(float(np.mean([hip.elapsed_ms(ctypes.c_void_p(sev[i][l][0]), ctypes.c_void_p(sev[i][l][1]))
-                                             for i in range(n_ev)])) if l else 0.0)
+                                             for i in range(n_ev)])) if l == 1 else 0.0)
         # layer 0's stage 0 is empty when S1 runs inside the scoring launch (bf16): S1+S2 as one span
         s12_0 = float(np.mean([span(i, 0, 0, 3) for i in range(n_ev)]))
         rps = self.row_positions()

@@ -257,6 +257,23 @@ int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t
                     const int32_t* chunk_quota, const sra_chunk* chunks, int32_t n_chunks,
                     int32_t Lq, int32_t* row_pos, hipStream_t stream);
 
+/* Nested Top-N of later layers (the recompute set shrinks layer by layer, each layer filtering
+ * the previous layer's set: KVCache reuse 01 §1.3.3 gradual filtering; QCFuse technical summary (zh),
+ * §2.A: the Top-N of one critical-layer ranking). For every level l and request q: the n_select[l]
+ * rows of prev_rows[q][0 .. n_prev) whose scores scores[q][row] rank first under the stable order
+ * by descending score (ties: the lower position first), written ascending, then the Lq query rows
+ * prev_rows[q][n_prev .. n_prev + Lq). When prev_rows holds the Top-n_prev of the same scores
+ * (as sra_score_select and sra_select_topn write it, ascending), level l equals sra_select_topn
+ * with n_select[l] on the whole context, at the cost of a selection among n_prev rows. All levels
+ * run as one launch.
+ * scores: [n_req][ctx_len] float32, not NaN. prev_rows: [n_req][prev_stride] int32, prev_stride >=
+ * n_prev + Lq, entries < n_prev in [0, ctx_len). n_select: host [n_levels], each in [0, n_prev].
+ * row_pos: host [n_levels] device pointers, level l [n_req][n_select[l] + Lq] int32 (outputs may
+ * not overlap prev_rows). Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_ALIAS, SRA_E_HIP. */
+int sra_select_topn_nested(const float* scores, int32_t n_req, int32_t ctx_len, const int32_t* prev_rows,
+                           int32_t prev_stride, int32_t n_prev, int32_t Lq, int32_t n_levels,
+                           const int32_t* n_select, int32_t* const* row_pos, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ Cache-Craft selection */
 
 /* Attention statistics of a full causal prefill, per token and chunk (Cache-Craft: the

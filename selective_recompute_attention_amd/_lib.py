@@ -78,6 +78,8 @@ _SIGS = {
                                     _P, _P, _P, _c.c_size_t, _P]),
     "sra_select_topn": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.POINTER(_c.c_int32),
                                    _c.POINTER(Chunk), _c.c_int32, _c.c_int32, _P, _P]),
+    "sra_select_topn_nested": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _P, _c.c_int32, _c.c_int32, _c.c_int32,
+                                          _c.c_int32, _c.POINTER(_c.c_int32), _c.POINTER(_P), _P]),
     "sra_scatter_kv": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _P, _c.c_int32, _P, _P,
                                   _c.c_int32, _P]),
     "sra_hkvd_select": (_c.c_int, [_c.POINTER(Shape), _c.c_int32, _P, _P, _c.c_int32, _P, _P, _P, _c.c_int32,

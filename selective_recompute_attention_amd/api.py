@@ -14,7 +14,7 @@ from ._lib import (DTYPE_BF16, DTYPE_F32, Chunk, LayerArgs, SRAError, Shape, che
 
 __all__ = ["make_shape", "select_count", "workspace_size", "anchor_workspace_size", "fuse_rerotate", "extract_anchors", "anchor_prefix",
            "stats_workspace_size", "chunk_attention_stats", "prefix_overlap", "cachecraft_count",
-           "score_select", "select_topn", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
+           "score_select", "select_topn", "select_topn_nested", "scatter_kv", "hkvd_select", "sparse_causal_attn", "fused_layer",
            "fused_layer_static",
            "pipelined_layers", "create_events", "destroy_events", "check_rows", "chunk_array", "SRAError"]
 
@@ -159,6 +159,19 @@ def select_topn(scores, n_select, quotas, chunks, Lq, row_pos, stream=None):
         carr, n_chunks = None, 0
     check(lib().sra_select_topn(_ptr(scores), n_req, ctx_len, -1 if n_select is None else int(n_select), qp,
                                 carr, n_chunks, int(Lq), _ptr(row_pos), _stream(stream)))
+
+
+def select_topn_nested(scores, prev_rows, n_prev, Lq, n_select, row_pos, stream=None):
+    """Nested Top-N among the first n_prev rows of prev_rows [n_req][>= n_prev + Lq]: level l writes
+    row_pos[l] [n_req][n_select[l] + Lq]; see sra_select_topn_nested."""
+    n_req, ctx_len = scores.shape
+    n_levels = len(n_select)
+    if len(row_pos) != n_levels:
+        raise ValueError("one row_pos tensor per level")
+    counts = (ctypes.c_int32 * n_levels)(*[int(n) for n in n_select])
+    outs = (ctypes.c_void_p * n_levels)(*[_ptr(r) for r in row_pos])
+    check(lib().sra_select_topn_nested(_ptr(scores), n_req, ctx_len, _ptr(prev_rows), prev_rows.stride(0),
+                                       int(n_prev), int(Lq), n_levels, counts, outs, _stream(stream)))
 
 
 def scatter_kv(shape, k_new, v_new, row_pos, k_fused, v_fused, stream=None):

@@ -303,9 +303,11 @@ int do_select(int n_req, int Lctx, int Lq, int R, int N, const int32_t* quota, c
       tab.quota[tab.n] = u.quota;
       tab.out_off[tab.n] = u.off;
       tab.writes_query[tab.n] = u.wq;
+      tab.out[tab.n] = row_pos + (int64_t)u.req * R;
+      tab.rows[tab.n] = R;
       ++tab.n;
     }
-    hipError_t e = sra::launch_select(tab, fx, nparts, Lctx, Lq, R, parts, scores, row_pos, st);
+    hipError_t e = sra::launch_select(tab, fx, nparts, Lctx, Lq, Lctx, parts, scores, st);
     if (e != hipSuccess) return hip_fail(e, "selection launch");
   }
   return SRA_OK;
@@ -330,9 +332,11 @@ int do_hkvd(const sra_shape* s, int n_req, const void* kn, const void* vn, int f
       tab.quota[tab.n] = n_keep;
       tab.out_off[tab.n] = 0;
       tab.writes_query[tab.n] = 1;
+      tab.out[tab.n] = rows_out + (int64_t)q * (n_keep + Lq);
+      tab.rows[tab.n] = n_keep + Lq;
       ++tab.n;
     }
-    e = sra::launch_select(tab, nullptr, 0, n_prev, Lq, n_keep + Lq, nullptr, dev, rows_out, st, prev, R_prev);
+    e = sra::launch_select(tab, nullptr, 0, n_prev, Lq, n_prev, nullptr, dev, st, prev, R_prev);
     if (e != hipSuccess) return hip_fail(e, "selection launch");
   }
   return SRA_OK;
@@ -804,6 +808,51 @@ int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t
   if ((rc = do_select(n_req, ctx_len, Lq, N + Lq, N, chunk_quota, chunks, n_chunks, nullptr, 0, nullptr,
                       const_cast<float*>(scores), row_pos, stream)))
     return rc;
+  return ok();
+}
+
+int sra_select_topn_nested(const float* scores, int32_t n_req, int32_t ctx_len, const int32_t* prev_rows,
+                           int32_t prev_stride, int32_t n_prev, int32_t Lq, int32_t n_levels,
+                           const int32_t* n_select, int32_t* const* row_pos, hipStream_t stream) {
+  if (!scores) return fail(SRA_E_NULL, "scores is NULL");
+  if (!prev_rows) return fail(SRA_E_NULL, "prev_rows is NULL");
+  if (!n_select || !row_pos) return fail(SRA_E_NULL, "n_select or row_pos is NULL");
+  if (n_req <= 0 || ctx_len < 1 || Lq < 0 || n_levels < 1 || n_prev < 0 || n_prev > ctx_len)
+    return fail(SRA_E_SHAPE, "need n_req > 0, ctx_len > 0, Lq >= 0, n_levels > 0, 0 <= n_prev <= ctx_len");
+  if ((int64_t)prev_stride < (int64_t)n_prev + Lq)
+    return fail(SRA_E_SHAPE, "prev_stride %d is below n_prev + Lq = %lld", prev_stride, (long long)n_prev + Lq);
+  const size_t pb = ((size_t)(n_req - 1) * prev_stride + n_prev + Lq) * sizeof(int32_t);
+  for (int l = 0; l < n_levels; ++l) {
+    if (n_select[l] < 0 || n_select[l] > n_prev)
+      return fail(SRA_E_SHAPE, "level %d selects %d of %d rows", l, n_select[l], n_prev);
+    if (!row_pos[l]) return fail(SRA_E_NULL, "row_pos[%d] is NULL", l);
+    if (overlap(row_pos[l], (size_t)n_req * (n_select[l] + Lq) * sizeof(int32_t), prev_rows, pb))
+      return fail(SRA_E_ALIAS, "row_pos[%d] overlaps prev_rows", l);
+  }
+  // one selection unit per (level, request): the unit's indices are prev_rows' entries
+  sra::SelTab tab;
+  std::memset(&tab, 0, sizeof(tab));
+  auto flush = [&]() -> int {
+    hipError_t e = sra::launch_select(tab, nullptr, 0, n_prev, Lq, ctx_len, nullptr, const_cast<float*>(scores),
+                                      stream, prev_rows, prev_stride, true);
+    if (e != hipSuccess) return hip_fail(e, "selection launch");
+    std::memset(&tab, 0, sizeof(tab));
+    return SRA_OK;
+  };
+  int rc;
+  for (int l = 0; l < n_levels; ++l)
+    for (int q = 0; q < n_req; ++q) {
+      tab.req[tab.n] = q;
+      tab.begin[tab.n] = 0;
+      tab.len[tab.n] = n_prev;
+      tab.quota[tab.n] = n_select[l];
+      tab.out_off[tab.n] = 0;
+      tab.writes_query[tab.n] = 1;
+      tab.out[tab.n] = row_pos[l] + (int64_t)q * (n_select[l] + Lq);
+      tab.rows[tab.n] = n_select[l] + Lq;
+      if (++tab.n == sra::kMaxEntries && (rc = flush())) return rc;
+    }
+  if (tab.n > 0 && (rc = flush())) return rc;
   return ok();
 }
 

@@ -35,6 +35,8 @@ struct SelTab {
   int quota[kMaxEntries];
   int out_off[kMaxEntries];
   int writes_query[kMaxEntries];
+  int* out[kMaxEntries];    // the entry's output row: out_off + i for its selected rows, rows - Lq + i
+  int rows[kMaxEntries];    // for the query rows
 };
 
 // The entry owning block blk: the number of entries i >= 1 with blk0[i] <= blk (blk0 ascends),
@@ -319,11 +321,13 @@ hipError_t launch_score_f32(int D, const ChunkTab& tab_req, int n_req, int Lq, i
 hipError_t launch_colsum_f32(int n_req, int rows, int Lctx, const float* prob, float* parts,
                              hipStream_t st);
 // Scores come from fixed-point totals (fx), from nparts float partials added in order, or (both
-// absent) from `scores` itself. With map, every written index i becomes map[req * map_stride + i]
-// (the query rows are indices Lctx .. Lctx + Lq - 1).
+// absent) from `scores` itself, row req at scores + req * sstride. With map, every written index i
+// becomes map[req * map_stride + i] (the query rows are indices Lctx .. Lctx + Lq - 1); with gather
+// (map required) the score of unit index j is the stored score of row map[j] instead of that of j.
+// Entry e writes into tab.out[e] (tab.rows[e] entries, the query rows last).
 hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
-                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
-                         const int* map = nullptr, int map_stride = 0);
+                         int sstride, const float* parts, float* scores, hipStream_t st,
+                         const int* map = nullptr, int map_stride = 0, bool gather = false);
 // qop: prepared query operand (qop_blocks blocks of 32 vectors per group); kh: fp16 copy of the fused
 // keys; tilecum: [n_req][tiles+1] ints, then (from int attn_merge_offset) [n_groups][pieces] int4 (each
 // piece's merge record); part_o

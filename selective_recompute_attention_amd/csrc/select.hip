@@ -3,7 +3,7 @@
 // sort by descending score, Cache-Craft CSDN article §2.2.2, so the lower index wins).
 //
 // One block of 1024 threads per selection unit (a whole request, or one chunk of a request when
-// per-chunk quotas are given). The block first forms the scores (fixed-point totals over KV heads,
+// per-chunk quotas are given, or one (level, request) of a nested selection among earlier rows). The block first forms the scores (fixed-point totals over KV heads,
 // or per-head float partials added in a fixed order), then finds the score of the N-th best token
 // exactly with an 8-bit radix select over order-preserving 32-bit keys (leading bytes shared by
 // every key are skipped), and finally writes, in ascending position order, every token above that
@@ -24,20 +24,25 @@ constexpr int kSelLdsKeys = 32768;   // keys of one selection unit kept in LDS (
 constexpr int kSelSub = 4;           // copies of each histogram bin, chosen by lane (a multiple of 4)
 static_assert(kSelSub % 4 == 0 && 4 * 256 * kSelSub % (4 * kSelThreads) == 0, "histogram layout");
 
-enum SelSrc { kFromFixed = 0, kFromParts = 1, kFromScores = 2 };
+// Score sources: fixed-point totals, per-head partials (both written back as the float scores), the
+// scores themselves, or the scores of the rows an index map lists (unit index j -> map[j]).
+enum SelSrc { kFromFixed = 0, kFromParts = 1, kFromScores = 2, kFromGather = 3 };
 
+// Order-preserving key of a score; -0 and +0 are equal scores (their ties go by position) and get
+// the key of +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 template <int SRC>
 __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsigned long long* __restrict__ fx,
-                                                        int nparts, int Lctx, int Lq, int R,
+                                                        int nparts, int Lctx, int Lq, int sstride,
                                                         const float* __restrict__ parts,
                                                         float* __restrict__ scores,
-                                                        int* __restrict__ row_pos,
                                                         const int* __restrict__ map, int map_stride) {
+  constexpr bool kWritesScores = SRC == kFromFixed || SRC == kFromParts;
   constexpr int NW = kSelThreads / 64;
   constexpr int KREG = 4;    // keys per thread held in registers (units up to 4096 keys)
   // one histogram per key byte, kSelSub copies of each bin (lanes of a wave that hit the same bin,
@@ -48,13 +53,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
   __shared__ uint32_t wsum[2][NW];
   const int e = blockIdx.x;
   const int req = tab.req[e], begin = tab.begin[e], len = tab.len[e];
-  const int quota = tab.quota[e], off = tab.out_off[e], wq = tab.writes_query[e];
+  const int quota = tab.quota[e], off = tab.out_off[e], wq = tab.writes_query[e], R = tab.rows[e];
+  int* out = tab.out[e];
   // every argument, fetched as one batch of scalar loads before the first global load
   asm volatile("" ::"s"(req), "s"(begin), "s"(len), "s"(quota), "s"(off), "s"(wq), "s"(fx), "s"(parts),
-               "s"(scores), "s"(row_pos), "s"(map), "s"(map_stride), "s"(nparts), "s"(Lctx), "s"(Lq), "s"(R));
-  float* srow = scores + (int64_t)req * Lctx + begin;
-  int* out = row_pos + (int64_t)req * R;
+               "s"(scores), "s"(out), "s"(map), "s"(map_stride), "s"(nparts), "s"(Lctx), "s"(Lq), "s"(R),
+               "s"(sstride));
+  float* srow = scores + (int64_t)req * sstride + begin;
   const int* mrow = map ? map + (int64_t)req * map_stride : nullptr;   // index -> written value
+  // score of unit index j where it is stored (written back above for the computed sources)
+  auto stored = [&](int j) -> float {
+    if constexpr (SRC == kFromGather) return srow[mrow[begin + j]];
+    else return srow[j];
+  };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // thread t owns the contiguous positions [jlo, jhi): block prefix sums of per-thread counts then
   // give ascending output slots
@@ -83,7 +94,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
       }
       return sv;
     } else {
-      return srow[j];
+      return stored(j);
     }
   };
 
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
       if (nparts <= 0) clear_hist();
     } else {
 #pragma unroll
-      for (int i = 0; i < KREG; ++i) sv[i] = srow[min((int)threadIdx.x + kSelThreads * i, len - 1)];
+      for (int i = 0; i < KREG; ++i) sv[i] = stored(min((int)threadIdx.x + kSelThreads * i, len - 1));
       clear_hist();
     }
 #pragma unroll
@@ -131,7 +142,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
       const int j = threadIdx.x + kSelThreads * i;
       if (j < len) {
         const uint32_t u = order_key(sv[i]);
-        if constexpr (SRC != kFromScores) srow[j] = sv[i];
+        if constexpr (kWritesScores) srow[j] = sv[i];
         kl[j] = u;
         kand &= u;
         kor |= u;
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
       for (int u = 0; u < BT; ++u) {
         const int j = j0 + kSelThreads * u;
         if (j < len) {
-          if constexpr (SRC != kFromScores) srow[j] = sv[u];
+          if constexpr (kWritesScores) srow[j] = sv[u];
           const uint32_t key = order_key(sv[u]);
           if (in_lds) kl[j] = key;
           kand &= key;
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
     for (int i = 0; i < KREG; ++i) kreg[i] = kl[min(jlo + i, len - 1)];
   }
   // keys of large units are read back from LDS, or re-derived from the scores written above
-  auto key_at = [&](int j) -> uint32_t { return in_lds ? kl[j] : order_key(srow[j]); };
+  auto key_at = [&](int j) -> uint32_t { return in_lds ? kl[j] : order_key(stored(j)); };
 
   if (quota > 0 && len > 0) {
     uint32_t thr = 0, need_eq = 0;
@@ -295,18 +306,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
 }  // namespace
 
 hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int nparts, int Lctx, int Lq,
-                         int R, const float* parts, float* scores, int* row_pos, hipStream_t st,
-                         const int* map, int map_stride) {
+                         int sstride, const float* parts, float* scores, hipStream_t st, const int* map,
+                         int map_stride, bool gather) {
   if (tab.n == 0) return hipSuccess;
+  if (gather && !map) return hipErrorInvalidValue;
   const dim3 g(tab.n), b(kSelThreads);
   if (fx)
-    k_select<kFromFixed><<<g, b, 0, st>>>(tab, fx, 0, Lctx, Lq, R, parts, scores, row_pos, map, map_stride);
+    k_select<kFromFixed><<<g, b, 0, st>>>(tab, fx, 0, Lctx, Lq, sstride, parts, scores, map, map_stride);
   else if (nparts > 0)
-    k_select<kFromParts><<<g, b, 0, st>>>(tab, nullptr, nparts, Lctx, Lq, R, parts, scores, row_pos, map,
-                                          map_stride);
+    k_select<kFromParts><<<g, b, 0, st>>>(tab, nullptr, nparts, Lctx, Lq, sstride, parts, scores, map, map_stride);
+  else if (gather)
+    k_select<kFromGather><<<g, b, 0, st>>>(tab, nullptr, 0, Lctx, Lq, sstride, parts, scores, map, map_stride);
   else
-    k_select<kFromScores><<<g, b, 0, st>>>(tab, nullptr, 0, Lctx, Lq, R, parts, scores, row_pos, map,
-                                           map_stride);
+    k_select<kFromScores><<<g, b, 0, st>>>(tab, nullptr, 0, Lctx, Lq, sstride, parts, scores, map, map_stride);
   return hipGetLastError();
 }
 

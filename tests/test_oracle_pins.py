@@ -246,6 +246,13 @@ def test_zero_query_gives_uniform_scores_and_first_indices():
     np.testing.assert_array_equal(O.select_topn(s, 5), [0, 1, 2, 3, 4])
 
 
+def test_select_topn_signed_zeros_are_equal_scores():
+    # -0 and +0 compare equal, so among zero scores the lower index wins whatever the sign
+    np.testing.assert_array_equal(O.select_topn([0.0, -0.0, 1.0, -0.0], 2), [0, 2])
+    np.testing.assert_array_equal(O.select_topn([-0.0, 0.0, 1.0, 0.0], 3), [0, 1, 2])
+    np.testing.assert_array_equal(O.select_topn([-1.0, 0.0, -0.0, 2.0], 3), [1, 2, 3])
+
+
 def test_scores_use_group_kv_head():
     # Zeroing KV head 1 makes every Q head of group 1 uniform over the context; group 0 is untouched.
     w = make_custom(dtype="f32", chunk_lens=(12,), query_len=2, n_q_heads=4, n_kv_heads=2, head_dim=8)
