@@ -267,7 +267,8 @@ int sra_select_topn(const float* scores, int32_t n_req, int32_t ctx_len, int32_t
  * with n_select[l] on the whole context, at the cost of a selection among n_prev rows. All levels
  * run as one launch.
  * scores: [n_req][ctx_len] float32, not NaN. prev_rows: [n_req][prev_stride] int32, prev_stride >=
- * n_prev + Lq, entries < n_prev in [0, ctx_len). n_select: host [n_levels], each in [0, n_prev].
+ * n_prev + Lq, entries < n_prev in [0, ctx_len) (an entry outside it reads a clamped score and
+ * leaves that level's choice unspecified). n_select: host [n_levels], each in [0, n_prev].
  * row_pos: host [n_levels] device pointers, level l [n_req][n_select[l] + Lq] int32 (outputs may
  * not overlap prev_rows). Errors: SRA_E_NULL, SRA_E_SHAPE, SRA_E_ALIAS, SRA_E_HIP. */
 int sra_select_topn_nested(const float* scores, int32_t n_req, int32_t ctx_len, const int32_t* prev_rows,

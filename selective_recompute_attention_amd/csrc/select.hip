@@ -3,8 +3,9 @@
 // sort by descending score, Cache-Craft CSDN article §2.2.2, so the lower index wins).
 //
 // One block of 1024 threads per selection unit (a whole request, or one chunk of a request when
-// per-chunk quotas are given, or one (level, request) of a nested selection among earlier rows). The block first forms the scores (fixed-point totals over KV heads,
-// or per-head float partials added in a fixed order), then finds the score of the N-th best token
+// per-chunk quotas are given, or one (level, request) of a nested selection among earlier rows).
+// The block first forms the scores (fixed-point totals over KV heads, or per-head float partials
+// added in a fixed order), then finds the score of the N-th best token
 // exactly with an 8-bit radix select over order-preserving 32-bit keys (leading bytes shared by
 // every key are skipped), and finally writes, in ascending position order, every token above that
 // score plus the lowest-index tokens equal to it. All decisions are integer comparisons of the
@@ -61,9 +62,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelTab tab, const unsign
                "s"(sstride));
   float* srow = scores + (int64_t)req * sstride + begin;
   const int* mrow = map ? map + (int64_t)req * map_stride : nullptr;   // index -> written value
-  // score of unit index j where it is stored (written back above for the computed sources)
+  // score of unit index j where it is stored (written back above for the computed sources); a
+  // gathered row outside the score row is clamped into it, so no read leaves the scores
   auto stored = [&](int j) -> float {
-    if constexpr (SRC == kFromGather) return srow[mrow[begin + j]];
+    if constexpr (SRC == kFromGather) return srow[min((uint32_t)mrow[begin + j], (uint32_t)(sstride - 1))];
     else return srow[j];
   };
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
