@@ -121,8 +121,8 @@ struct Plan {
   // score (f32)
   size_t prob = 0, parts = 0;
   // attention (bf16): prepared query operand, tile prefix sums, partial results
-  int n_tiles = 0, qop_blocks = 0, pieces = 1;
-  size_t qop = 0, tilecum = 0, part_o = 0, part_ml = 0;
+  int n_tiles = 0, qop_blocks = 0, pieces = 1, n_groups = 0;
+  size_t qop = 0, tilecum = 0, queue = 0, part_o = 0, part_ml = 0;
   size_t score_end = 0, attn_end = 0, total = 0;
 };
 
@@ -169,9 +169,11 @@ Plan make_plan(const sra_shape* s, int n_req, int n_chunks, int L, int R, int Lq
     p.qop_blocks = 4 * p.n_tiles;
     p.pieces = attn_pieces(n_req, Hkv);
     p.qop = ao; ao = align256(ao + (size_t)groups * p.qop_blocks * 32 * 2 * D * sizeof(uint16_t));
-    // the tiles' unit prefix sums, then each piece's merge record (four ints)
+    // the tiles' unit prefix sums, then each piece's merge record (four ints), then the groups' queues
     p.tilecum = ao;
-    ao = align256(ao + ((size_t)sra::attn_merge_offset(n_req, p.n_tiles) + (size_t)groups * p.pieces * 4) * sizeof(int));
+    p.n_groups = (int)groups;
+    p.queue = ao + (size_t)sra::attn_queue_offset(n_req, p.n_tiles, (int)groups, p.pieces) * sizeof(int);
+    ao = align256(p.queue + (size_t)groups * sizeof(int));
     const int64_t slots = groups * p.pieces * 2 * 128;
     p.part_o = ao; ao = align256(ao + (size_t)slots * D * sizeof(uint16_t));
     p.part_ml = ao; ao = align256(ao + (size_t)slots * sizeof(float4));
@@ -196,6 +198,10 @@ sra::F16Shadow shadow_of(const sra_shape* s, void* ws, const Plan& p, unsigned c
   sh.kh = reinterpret_cast<uint16_t*>(wsp(ws, p.k16));
   sh.flags = reinterpret_cast<unsigned*>(wsp(ws, p.flags));
   sh.call_id = call_id;
+  if (p.n_groups > 0) {   // the attention's queues (the scatter before each attention empties them)
+    sh.queue = reinterpret_cast<int*>(wsp(ws, p.queue));
+    sh.n_queue = p.n_groups;
+  }
   return sh;
 }
 
@@ -464,6 +470,7 @@ int do_attn(const sra_shape* s, int n_req, const void* q, int q_rows, int indexe
     ex.call_id = call_id;
     ex.fallback = fallback;
     ex.base = s->rope_base;
+    ex.queue_ready = 1;   // both callers ran the row scatter with the plan's shadow just before
     e = sra::launch_attn_bf16(D, n_req, Hq, Hkv, R, L, reinterpret_cast<const uint16_t*>(wsp(ws, p.qop)),
                               p.qop_blocks, row_pos, reinterpret_cast<const uint16_t*>(wsp(ws, p.k16)),
                               (const uint16_t*)kf, (const uint16_t*)vf,

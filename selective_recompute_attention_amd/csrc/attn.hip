@@ -84,6 +84,9 @@ struct AttnArgs {
   int q_rows, q_indexed;
   int n_req, Hq, Hkv, g, R, L;
   int n_groups, n_tiles, qop_blocks, pieces;
+  int dynamic;      // whole tiles from each group's queue (largest first) instead of the static split
+  int* queue;       // [n_groups] next item of each group's queue (dynamic), zeroed before the launch
+  int comb_idx;     // index range of the merge kernel's grid (its exact path strides by it)
   Theta th;
 };
 
@@ -204,35 +207,49 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     __syncthreads();
   }
   const int U = cum[nt];
-  const int P = attn_pieces_used(U, a.pieces);
   if (kvh == 0 && piece == 0)
     for (int t = threadIdx.x; t <= nt; t += 256) a.tilecum[(int64_t)req * (nt + 1) + t] = cum[t];
-  int4* merge = a.merge + (int64_t)group * a.pieces + piece;
-  if (piece >= P) {
-    if (threadIdx.x == 0) *merge = make_int4(-1, 0, 0, 0);
-    return;
-  }
-  const int u0 = attn_piece_start(U, P, piece), u1 = attn_piece_start(U, P, piece + 1);
-  int t = 0;  // last tile with cum[t] <= u0: the tile holding unit u0
-  {
-    int hi = nt - 1;
-    while (t < hi) {
-      const int mid = (t + hi + 1) >> 1;
-      if (cum[mid] <= u0) t = mid;
-      else hi = mid - 1;
+  // Static split: this piece's unit range [u0, u1) and the tile holding u0. Dynamic: every work
+  // group of the group takes whole tiles from its queue, largest first (item k is tile nt - 1 - k,
+  // tiles grow with their last position), until the queue is empty; a work group that finishes a
+  // tile early takes the next one, so uneven speeds of the work groups even out.
+  const bool dyn = a.dynamic != 0;
+  __shared__ int s_item;
+  int u0 = 0, u1 = 0, t = 0, item = 0, item_next = 0;
+  int* queue = a.queue + group;
+  if (dyn) {
+    if (threadIdx.x == 0) s_item = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __syncthreads();
+    item = s_item;
+  } else {
+    const AttnSplit sp = attn_split(U, a.pieces, group, a.n_groups);
+    int4* merge = a.merge + (int64_t)group * a.pieces + piece;
+    if (piece >= sp.P) {
+      if (threadIdx.x == 0) *merge = make_int4(-1, 0, 0, 0);
+      return;
     }
-  }
-  // a piece that starts inside its first tile and reaches that tile's end is the last of the pieces
-  // over it: it is the one whose merge work group combines the tile's partials. The pieces over the
-  // tile run from the one holding its first unit to this one; the first piece's partial of the tile
-  // is in slot 1 unless the tile is also where that piece starts.
-  if (threadIdx.x == 0) {
-    int4 rec = make_int4(-1, 0, 0, 0);
-    if (u0 > cum[t] && u1 >= cum[t + 1]) {
-      const int i0 = attn_piece_of(U, P, cum[t]);
-      rec = make_int4(t, i0, piece - i0 + 1, attn_piece_start(U, P, i0) < cum[t] ? 1 : 0);
+    u0 = attn_piece_start(sp, piece);
+    u1 = attn_piece_start(sp, piece + 1);
+    {   // last tile with cum[t] <= u0: the tile holding unit u0
+      int hi = nt - 1;
+      while (t < hi) {
+        const int mid = (t + hi + 1) >> 1;
+        if (cum[mid] <= u0) t = mid;
+        else hi = mid - 1;
+      }
     }
-    *merge = rec;
+    // a piece that starts inside its first tile and reaches that tile's end is the last of the
+    // pieces over it: it is the one whose merge work group combines the tile's partials. The pieces
+    // over the tile run from the one holding its first unit to this one; the first piece's partial
+    // of the tile is in slot 1 unless the tile is also where that piece starts.
+    if (threadIdx.x == 0) {
+      int4 rec = make_int4(-1, 0, 0, 0);
+      if (u0 > cum[t] && u1 >= cum[t + 1]) {
+        const int i0 = attn_piece_of(sp, cum[t]);
+        rec = make_int4(t, i0, piece - i0 + 1, attn_piece_start(sp, i0) < cum[t] ? 1 : 0);
+      }
+      *merge = rec;
+    }
   }
 
   // uniform base of this (request, KV head); per-thread byte offsets fit 32 bits (checked by the host)
@@ -272,6 +289,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, nrec, 0x00020000);
 
   int slot = 0;
+  for (;;) {   // items of the queue (dynamic), or the one static range
+  if (dyn) {
+    if (item >= nt) break;
+    t = nt - 1 - item;
+    u0 = cum[t];
+    u1 = cum[t + 1];
+    // the next item is claimed now (one vector memory operation ahead of this tile's loads: the
+    // tile waits count it among the older ones, so they only get stricter)
+    if (threadIdx.x == 0) item_next = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   for (int u = u0; u < u1; ++t) {
     const int c0 = cum[t], c1 = cum[t + 1];
     const int se = min(u1, c1);
@@ -534,6 +561,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     slot = 1;
     u = se;
   }
+  if (!dyn) break;
+  if (threadIdx.x == 0) s_item = item_next;
+  __syncthreads();
+  item = s_item;
+  }
+}
+
+// Empties the groups' queues before a dynamic launch (system-scope stores: the queue is taken with
+// system-scope atomics, which work past the XCDs' caches)
+__global__ __launch_bounds__(64) void k_attn_queue_reset(int* q, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) __hip_atomic_store(q + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Exact float32 attention of one query vector per 32 threads (4 dims each), for a group whose fp16
@@ -618,7 +656,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   const int g = a.g, Mv = a.R * g;
   if (exact) {
     constexpr int VPE = 256 / (D / 4);   // vectors per pass of exact_vector (4 dims per thread)
-    const int stride = by_tile ? nt : a.pieces;
+    const int stride = a.comb_idx;
     for (int t = idx; t < nt; t += stride)
       for (int sub = 0; sub < VPB / VPE; ++sub) {
         const int v = t * 128 + slab * VPB + sub * VPE + (int)threadIdx.x / (D / 4);
@@ -626,15 +664,16 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
       }
     return;
   }
+  if (a.dynamic) return;   // every tile was written whole by one work group
   int tile = rec.x, i0 = rec.y, n = rec.z, slot0 = rec.w;
   if (by_tile) {   // the tile's unit range and the request's total give its pieces
     const int* cum = a.tilecum + (int64_t)req * (nt + 1);
     const int c0 = cum[tile], c1 = cum[tile + 1], U = cum[nt];
     if (c1 <= c0) return;
-    const int P = attn_pieces_used(U, a.pieces);
-    i0 = attn_piece_of(U, P, c0);
-    n = attn_piece_of(U, P, c1 - 1) - i0 + 1;
-    slot0 = attn_piece_start(U, P, i0) < c0 ? 1 : 0;
+    const AttnSplit sp = attn_split(U, a.pieces, group, a.n_groups);
+    i0 = attn_piece_of(sp, c0);
+    n = attn_piece_of(sp, c1 - 1) - i0 + 1;
+    slot0 = attn_piece_start(sp, i0) < c0 ? 1 : 0;
   }
   if (tile < 0 || n < 2) return;  // no cut tile, or one written directly by its only piece
   const int ql = slab * VPB + threadIdx.x / TPV, dc = threadIdx.x % TPV;
@@ -817,14 +856,24 @@ hipError_t launch_attn_bf16(int D, int n_req, int Hq, int Hkv, int R, int L, con
   a.qop_blocks = qop_blocks;
   a.pieces = pieces;
   if (a.n_tiles > kAttnMaxTiles || qop_blocks < 4 * a.n_tiles || pieces < 1) return hipErrorInvalidValue;
-  // the pieces' merge records follow the tiles' unit prefix sums in the same buffer (16-byte aligned)
+  // the pieces' merge records follow the tiles' unit prefix sums in the same buffer (16-byte aligned),
+  // then the groups' queues
   a.merge = reinterpret_cast<int4*>(tilecum + attn_merge_offset(n_req, a.n_tiles));
+  a.queue = tilecum + attn_queue_offset(n_req, a.n_tiles, a.n_groups, pieces);
+  // whole tiles from queues where every work group gets several of them
+  a.dynamic = attn_dynamic(a.n_tiles, pieces) ? 1 : 0;
+  a.comb_idx = a.dynamic ? min(16, pieces) : min(a.n_tiles, pieces);
+  hipError_t err;
+  if (a.dynamic && !ex.queue_ready) {
+    k_attn_queue_reset<<<dim3(1), dim3(64), 0, st>>>(a.queue, a.n_groups);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const unsigned nblk = (unsigned)(a.n_groups * pieces);
   if (D == 128) k_attn_mfma<128><<<dim3(nblk), dim3(256), 0, st>>>(a);
   else k_attn_mfma<64><<<dim3(nblk), dim3(256), 0, st>>>(a);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned ncomb = (unsigned)(a.n_groups * min(a.n_tiles, pieces) * (D == 128 ? 8 : 4));
+  const unsigned ncomb = (unsigned)(a.n_groups * a.comb_idx * (D == 128 ? 8 : 4));
   if (D == 128) k_attn_combine<128><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   else k_attn_combine<64><<<dim3(ncomb), dim3(256), 0, st>>>(a);
   return hipGetLastError();

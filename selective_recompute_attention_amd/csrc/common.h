@@ -173,6 +173,8 @@ struct F16Shadow {
   uint16_t* kh = nullptr;
   unsigned* flags = nullptr;
   unsigned call_id = 0;
+  int* queue = nullptr;   // the attention's group queues, emptied by the scatter that precedes it
+  int n_queue = 0;
 };
 // fp16 of the two bf16 values of word w (exact for magnitudes 2^-14 .. 65504; beyond 65504 infinity),
 // with the larger magnitude of the two folded into amax.
@@ -198,25 +200,65 @@ __host__ __device__ __forceinline__ int64_t qop_index(int64_t group, int b, int 
 
 // Work split of the bf16 attention. A group's 128-vector tiles need ceil((p_last + 1) / 64) units
 // of 64 keys each; the U units of a group are dealt to `pieces_used` work groups as contiguous
-// ranges [U i / P, U (i + 1) / P). kAttnSlots is the number of resident attention work groups on
-// 256 compute units (two per unit).
+// ranges. kAttnSlots is the number of resident attention work groups on 256 compute units (two per
+// unit): work groups b and b + kAttnSlots / 2 share a unit, and the first of the two runs faster
+// while both are resident (the older waves win the issue arbitration), so a piece whose work group
+// is the first on its unit takes kAttnFirstW parts of the units to the second's kAttnSecondW.
+#ifndef SRA_ATTN_FIRST_W
+#define SRA_ATTN_FIRST_W 11
+#endif
 constexpr int kAttnSlots = 512;
 constexpr int kAttnMinUnits = 3;
 constexpr int kAttnMaxTiles = 2048;
+constexpr int kAttnFirstW = SRA_ATTN_FIRST_W, kAttnSecondW = 10;
 __host__ __device__ __forceinline__ int attn_pieces_used(int U, int pieces) {
   const int p = (U + kAttnMinUnits - 1) / kAttnMinUnits;
   return p < 1 ? 1 : (p < pieces ? p : pieces);
 }
-__host__ __device__ __forceinline__ int attn_piece_start(int U, int P, int i) {
-  return (int)((int64_t)U * i / P);
+// The split of one (request, KV head) group: U units over P pieces, the first P1 of them (work
+// groups group + n_groups i below kAttnSlots / 2) weighted kAttnFirstW, the rest kAttnSecondW.
+struct AttnSplit {
+  int U, P, P1;
+};
+__host__ __device__ __forceinline__ AttnSplit attn_split(int U, int pieces, int group, int n_groups) {
+  AttnSplit s;
+  s.U = U;
+  s.P = attn_pieces_used(U, pieces);
+  const int h = kAttnSlots / 2 - group;
+  const int p1 = h > 0 ? (h + n_groups - 1) / n_groups : 0;
+  s.P1 = p1 < s.P ? p1 : s.P;
+  return s;
 }
-__host__ __device__ __forceinline__ int attn_piece_of(int U, int P, int u) {
-  return (int)(((int64_t)(u + 1) * P - 1) / U);
+__host__ __device__ __forceinline__ int64_t attn_weight_before(const AttnSplit& s, int i) {
+  const int a = i < s.P1 ? i : s.P1, b = i > s.P1 ? i - s.P1 : 0;
+  return (int64_t)kAttnFirstW * a + (int64_t)kAttnSecondW * b;
+}
+// first unit of piece i (i = P gives U)
+__host__ __device__ __forceinline__ int attn_piece_start(const AttnSplit& s, int i) {
+  return (int)((int64_t)s.U * attn_weight_before(s, i) / attn_weight_before(s, s.P));
+}
+// the piece whose range holds unit u (0 <= u < U): the last piece starting at or before it
+__host__ __device__ __forceinline__ int attn_piece_of(const AttnSplit& s, int u) {
+  int lo = 0, hi = s.P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (attn_piece_start(s, mid) <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 // ints before the pieces' 16-byte merge records in the attention's tilecum buffer
 __host__ __device__ __forceinline__ int64_t attn_merge_offset(int n_req, int n_tiles) {
   return ((int64_t)n_req * (n_tiles + 1) + 3) & ~(int64_t)3;
 }
+// ints before the groups' work queues (after the merge records); the buffer holds
+// attn_queue_offset + n_groups ints
+__host__ __device__ __forceinline__ int64_t attn_queue_offset(int n_req, int n_tiles, int n_groups, int pieces) {
+  return attn_merge_offset(n_req, n_tiles) + (int64_t)n_groups * pieces * 4;
+}
+// the attention takes whole tiles from per-group queues when a group has at least 2.5 tiles per work
+// group (fewer, and the largest tiles outweigh a work group's share: the static split is then better)
+__host__ __device__ __forceinline__ bool attn_dynamic(int n_tiles, int pieces) { return 2 * n_tiles >= 5 * pieces; }
 
 }  // namespace sra
 
@@ -336,6 +378,7 @@ hipError_t launch_select(const SelTab& tab, const unsigned long long* fx, int np
 // from the fresh queries q ([n_req][q_rows][Hq][D] before rotation, row p when indexed, else row r)
 // and the bf16 K/V; fallback (optional, [n_req][Hkv]) receives 1 for those groups and 0 for the rest.
 struct AttnExact {
+  int queue_ready = 0;   // the group queues were emptied by an earlier launch (the row scatter)
   const uint16_t* q = nullptr;
   int q_rows = 0;
   int indexed = 0;

@@ -78,6 +78,10 @@ __global__ __launch_bounds__(128) void k_scatter(int Hq, int Hkv, int R, int L,
   constexpr int VW = Vec<T>::N;
   constexpr int UPH = H / VW;
   constexpr int NT = 128;
+  // the attention that follows takes work from per-group queues: they start empty (system-scope
+  // stores: the queues are taken with system-scope atomics, past the XCDs' caches)
+  if (sh.queue && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < sh.n_queue; i += NT) __hip_atomic_store(sh.queue + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   __shared__ float2 cs[H];
   const int r = blockIdx.x, q = blockIdx.y;
   const int p = row_pos ? row_pos[(int64_t)q * R + r] : r;   // no table: row r sits at position r
