@@ -210,17 +210,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   if (kvh == 0 && piece == 0)
     for (int t = threadIdx.x; t <= nt; t += 256) a.tilecum[(int64_t)req * (nt + 1) + t] = cum[t];
   // Static split: this piece's unit range [u0, u1) and the tile holding u0. Dynamic: every work
-  // group of the group takes whole tiles from its queue, largest first (item k is tile nt - 1 - k,
-  // tiles grow with their last position), until the queue is empty; a work group that finishes a
-  // tile early takes the next one, so uneven speeds of the work groups even out.
+  // group of the group takes whole tiles, largest first (item k is tile nt - 1 - k, tiles grow with
+  // their last position): item `piece` first, then items pieces, pieces + 1, ... from the group's
+  // queue until it is empty; a work group that finishes a tile early takes the next one, so uneven
+  // speeds of the work groups even out.
   const bool dyn = a.dynamic != 0;
   __shared__ int s_item;
   int u0 = 0, u1 = 0, t = 0, item = 0, item_next = 0;
   int* queue = a.queue + group;
   if (dyn) {
-    if (threadIdx.x == 0) s_item = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    __syncthreads();
-    item = s_item;
+    item = piece;
   } else {
     const AttnSplit sp = attn_split(U, a.pieces, group, a.n_groups);
     int4* merge = a.merge + (int64_t)group * a.pieces + piece;
@@ -297,7 +296,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     u1 = cum[t + 1];
     // the next item is claimed now (one vector memory operation ahead of this tile's loads: the
     // tile waits count it among the older ones, so they only get stricter)
-    if (threadIdx.x == 0) item_next = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (threadIdx.x == 0)
+      item_next = a.pieces + __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   for (int u = u0; u < u1; ++t) {
     const int c0 = cum[t], c1 = cum[t + 1];
