@@ -256,9 +256,9 @@ __host__ __device__ __forceinline__ int64_t attn_merge_offset(int n_req, int n_t
 __host__ __device__ __forceinline__ int64_t attn_queue_offset(int n_req, int n_tiles, int n_groups, int pieces) {
   return attn_merge_offset(n_req, n_tiles) + (int64_t)n_groups * pieces * 4;
 }
-// the attention takes whole tiles from per-group queues when a group has at least 2.5 tiles per work
+// the attention takes whole tiles from per-group queues when a group has at least 2.25 tiles per work
 // group (fewer, and the largest tiles outweigh a work group's share: the static split is then better)
-__host__ __device__ __forceinline__ bool attn_dynamic(int n_tiles, int pieces) { return 2 * n_tiles >= 5 * pieces; }
+__host__ __device__ __forceinline__ bool attn_dynamic(int n_tiles, int pieces) { return 4 * n_tiles >= 9 * pieces; }
 
 }  // namespace sra
 
