@@ -10,13 +10,13 @@
 //     group) pairs v = r*g + hh, so any group size g packs without padding. Rows are ascending, so
 //     a tile's key range ends at the position of its last row and takes ceil((p_last+1)/64) units
 //     of 64 keys.
-//   * Persistent split: a fixed grid of work groups per group (two per compute unit in total).
-//     Each work group computes the tiles' unit counts from row_pos, takes the contiguous unit range
-//     [U i / P, U (i+1) / P) and walks it tile by tile. A tile it covers whole is written directly;
-//     a cut tile leaves a partial (O as fp16 scaled by the vector's largest |O|, max, sum) in one of
-//     two slots (first / last tile of the range) and the merge kernel combines the pieces of such
-//     tiles in key order. Every work group therefore gets the same number of key units, whatever
-//     the position mix.
+//   * Persistent work groups: a fixed grid of work groups per group (two per compute unit in total).
+//     Where a group has several tiles per work group, its work groups take whole tiles from the
+//     group's queue, largest first, and write each one directly. Otherwise each work group computes
+//     the tiles' unit counts from row_pos, takes a contiguous unit range (shares weighted by dispatch
+//     order) and walks it tile by tile: a tile it covers whole is written directly, a cut tile leaves
+//     a partial (O as fp16 scaled by the vector's largest |O|, max, sum) in one of two slots (first /
+//     last tile of the range) and the merge kernel combines the pieces of such tiles in key order.
 //   * Four waves, 32 query vectors each. S^T = K Q^T puts one query vector per lane column, so the
 //     online-softmax row reductions stay in-lane plus one cross-half shuffle, and the probabilities
 //     feed O^T = V^T P^T directly from registers (keys permuted consistently on both operands).
