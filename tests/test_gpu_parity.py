@@ -444,6 +444,30 @@ def test_fp16_range_fallback_matches_oracle():
     say(f"    fallback {res['fallback'].tolist()}, out max {stats['out_max']:.3g}")
 
 
+def test_fp16_range_fallback_whole_tile_mode():
+    """The same exact recomputation where the attention takes whole tiles from per-group queues (four
+    requests, 40 tiles per group over 16 work groups, d = 64): one fresh key of magnitude 1e5 on a query
+    row of request 2, KV head 1 flags that group alone, and every sampled row still matches the
+    oracle."""
+    w = make_custom(dtype="bf16", n_q_heads=32, n_kv_heads=8, head_dim=64, chunk_lens=(700, 700),
+                    orig_pos=(0, 40), query_len=8, n_req=4, seed=43, select=("pct", 90))
+    lay = w.layer(0)
+    Lctx = int(w.chunks[0, :, 1].sum())
+    big = O.storage_bits(O.bf16_round(np.array([1e5], dtype=np.float64)), "bf16")
+    lay["k_new"][2, Lctx + 2, 1, 5] = big[0]
+    N = O.select_count(90, 100, Lctx)
+    R, g = N + w.cfg.query_len, w.cfg.n_q_heads // w.cfg.n_kv_heads
+    tiles, pieces = -(-R * g // 128), 512 // (w.cfg.n_req * w.cfg.n_kv_heads)
+    assert 4 * tiles >= 9 * pieces, "the shape must take whole tiles from the queues"
+    say(f"case fp16 range, whole tiles: {tiles} tiles per group over {pieces} work groups, N={N}")
+    res = run_fused(w, n_select=N, fallback=True)
+    want = np.zeros((w.cfg.n_req, w.cfg.n_kv_heads), np.int32)
+    want[2, 1] = 1
+    np.testing.assert_array_equal(res["fallback"], want)
+    stats = oracle_compare(w, res, rows=wide_rows(res, "bf16", w.cfg.query_len, 64, 16))
+    say(f"    fallback {res['fallback'].tolist()}, out max {stats['out_max']:.3g}")
+
+
 def test_fp16_range_query_fallback_standalone():
     """A rotated query whose scaled value reaches fp16's infinity (|q| ~ 6e5) flags its group in the
     standalone attention entry; the group is recomputed exactly and matches the oracle (log-sum-exp
