@@ -67,7 +67,16 @@ extern "C" {
 #define SRA_DTYPE_BF16   0
 #define SRA_DTYPE_F32    1
 
-/* Implementation limits (checked, reported as SRA_E_LIMIT). */
+/* Implementation limits (checked on the host before anything is enqueued, reported as
+ * SRA_E_LIMIT with the limit in sra_last_error()):
+ *   - anchors: k <= SRA_MAX_ANCHOR_K per chunk, at most 256 KV heads;
+ *   - scoring: at most 80 requests per call; bf16: query rows x (Hq/Hkv) <= 2048; float32: at
+ *     most 80 (request, chunk) entries per call;
+ *   - attention, bf16: at most 262144 query vectors (rows x Hq/Hkv) per request and KV head, one
+ *     request's fused K or V below 4 GiB, one request's output below 2^31 elements; float32:
+ *     Hq/Hkv <= 16;
+ *   - chunk statistics: at most 80 chunks per request, context x (Hq/Hkv) <= 262144;
+ *   - sra_fused_layer_static: a workspace of at most 64 MiB (sra_workspace_size), devices 0..63. */
 #define SRA_MAX_ANCHOR_K        64      /* anchors per chunk                              */
 
 /* Head geometry shared by every call. Hq must be a multiple of Hkv; query head h reads
